@@ -1,0 +1,225 @@
+"""CPU oracle for MoE expert-parallel layout / dispatch / combine / fp8 cast.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg are the only callers.  The GPU library never imports, links or
+runs anything here, and nothing here imports the GPU package.
+
+The arithmetic lives in ``ep_oracle.c`` (plain C loops, one function per step
+of the method, each citing the passage it follows); this module compiles it
+with gcc on first use and marshals numpy arrays through ctypes.  ``brute`` is a
+separately written pure-Python brute force for tiny inputs that pins the C
+code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ep_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BAD_EXPERT = 1
+CAPACITY = 2
+RECV_OVERFLOW = 4
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ep_oracle.c into liboracle.so with gcc (plain -O2, no FMA
+    contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC",
+                               "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        _lib.oracle_bf16_from_float.restype = ctypes.c_uint16
+        _lib.oracle_bf16_from_float.argtypes = [ctypes.c_float]
+        _lib.oracle_e4m3_from_float.restype = ctypes.c_uint8
+        _lib.oracle_e4m3_from_float.argtypes = [ctypes.c_float]
+        _lib.oracle_e4m3_to_float.restype = ctypes.c_float
+        _lib.oracle_e4m3_to_float.argtypes = [ctypes.c_uint8]
+        _lib.oracle_bf16_to_float.restype = ctypes.c_float
+        _lib.oracle_bf16_to_float.argtypes = [ctypes.c_uint16]
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i64(v):
+    return ctypes.c_int64(int(v))
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+class Layout(dict):
+    """Plain dict of the oracle layout: count, offset, dst, src_of_slot,
+    in_part, tok_per_part, pairs_per_part, R, status."""
+    __getattr__ = dict.__getitem__
+
+
+def get_layout(topk_idx, num_experts, expert_alignment=1, num_partitions=1,
+               capacity=0, rows_cap=None) -> Layout:
+    lib = _load()
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    E, A, P, C = int(num_experts), int(expert_alignment), int(num_partitions), int(capacity)
+    if rows_cap is None:
+        rows_cap = E * C if C > 0 else T * K + min(E, T * K) * (A - 1)
+    count = np.zeros(E, np.int32)
+    offset = np.zeros(E + 1, np.int32)
+    dst = np.zeros(T * K, np.int32)
+    src = np.full(max(int(rows_cap), 1), -1, np.int32)
+    in_part = np.zeros(max(T * P, 1), np.uint8)
+    tpp = np.zeros(P, np.int32)
+    ppp = np.zeros(P, np.int32)
+    R = ctypes.c_int64(0)
+    st = ctypes.c_int32(0)
+    rc = lib.oracle_get_layout(_p(idx), _i64(T), _i64(K), _i64(E), _i64(A), _i64(P), _i64(C),
+                               _p(count), _p(offset), _p(dst), _p(src), _i64(rows_cap),
+                               _p(in_part), _p(tpp), _p(ppp), ctypes.byref(R), ctypes.byref(st))
+    if rc != 0:
+        raise ValueError("oracle_get_layout: invalid arguments")
+    R = int(R.value)
+    return Layout(count=count, offset=offset, dst=dst.reshape(T, K),
+                  src_of_slot=src[:min(R, int(rows_cap))], in_part=in_part[:T * P].reshape(T, P),
+                  tok_per_part=tpp, pairs_per_part=ppp, R=R, status=int(st.value))
+
+
+def dispatch(x_rows, layout: Layout, topk_weights=None, x_scales=None, zero_padding=False,
+             recv_init=None, scales_init=None):
+    """recv[dst[t,k]] = x[t] byte for byte.  x_rows is [T, H] of any dtype
+    (bf16 bits as uint16, fp8 codes as uint8); x_scales [T, H/G] float32 or
+    None.  Returns (recv [R, ...], recv_scales or None, recv_w [R]).  Padding
+    rows keep recv_init's content (zeros by default) unless zero_padding."""
+    lib = _load()
+    x = np.ascontiguousarray(x_rows)
+    T = x.shape[0]
+    K = layout.dst.shape[1] if T else 1
+    R = layout.R
+    row_bytes = x[0].nbytes if T else x.itemsize * int(np.prod(x.shape[1:]))
+    recv = (np.zeros((R,) + x.shape[1:], x.dtype) if recv_init is None
+            else np.array(recv_init, dtype=x.dtype, copy=True))
+    xs = _c(x_scales, np.float32)
+    recv_s = None
+    srow = 0
+    if xs is not None:
+        srow = xs.shape[1] * 4
+        recv_s = (np.zeros((R, xs.shape[1]), np.float32) if scales_init is None
+                  else np.array(scales_init, dtype=np.float32, copy=True))
+    recv_w = np.zeros(R, np.float32)
+    w = _c(topk_weights, np.float32)
+    lib.oracle_dispatch(_p(x), _i64(row_bytes), _p(xs), _i64(srow), _p(w), _i64(T), _i64(K),
+                        _p(np.ascontiguousarray(layout.dst, np.int32)),
+                        _p(np.ascontiguousarray(layout.src_of_slot, np.int32)), _i64(R),
+                        ctypes.c_int(1 if zero_padding else 0), _p(recv), _p(recv_s), _p(recv_w))
+    return recv, recv_s, recv_w
+
+
+def cast_fp8(x_bits, group=128):
+    """Per (token, group) e4m3 cast.  Returns (codes uint8 [T,H], scales f32 [T,H/G])."""
+    lib = _load()
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    q = np.zeros((T, H), np.uint8)
+    s = np.zeros((T, H // group), np.float32)
+    rc = lib.oracle_cast_fp8(_p(x), _i64(T), _i64(H), _i64(group), _p(q), _p(s))
+    if rc != 0:
+        raise ValueError("oracle_cast_fp8: invalid arguments")
+    return q, s
+
+
+def cast_back(q, scales, group=128):
+    lib = _load()
+    q = _c(q, np.uint8)
+    s = _c(scales, np.float32)
+    T, H = q.shape
+    out = np.zeros((T, H), np.float32)
+    lib.oracle_cast_back(_p(q), _p(s), _i64(T), _i64(H), _i64(group), _p(out))
+    return out
+
+
+def _combine(fn, out_dtype, y, dst, topk_weights, bias0, bias1, tokens):
+    y = _c(y, np.uint16)
+    H = y.shape[1]
+    dst = _c(dst, np.int32)
+    T, K = dst.shape
+    w = _c(topk_weights, np.float32)
+    b0 = _c(bias0, np.uint16)
+    b1 = _c(bias1, np.uint16)
+    tk = _c(tokens, np.int64)
+    n = T if tk is None else tk.shape[0]
+    out = np.zeros((n, H), out_dtype)
+    fn(_p(y), _i64(H), _p(w), _p(b0), _p(b1), _i64(T), _i64(K), _p(dst), _p(tk), _i64(n), _p(out))
+    return out
+
+
+def combine_f64(y, dst, topk_weights=None, bias0=None, bias1=None, tokens=None):
+    """float64 reference: sum of biases + sum_k w[t,k] * y[dst[t,k]]."""
+    return _combine(_load().oracle_combine_f64, np.float64, y, dst, topk_weights, bias0, bias1,
+                    tokens)
+
+
+def combine_f32(y, dst, topk_weights=None, bias0=None, bias1=None, tokens=None):
+    """Ordered fp32 accumulation (bias0, bias1, then fmaf over k ascending),
+    rounded to bf16; returns uint16 bits."""
+    return _combine(_load().oracle_combine_f32, np.uint16, y, dst, topk_weights, bias0, bias1,
+                    tokens)
+
+
+def combined_weights(recv_w, dst):
+    lib = _load()
+    dst = _c(dst, np.int32)
+    T, K = dst.shape
+    rw = _c(recv_w, np.float32)
+    out = np.zeros((T, K), np.float32)
+    lib.oracle_combined_weights(_p(rw), _i64(T), _i64(K), _p(dst), _p(out))
+    return out
+
+
+def e4m3_from_float(v):
+    v = _c(v, np.float32).ravel()
+    out = np.zeros(v.shape, np.uint8)
+    _load().oracle_e4m3_from_float_n(_p(v), _i64(v.size), _p(out))
+    return out
+
+
+def e4m3_to_float(codes):
+    lib = _load()
+    return np.array([lib.oracle_e4m3_to_float(int(c)) for c in np.asarray(codes).ravel()],
+                    np.float32)
+
+
+def bf16_from_float(v):
+    v = _c(v, np.float32).ravel()
+    out = np.zeros(v.shape, np.uint16)
+    _load().oracle_bf16_from_float_n(_p(v), _i64(v.size), _p(out))
+    return out
+
+
+def div_f32(a, b):
+    a = _c(a, np.float32).ravel()
+    b = _c(b, np.float32).ravel()
+    out = np.zeros(a.shape, np.float32)
+    _load().oracle_div_f32_n(_p(a), _p(b), _i64(a.size), _p(out))
+    return out
+
+
+def bf16_to_float(bits):
+    """bf16 bit patterns (uint16) widened to float32 (exact)."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
