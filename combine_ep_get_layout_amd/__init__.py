@@ -1,0 +1,276 @@
+"""MI355X-native MoE expert-parallel layout / dispatch / combine.
+
+Thin PyTorch binding over libep.so (include/ep.h).  PyTorch only provides
+device memory and the current HIP stream; every step of the path runs in the
+library's gfx950 kernels.  The functions carry the C entry points' names:
+
+  ep_get_layout(topk_idx, num_experts, ...)        -> Layout
+  ep_dispatch(x, layout, ...)                      -> (recv_x, recv_scales, recv_topk_weights)
+  ep_combine(y, layout, ...)                       -> (combined_x, combined_topk_weights)
+  ep_cast_fp8(x, group=128)                        -> (x_fp8, scales)
+
+Semantics follow the DeepEP v2 test page ("DeepEP test target API
+reference", sec. 2.1 dispatch, 2.2 combine, 3.1-3.2 the V1 layout tensors and
+unweighted combine, 4.2 the per-token e4m3 cast); the layout object plays the
+part of the page's handle.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+from . import _abi
+from ._abi import (EP_DEV_BAD_EXPERT, EP_DEV_CAPACITY, EP_DEV_RECV_OVERFLOW, EpError,
+                   LayoutParams, LayoutPtrs)
+
+__all__ = ["load_library", "Layout", "ep_get_layout", "ep_dispatch", "ep_combine", "ep_cast_fp8",
+           "worst_case_recv_rows", "EpError", "EP_DEV_BAD_EXPERT", "EP_DEV_CAPACITY",
+           "EP_DEV_RECV_OVERFLOW"]
+
+
+def load_library() -> ctypes.CDLL:
+    return _abi.load()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def worst_case_recv_rows(num_tokens, num_topk, num_experts, expert_alignment=1, capacity=0) -> int:
+    p = LayoutParams(num_tokens, num_topk, num_experts, expert_alignment, 1, capacity, 0)
+    return int(load_library().ep_worst_case_recv_rows(ctypes.byref(p)))
+
+
+class Layout:
+    """Device-resident receive layout (the dispatch "handle").
+
+    Tensors: num_tokens_per_expert [E], expert_offset [E+1] (R at [E]),
+    num_tokens_per_partition [P], is_token_in_partition [T, P] uint8,
+    dst_slot [T, K], src_of_slot [max_recv_rows], status [1]."""
+
+    def __init__(self, params: LayoutParams, device):
+        T, K, E, P = params.num_tokens, params.num_topk, params.num_experts, params.num_partitions
+        i32 = dict(dtype=torch.int32, device=device)
+        self.params = params
+        self.device = device
+        self.num_tokens_per_expert = torch.empty(E, **i32)
+        self.expert_offset = torch.empty(E + 1, **i32)
+        self.num_tokens_per_partition = torch.empty(P, **i32)
+        self.is_token_in_partition = torch.empty((T, P), dtype=torch.uint8, device=device)
+        self.dst_slot = torch.empty((T, K), **i32)
+        self.src_of_slot = torch.empty(max(params.max_recv_rows, 1), **i32)
+        self.status = torch.zeros(1, **i32)
+        nbytes = load_library().ep_get_layout_workspace_bytes(ctypes.byref(params))
+        self.workspace = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+    @property
+    def num_tokens(self):
+        return self.params.num_tokens
+
+    @property
+    def num_topk(self):
+        return self.params.num_topk
+
+    @property
+    def num_experts(self):
+        return self.params.num_experts
+
+    @property
+    def max_recv_rows(self) -> int:
+        return int(self.params.max_recv_rows)
+
+    def ptrs(self) -> LayoutPtrs:
+        return LayoutPtrs(self.num_tokens_per_expert.data_ptr(), self.expert_offset.data_ptr(),
+                          self.num_tokens_per_partition.data_ptr(),
+                          self.is_token_in_partition.data_ptr(), self.dst_slot.data_ptr(),
+                          self.src_of_slot.data_ptr(), self.status.data_ptr())
+
+    def num_recv_rows(self) -> int:
+        """R, the receive rows in use (synchronises: the page's do_cpu_sync)."""
+        return int(self.expert_offset[-1].item())
+
+    def check(self) -> int:
+        """Synchronise and raise on device status bits; returns the bits."""
+        st = int(self.status.item())
+        if st & EP_DEV_BAD_EXPERT:
+            raise ValueError("topk_idx holds an expert id outside [-1, num_experts)")
+        if st & EP_DEV_CAPACITY:
+            raise RuntimeError("an expert received more pairs than the fixed capacity")
+        if st & EP_DEV_RECV_OVERFLOW:
+            raise RuntimeError("receive rows exceed the allocated buffer")
+        return st
+
+
+def ep_get_layout(topk_idx: torch.Tensor, num_experts: int, expert_alignment: int = 1,
+                  num_partitions: int = 1, capacity: int = 0,
+                  max_recv_rows: Optional[int] = None,
+                  cumulative_expert_stats: Optional[torch.Tensor] = None,
+                  layout: Optional[Layout] = None) -> Layout:
+    """Derive the receive layout from topk_idx (int64 [T, K], -1 = none).
+    capacity > 0 selects the fixed-capacity ("expand") layout.  A `layout` of
+    the same shape may be passed in to be rewritten in place."""
+    lib = load_library()
+    _need_cuda(topk_idx, "topk_idx")
+    if topk_idx.dtype != torch.int64 or topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be int64 [T, K]")
+    T, K = topk_idx.shape
+    if max_recv_rows is None:
+        max_recv_rows = worst_case_recv_rows(T, K, num_experts, expert_alignment, capacity)
+    params = LayoutParams(T, K, num_experts, expert_alignment, num_partitions, capacity,
+                          int(max_recv_rows))
+    if layout is None:
+        layout = Layout(params, topk_idx.device)
+    elif (layout.params.num_tokens, layout.params.num_topk, layout.params.num_experts,
+          layout.params.num_partitions, layout.params.max_recv_rows) != (T, K, num_experts,
+                                                                         num_partitions,
+                                                                         int(max_recv_rows)):
+        raise ValueError("layout buffers do not match these shapes")
+    else:
+        layout.params = params
+    if cumulative_expert_stats is not None:
+        _need_cuda(cumulative_expert_stats, "cumulative_expert_stats")
+        if cumulative_expert_stats.dtype != torch.int32 or cumulative_expert_stats.numel() != num_experts:
+            raise ValueError("cumulative_expert_stats must be int32 [num_experts]")
+    ptrs = layout.ptrs()
+    rc = lib.ep_get_layout(_ptr(topk_idx), ctypes.byref(params), ctypes.byref(ptrs),
+                           _ptr(cumulative_expert_stats), _ptr(layout.workspace),
+                           layout.workspace.numel(), _stream(topk_idx.device))
+    _abi.check("ep_get_layout", rc)
+    return layout
+
+
+def _is_fp8(t: torch.Tensor) -> bool:
+    return t.dtype in (torch.float8_e4m3fn, torch.uint8)
+
+
+def ep_dispatch(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]], layout: Layout,
+                topk_weights: Optional[torch.Tensor] = None, recv_fp8: bool = False,
+                scale_group: int = 128, zero_padding: bool = False,
+                num_recv_rows: Optional[int] = None,
+                out: Optional[Sequence[Optional[torch.Tensor]]] = None):
+    """Permute token rows into the receive buffer.
+
+    x: bf16 [T, H], or (fp8 codes [T, H], fp32 scales [T, H/G]).  With bf16 x
+    and recv_fp8=True the rows are cast to e4m3 on the fly.  Returns
+    (recv_x, recv_scales or None, recv_topk_weights or None); recv buffers
+    have num_recv_rows rows (default: the layout's max_recv_rows)."""
+    lib = load_library()
+    x_scales = None
+    if isinstance(x, (tuple, list)):
+        x, x_scales = x
+    _need_cuda(x, "x")
+    T, H = x.shape
+    if T != layout.num_tokens:
+        raise ValueError("x rows != layout tokens")
+    fp8_in = _is_fp8(x)
+    if fp8_in:
+        if x_scales is None:
+            raise ValueError("fp8 x needs its scales")
+        _need_cuda(x_scales, "x_scales")
+        scale_group = H // x_scales.shape[1]
+        x_dtype, recv_dtype = _abi.EP_DTYPE_FP8_E4M3, _abi.EP_DTYPE_FP8_E4M3
+    else:
+        if x.dtype != torch.bfloat16:
+            raise ValueError("x must be bf16 or fp8")
+        x_dtype = _abi.EP_DTYPE_BF16
+        recv_dtype = _abi.EP_DTYPE_FP8_E4M3 if recv_fp8 else _abi.EP_DTYPE_BF16
+    rows = layout.max_recv_rows if num_recv_rows is None else int(num_recv_rows)
+    dev = x.device
+    recv_x = recv_s = recv_w = None
+    if out is not None:
+        recv_x, recv_s, recv_w = (list(out) + [None, None, None])[:3]
+    fp8_out = recv_dtype == _abi.EP_DTYPE_FP8_E4M3
+    if recv_x is None:
+        recv_x = torch.empty((rows, H), dtype=torch.float8_e4m3fn if fp8_out else torch.bfloat16,
+                             device=dev)
+    if fp8_out and recv_s is None:
+        recv_s = torch.empty((rows, H // scale_group), dtype=torch.float32, device=dev)
+    if topk_weights is not None:
+        _need_cuda(topk_weights, "topk_weights")
+        if topk_weights.dtype != torch.float32:
+            raise ValueError("topk_weights must be float32 [T, K]")
+        if recv_w is None:
+            recv_w = torch.empty(rows, dtype=torch.float32, device=dev)
+    if recv_x.shape[0] < rows:
+        raise ValueError("recv_x has fewer rows than num_recv_rows")
+    params = layout.params
+    ptrs = layout.ptrs()
+    rc = lib.ep_dispatch(_ptr(x), x_dtype, _ptr(x_scales), recv_dtype, H, scale_group,
+                         _ptr(topk_weights), ctypes.byref(params), ctypes.byref(ptrs),
+                         _ptr(recv_x), _ptr(recv_s), _ptr(recv_w), rows,
+                         1 if zero_padding else 0, _stream(dev))
+    _abi.check("ep_dispatch", rc)
+    return recv_x, recv_s, recv_w
+
+
+def ep_combine(y: torch.Tensor, layout: Layout, topk_weights: Optional[torch.Tensor] = None,
+               bias: Union[None, torch.Tensor, Tuple[torch.Tensor, torch.Tensor]] = None,
+               recv_topk_weights: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None):
+    """Reduce expert outputs y (bf16 [rows, H], the receive layout) back to the
+    tokens: out[t] = bias0 + bias1 + sum_k w[t,k] * y[dst_slot[t,k]] (fp32,
+    k ascending, bf16 round to nearest even).  Returns (combined_x,
+    combined_topk_weights or None)."""
+    lib = load_library()
+    _need_cuda(y, "y")
+    if y.dtype != torch.bfloat16:
+        raise ValueError("y must be bf16")
+    rows, H = y.shape
+    T, K = layout.num_tokens, layout.num_topk
+    b0 = b1 = None
+    if isinstance(bias, (tuple, list)):
+        b0, b1 = (list(bias) + [None, None])[:2]
+    elif bias is not None:
+        b0 = bias
+    for name, b in (("bias0", b0), ("bias1", b1)):
+        if b is not None:
+            _need_cuda(b, name)
+            if b.dtype != torch.bfloat16 or tuple(b.shape) != (T, H):
+                raise ValueError(f"{name} must be bf16 [T, H]")
+    if topk_weights is not None:
+        _need_cuda(topk_weights, "topk_weights")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    cw = None
+    if recv_topk_weights is not None:
+        _need_cuda(recv_topk_weights, "recv_topk_weights")
+        cw = torch.empty((T, K), dtype=torch.float32, device=y.device)
+    params = layout.params
+    ptrs = layout.ptrs()
+    rc = lib.ep_combine(_ptr(y), H, rows, _ptr(topk_weights), _ptr(b0), _ptr(b1),
+                        ctypes.byref(params), ctypes.byref(ptrs), _ptr(recv_topk_weights),
+                        _ptr(cw), _ptr(out), _stream(y.device))
+    _abi.check("ep_combine", rc)
+    return out, cw
+
+
+def ep_cast_fp8(x: torch.Tensor, group: int = 128,
+                out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Per (token, group of `group` channels) cast of bf16 rows to e4m3.
+    Returns (codes float8_e4m3fn [T, H], scales float32 [T, H/group])."""
+    lib = load_library()
+    _need_cuda(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    T, H = x.shape
+    if out is None:
+        q = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=x.device)
+        s = torch.empty((T, H // group), dtype=torch.float32, device=x.device)
+    else:
+        q, s = out
+    rc = lib.ep_cast_fp8(_ptr(x), T, H, group, _ptr(q), _ptr(s), _stream(x.device))
+    _abi.check("ep_cast_fp8", rc)
+    return q, s

@@ -1,0 +1,185 @@
+// C ABI of libep.so: argument validation and launches.  Every entry point
+// checks what the host can see (sizes, null pointers, alignment, limits) and
+// returns a negative ep_status before enqueuing anything, like the length
+// checks of the Rust EP=2 routing table ("spark_model/layers/ep_dispatch.rs",
+// build_ep_routing_table).  Nothing here allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include "../../include/ep.h"
+#include "ep_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_LAUNCH; }
+
+// Shape checks shared by every call that takes layout params.
+int check_params(const ep_layout_params *p) {
+    if (!p) return EP_ERR_INVALID_ARG;
+    if (p->num_tokens < 0 || p->num_topk < 1 || p->num_experts < 1 || p->expert_alignment < 1 ||
+        p->num_partitions < 1 || p->capacity < 0 || p->max_recv_rows < 0)
+        return EP_ERR_INVALID_ARG;
+    if (p->num_experts % p->num_partitions != 0) return EP_ERR_INVALID_ARG;
+    if (p->capacity > 0 && p->capacity % p->expert_alignment != 0) return EP_ERR_INVALID_ARG;
+    if (p->num_experts > EP_MAX_EXPERTS || p->num_partitions > EP_MAX_PARTITIONS)
+        return EP_ERR_UNSUPPORTED;
+    if (p->num_topk > EP_MAX_TOPK) return EP_ERR_UNSUPPORTED;
+    const int64_t pairs = (int64_t)p->num_tokens * p->num_topk;
+    if (pairs >= ((int64_t)1 << 31)) return EP_ERR_INVALID_ARG;
+    const int64_t worst = ep_worst_case_recv_rows(p);
+    if (worst >= ((int64_t)1 << 31)) return EP_ERR_INVALID_ARG;
+    if ((int64_t)p->num_tokens * p->num_partitions >= ((int64_t)1 << 40)) return EP_ERR_INVALID_ARG;
+    if (p->capacity > 0 && (int64_t)p->num_experts * p->capacity > p->max_recv_rows)
+        return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t ep_worst_case_recv_rows(const ep_layout_params *p) {
+    if (!p) return 0;
+    if (p->capacity > 0) return (int64_t)p->num_experts * p->capacity;
+    const int64_t pairs = (int64_t)p->num_tokens * p->num_topk;
+    const int64_t ne = pairs < p->num_experts ? pairs : p->num_experts;
+    return pairs + ne * (int64_t)(p->expert_alignment - 1);
+}
+
+size_t ep_get_layout_workspace_bytes(const ep_layout_params *p) {
+    if (check_params(p) != EP_OK) return 0;
+    ep::LayoutPlan plan;
+    if (!ep::make_layout_plan(p, &plan)) return 0;
+    return plan.ws_bytes;
+}
+
+int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *p, const ep_layout *layout,
+                  int32_t *cumulative_expert_stats, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+    int rc = check_params(p);
+    if (rc != EP_OK) return rc;
+    if (!layout || !layout->num_tokens_per_expert || !layout->expert_offset ||
+        !layout->num_tokens_per_partition || !layout->status)
+        return EP_ERR_INVALID_ARG;
+    if (p->num_tokens > 0 && (!topk_idx || !layout->is_token_in_partition || !layout->dst_slot))
+        return EP_ERR_INVALID_ARG;
+    if (p->max_recv_rows > 0 && !layout->src_of_slot) return EP_ERR_INVALID_ARG;
+    ep::LayoutPlan plan;
+    if (!ep::make_layout_plan(p, &plan)) return EP_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace))
+        return EP_ERR_WORKSPACE;
+    return to_status(ep::launch_layout(plan, topk_idx, layout, cumulative_expert_stats, workspace,
+                                       (hipStream_t)stream));
+}
+
+static bool valid_group(int hidden, int group) {
+    if (group == hidden) return true;
+    if (group < 16 || group > 512 || (group & (group - 1)) != 0) return false;
+    return hidden % group == 0;
+}
+
+int ep_dispatch(const void *x, int x_dtype, const float *x_scales, int recv_dtype, int32_t hidden,
+                int32_t scale_group, const float *topk_weights, const ep_layout_params *p,
+                const ep_layout *layout, void *recv_x, float *recv_scales,
+                float *recv_topk_weights, int64_t num_recv_rows, int zero_padding, void *stream) {
+    int rc = check_params(p);
+    if (rc != EP_OK) return rc;
+    if (!layout || !layout->num_tokens_per_expert || !layout->expert_offset || !layout->status)
+        return EP_ERR_INVALID_ARG;
+    if (p->num_tokens > 0 && !layout->dst_slot) return EP_ERR_INVALID_ARG;
+    if (num_recv_rows < 0 || hidden < 1) return EP_ERR_INVALID_ARG;
+    int mode;
+    if (x_dtype == EP_DTYPE_BF16 && recv_dtype == EP_DTYPE_BF16) mode = 0;
+    else if (x_dtype == EP_DTYPE_FP8_E4M3 && recv_dtype == EP_DTYPE_FP8_E4M3) mode = 1;
+    else if (x_dtype == EP_DTYPE_BF16 && recv_dtype == EP_DTYPE_FP8_E4M3) mode = 2;
+    else return EP_ERR_INVALID_ARG;
+    if (mode == 0 && hidden % 8 != 0) return EP_ERR_INVALID_ARG;
+    if (mode != 0) {
+        if (hidden % 16 != 0) return EP_ERR_INVALID_ARG;
+        if (!valid_group(hidden, scale_group)) return EP_ERR_UNSUPPORTED;
+        if (mode == 2 && scale_group == hidden && hidden > 16 * 64 * 8) return EP_ERR_UNSUPPORTED;
+        if (!recv_scales && num_recv_rows > 0) return EP_ERR_INVALID_ARG;
+        if (mode == 1 && !x_scales && p->num_tokens > 0) return EP_ERR_INVALID_ARG;
+    }
+    if (p->num_tokens > 0 && (!x || !aligned16(x))) return EP_ERR_INVALID_ARG;
+    if (num_recv_rows > 0 && (!recv_x || !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
+    ep::DispatchArgs a = {};
+    a.x = x;
+    a.x_scales = x_scales;
+    a.topk_weights = topk_weights;
+    a.dst = layout->dst_slot;
+    a.counts = layout->num_tokens_per_expert;
+    a.offsets = layout->expert_offset;
+    a.status = layout->status;
+    a.recv = recv_x;
+    a.recv_scales = recv_scales;
+    a.recv_w = recv_topk_weights;
+    a.recv_rows = num_recv_rows;
+    a.T = p->num_tokens;
+    a.K = p->num_topk;
+    a.E = p->num_experts;
+    a.A = p->expert_alignment;
+    a.C = p->capacity;
+    a.hidden = hidden;
+    a.group = mode == 0 ? 0 : scale_group;
+    a.mode = mode;
+    a.zero_padding = zero_padding ? 1 : 0;
+    return to_status(ep::launch_dispatch(a, (hipStream_t)stream));
+}
+
+int ep_combine(const void *y, int32_t hidden, int64_t num_y_rows, const float *topk_weights,
+               const void *bias0, const void *bias1, const ep_layout_params *p,
+               const ep_layout *layout, const float *recv_topk_weights,
+               float *combined_topk_weights, void *out, void *stream) {
+    int rc = check_params(p);
+    if (rc != EP_OK) return rc;
+    if (!layout || !layout->status || (p->num_tokens > 0 && !layout->dst_slot))
+        return EP_ERR_INVALID_ARG;
+    if (hidden < 8 || hidden % 8 != 0 || num_y_rows < 0) return EP_ERR_INVALID_ARG;
+    if (combined_topk_weights && !recv_topk_weights) return EP_ERR_INVALID_ARG;
+    if (p->num_tokens > 0) {
+        if (!out || !aligned16(out)) return EP_ERR_INVALID_ARG;
+        if (num_y_rows > 0 && (!y || !aligned16(y))) return EP_ERR_INVALID_ARG;
+        if ((bias0 && !aligned16(bias0)) || (bias1 && !aligned16(bias1))) return EP_ERR_INVALID_ARG;
+    }
+    ep::CombineArgs c = {};
+    c.y = y;
+    c.y_rows = num_y_rows;
+    c.w = topk_weights;
+    c.bias0 = bias0;
+    c.bias1 = bias1;
+    c.dst = layout->dst_slot;
+    c.status = layout->status;
+    c.recv_w = recv_topk_weights;
+    c.combined_w = combined_topk_weights;
+    c.out = out;
+    c.T = p->num_tokens;
+    c.K = p->num_topk;
+    c.hidden = hidden;
+    return to_status(ep::launch_combine(c, (hipStream_t)stream));
+}
+
+int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group, uint8_t *x_fp8,
+                float *scales, void *stream) {
+    if (num_tokens < 0 || hidden < 16 || hidden % 16 != 0) return EP_ERR_INVALID_ARG;
+    if (!valid_group(hidden, group)) return EP_ERR_UNSUPPORTED;
+    if (group == hidden && hidden > 16 * 64 * 8) return EP_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return EP_OK;
+    if (!x || !x_fp8 || !scales || !aligned16(x) || !aligned16(x_fp8)) return EP_ERR_INVALID_ARG;
+    return to_status(ep::launch_cast_fp8(x, num_tokens, hidden, group, x_fp8, scales,
+                                         (hipStream_t)stream));
+}
+
+const char *ep_status_string(int code) {
+    switch (code) {
+        case EP_OK: return "ok";
+        case EP_ERR_INVALID_ARG: return "invalid argument";
+        case EP_ERR_UNSUPPORTED: return "unsupported by this build";
+        case EP_ERR_WORKSPACE: return "workspace missing or too small";
+        case EP_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

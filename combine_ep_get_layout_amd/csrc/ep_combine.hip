@@ -1,0 +1,201 @@
+// Combine: gather expert outputs back to their source tokens and reduce.
+//
+// What is computed ("DeepEP test target API reference", sec. 2.2: weighted
+// reduction back to the source with 0/1/2 bias tensors, combined_x bf16
+// [T, hidden]; sec. 3.2: without weights it is a plain sum; sec. 4.1: an
+// ordered accumulation, no scatter_add, so results are bitwise
+// reproducible):
+//   acc = 0; acc += bias0; acc += bias1;
+//   for k = 0..K-1 with dst[t,k] >= 0:  acc = fmaf(w[t,k], y[dst[t,k]], acc)
+//   out[t] = bf16 round-to-nearest-even(acc)
+//
+// Kernel shape (gfx950, wave64).  A wave owns one chunk of VPL x 64 vectors
+// (8 channels each) of one output row and keeps 8*VPL fp32 accumulators per
+// lane.  The K destination slots and weights of the token are fetched once,
+// one per lane, and broadcast with readlane, so every row address is
+// wave-uniform.  Rows are fetched U at a time (U*VPL 16-byte loads in flight
+// per lane) and folded in ascending k.  No atomics: each output element is
+// produced by exactly one lane in a fixed order, so the result is
+// deterministic and independent of the other tokens in the batch.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+#ifndef EP_COMBINE_VPL
+#define EP_COMBINE_VPL 8
+#endif
+
+namespace ep {
+
+namespace {
+
+struct CombineK {
+    const uint8_t *y;
+    int64_t y_rows;
+    const float *w;
+    const uint8_t *b0;
+    const uint8_t *b1;
+    const int32_t *dst;
+    int32_t *status;
+    const float *recv_w;
+    float *combined_w;
+    uint8_t *out;
+    int T, K;
+    int nvec;       // 16-byte vectors per row
+    int row_bytes;
+    int wpr;
+};
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / 64;
+
+__device__ __forceinline__ void add_bf16x8(float *acc, ep_u32x4 v) {
+    acc[0] = acc[0] + bf16_lo(v.x);
+    acc[1] = acc[1] + bf16_hi(v.x);
+    acc[2] = acc[2] + bf16_lo(v.y);
+    acc[3] = acc[3] + bf16_hi(v.y);
+    acc[4] = acc[4] + bf16_lo(v.z);
+    acc[5] = acc[5] + bf16_hi(v.z);
+    acc[6] = acc[6] + bf16_lo(v.w);
+    acc[7] = acc[7] + bf16_hi(v.w);
+}
+
+__device__ __forceinline__ void fma_bf16x8(float *acc, float w, ep_u32x4 v) {
+    acc[0] = __builtin_fmaf(w, bf16_lo(v.x), acc[0]);
+    acc[1] = __builtin_fmaf(w, bf16_hi(v.x), acc[1]);
+    acc[2] = __builtin_fmaf(w, bf16_lo(v.y), acc[2]);
+    acc[3] = __builtin_fmaf(w, bf16_hi(v.y), acc[3]);
+    acc[4] = __builtin_fmaf(w, bf16_lo(v.z), acc[4]);
+    acc[5] = __builtin_fmaf(w, bf16_hi(v.z), acc[5]);
+    acc[6] = __builtin_fmaf(w, bf16_lo(v.w), acc[6]);
+    acc[7] = __builtin_fmaf(w, bf16_hi(v.w), acc[7]);
+}
+
+template <int VPL>
+__global__ void __launch_bounds__(kBlock) combine_kernel(CombineK a) {
+    constexpr int U = VPL >= 16 ? 1 : (VPL >= 8 ? 2 : (VPL >= 4 ? 4 : 8));
+    const int lane = __lane_id();
+    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int t = gw / a.wpr;
+    const int ci = gw - t * a.wpr;
+    if (t >= a.T) return;
+    const int v0 = ci * VPL * 64;
+
+    float acc[VPL][8];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+
+    const uint8_t *biases[2] = {a.b0, a.b1};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        if (!biases[b]) continue;
+        const ep_u32x4 *src = (const ep_u32x4 *)(biases[b] + (int64_t)t * a.row_bytes);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int vi = v0 + i * 64 + lane;
+            if (vi < a.nvec) add_bf16x8(acc[i], load_nt(src + vi));
+        }
+    }
+
+    for (int kb = 0; kb < a.K; kb += 64) {
+        int my_slot = -1;
+        float my_w = 1.0f;
+        if (kb + lane < a.K) {
+            my_slot = a.dst[(int64_t)t * a.K + kb + lane];
+            if (a.w) my_w = a.w[(int64_t)t * a.K + kb + lane];
+        }
+        if ((int64_t)my_slot >= a.y_rows) {
+            atomicOr(a.status, kDevRecvOverflow);
+            my_slot = -1;
+        }
+        if (ci == 0 && a.combined_w && kb + lane < a.K)
+            a.combined_w[(int64_t)t * a.K + kb + lane] = my_slot >= 0 ? a.recv_w[my_slot] : 0.0f;
+        const int kn = min(64, a.K - kb);
+        for (int k0 = 0; k0 < kn; k0 += U) {
+            ep_u32x4 v[U][VPL];
+            int slot[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                slot[u] = k0 + u < kn ? lane_read(my_slot, k0 + u) : -1;
+                if (slot[u] >= 0) {
+                    const ep_u32x4 *src = (const ep_u32x4 *)(a.y + (int64_t)slot[u] * a.row_bytes);
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) {
+                        const int vi = v0 + i * 64 + lane;
+                        v[u][i] = vi < a.nvec ? load_nt(src + vi) : ep_u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (slot[u] < 0) continue;
+                const float wk = lane_read_f(my_w, k0 + u);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) fma_bf16x8(acc[i], wk, v[u][i]);
+            }
+        }
+    }
+
+    ep_u32x4 *dst = (ep_u32x4 *)(a.out + (int64_t)t * a.row_bytes);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int vi = v0 + i * 64 + lane;
+        if (vi >= a.nvec) continue;
+        ep_u32x4 o;
+        o.x = bf16_rne(acc[i][0]) | (bf16_rne(acc[i][1]) << 16);
+        o.y = bf16_rne(acc[i][2]) | (bf16_rne(acc[i][3]) << 16);
+        o.z = bf16_rne(acc[i][4]) | (bf16_rne(acc[i][5]) << 16);
+        o.w = bf16_rne(acc[i][6]) | (bf16_rne(acc[i][7]) << 16);
+        store_nt(dst + vi, o);
+    }
+}
+
+int choose_vpl(int nvec, int limit) {
+    static const int cand[] = {16, 14, 8, 7, 4, 2, 1};
+    const int q = (nvec + 63) / 64;
+    for (int c : cand)
+        if (c <= limit && c <= q && q % c == 0 && nvec % 64 == 0) return c;
+    for (int c : cand)
+        if (c <= limit && c <= q) return c;
+    return 1;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
+    CombineK k = {};
+    k.y = (const uint8_t *)c.y;
+    k.y_rows = c.y_rows;
+    k.w = c.w;
+    k.b0 = (const uint8_t *)c.bias0;
+    k.b1 = (const uint8_t *)c.bias1;
+    k.dst = c.dst;
+    k.status = c.status;
+    k.recv_w = c.recv_w;
+    k.combined_w = c.combined_w;
+    k.out = (uint8_t *)c.out;
+    k.T = c.T;
+    k.K = c.K;
+    k.nvec = c.hidden / 8;
+    k.row_bytes = c.hidden * 2;
+    const int vpl = choose_vpl(k.nvec, EP_COMBINE_VPL);
+    k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
+    if (k.wpr < 1) k.wpr = 1;
+    const int64_t waves = (int64_t)k.T * k.wpr;
+    const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+#define EP_CASE(V)                                                                              \
+    case V:                                                                                     \
+        hipLaunchKernelGGL(combine_kernel<V>, dim3((unsigned)grid), dim3(kBlock), 0, stream, k); \
+        break;
+    switch (vpl) {
+        EP_CASE(1) EP_CASE(2) EP_CASE(4) EP_CASE(7) EP_CASE(8) EP_CASE(14) EP_CASE(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef EP_CASE
+    return hipGetLastError();
+}
+
+}  // namespace ep

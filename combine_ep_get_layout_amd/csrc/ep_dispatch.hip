@@ -1,0 +1,291 @@
+// Dispatch: permute token rows into the expert-ordered receive buffer, with
+// the fp8 e4m3 variants, plus the standalone per-(token, group) fp8 cast.
+//
+// What is computed ("DeepEP test target API reference", sec. 2.1: recv_x has
+// the input's type, fp8 input travels as (codes, scales), do_zero_padding;
+// sec. 4.2: per-token cast, scale = amax / 448, codes = x / scale as
+// float8_e4m3fn, here with one scale per group of G channels):
+//   recv[dst[t,k]] = row(x[t])       for every pair with dst >= 0,
+// with padding rows zeroed on request and recv weights 0 on padding.
+//
+// Kernel shape (gfx950, wave64).  A wave owns one chunk of VPL x 64 16-byte
+// vectors of one token row: it loads the chunk once into registers (x is
+// read exactly once) and stores it to each of the token's K destination rows
+// with 16-byte non-temporal stores, so the write stream (K times the read
+// stream) does not evict the routing tables from L2.  Rows are moved as
+// integer vectors, never as floats.  In the fused-cast mode the chunk is
+// converted in registers: per-group amax by a butterfly over the group's
+// lanes, fp32 scale, correctly rounded fp32 division, e4m3 round-to-nearest-
+// even, 8 codes per lane per vector.  Padding rows are handled by extra
+// workgroups of the same launch (one slice of one expert's padding each).
+#include "ep_device.h"
+#include "ep_internal.h"
+
+#ifndef EP_DISPATCH_VPL
+#define EP_DISPATCH_VPL 16
+#endif
+
+namespace ep {
+
+namespace {
+
+enum { kModeCopy16 = 0, kModeCopyFp8 = 1, kModeCast = 2 };
+
+struct DispatchK {
+    const uint8_t *x;
+    const float *x_scales;
+    const float *w;
+    const int32_t *dst;       // NULL: identity (cast only), slot = t, K = 1
+    const int32_t *counts;
+    const int32_t *offsets;
+    int32_t *status;
+    uint8_t *recv;
+    float *recv_scales;
+    float *recv_w;
+    int64_t recv_rows;
+    int T, K, E, C;
+    int nvec;                 // 16-byte vectors per input row
+    int in_row_bytes;
+    int out_row_bytes;
+    int ng;                   // scales per row (fp8 modes)
+    int group_lanes;          // cast: lanes per scale group; 0 = one scale per row
+    int wpr;                  // waves per row
+    int n_tok_blocks;
+    int pad_slices;           // padding workgroups per expert (0 = none)
+    int zero_padding;
+};
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / 64;
+
+__device__ __forceinline__ void pad_rows(const DispatchK &a, int pb) {
+    const int e = pb / a.pad_slices;
+    const int sl = pb - e * a.pad_slices;
+    if (e >= a.E) return;
+    const int c = a.counts[e];
+    const int used = a.C > 0 ? min(c, a.C) : c;
+    const int64_t beg = (int64_t)a.offsets[e] + used;
+    int64_t end = a.C > 0 ? (int64_t)a.offsets[e] + a.C : (int64_t)a.offsets[e + 1];
+    if (end > a.recv_rows) end = a.recv_rows;
+    if (!a.zero_padding) {
+        // weights only: one thread per padding row
+        if (a.recv_w)
+            for (int64_t r = beg + sl * kBlock + threadIdx.x; r < end; r += (int64_t)a.pad_slices * kBlock)
+                a.recv_w[r] = 0.0f;
+        return;
+    }
+    const int nv_out = a.out_row_bytes >> 4;
+    const ep_u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t r = beg + sl; r < end; r += a.pad_slices) {
+        ep_u32x4 *row = (ep_u32x4 *)(a.recv + r * (int64_t)a.out_row_bytes);
+        for (int v = threadIdx.x; v < nv_out; v += kBlock) store_nt(row + v, z);
+        if (a.recv_scales)
+            for (int j = threadIdx.x; j < a.ng; j += kBlock) a.recv_scales[r * a.ng + j] = 0.0f;
+        if (a.recv_w && threadIdx.x == 0) a.recv_w[r] = 0.0f;
+    }
+}
+
+template <int VPL, int MODE>
+__global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
+    if ((int)blockIdx.x >= a.n_tok_blocks) {
+        pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        return;
+    }
+    const int lane = __lane_id();
+    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int t = gw / a.wpr;
+    const int ci = gw - t * a.wpr;
+    if (t >= a.T) return;
+    const int K = a.dst ? a.K : 1;
+    const int v0 = ci * VPL * 64;
+
+    // Load this wave's chunk of the row once.
+    ep_u32x4 v[VPL];
+    const ep_u32x4 *src = (const ep_u32x4 *)(a.x + (int64_t)t * a.in_row_bytes);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int vi = v0 + i * 64 + lane;
+        if (vi < a.nvec) v[i] = load_nt(src + vi);
+        else v[i] = ep_u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // Per-pair destinations and weights, one pair per lane (K <= 64 per pass).
+    for (int kb = 0; kb < K; kb += 64) {
+        int my_slot = -1;
+        float my_w = 1.0f;
+        if (kb + lane < K) {
+            my_slot = a.dst ? a.dst[(int64_t)t * a.K + kb + lane] : t;
+            if (a.w) my_w = a.w[(int64_t)t * a.K + kb + lane];
+        }
+        if ((int64_t)my_slot >= a.recv_rows) {
+            if (a.status) atomicOr(a.status, kDevRecvOverflow);
+            my_slot = -1;
+        }
+        if (ci == 0 && a.recv_w && my_slot >= 0) a.recv_w[my_slot] = my_w;
+        const int kn = min(64, K - kb);
+
+        if (MODE == kModeCast) {
+            // Per-group scales, then codes; 8 codes (8 bytes) per lane per vector.
+            float s[VPL];
+            if (a.group_lanes > 0) {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) s[i] = scale_of(group_max(amax8(v[i]), a.group_lanes));
+            } else {
+                float m = 0.0f;
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) m = fmaxf(m, amax8(v[i]));
+                const float sr = scale_of(group_max(m, 64));
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) s[i] = sr;
+            }
+            ep_u32x2 q[VPL];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) q[i] = encode8(v[i], s[i]);
+            for (int k = 0; k < kn; ++k) {
+                const int slot = lane_read(my_slot, k);
+                if (slot < 0) continue;
+                ep_u32x2 *dstrow = (ep_u32x2 *)(a.recv + (int64_t)slot * a.out_row_bytes);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int vi = v0 + i * 64 + lane;
+                    if (vi < a.nvec) store_nt(dstrow + vi, q[i]);
+                }
+                float *srow = a.recv_scales + (int64_t)slot * a.ng;
+                if (a.group_lanes > 0) {
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) {
+                        const int vi = v0 + i * 64 + lane;
+                        if (vi < a.nvec && (vi % a.group_lanes) == 0) srow[vi / a.group_lanes] = s[i];
+                    }
+                } else if (lane == 0) {
+                    srow[0] = s[0];
+                }
+            }
+        } else {
+            for (int k = 0; k < kn; ++k) {
+                const int slot = lane_read(my_slot, k);
+                if (slot < 0) continue;
+                ep_u32x4 *dstrow = (ep_u32x4 *)(a.recv + (int64_t)slot * a.out_row_bytes);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int vi = v0 + i * 64 + lane;
+                    if (vi < a.nvec) store_nt(dstrow + vi, v[i]);
+                }
+                if (MODE == kModeCopyFp8 && ci == 0) {
+                    const float *ss = a.x_scales + (int64_t)t * a.ng;
+                    float *sd = a.recv_scales + (int64_t)slot * a.ng;
+                    for (int j = lane; j < a.ng; j += 64) sd[j] = ss[j];
+                }
+            }
+        }
+    }
+}
+
+template <int MODE>
+hipError_t launch_mode(const DispatchK &k, int vpl, int grid, hipStream_t stream) {
+#define EP_CASE(V)                                                                        \
+    case V:                                                                               \
+        hipLaunchKernelGGL((dispatch_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
+        break;
+    switch (vpl) {
+        EP_CASE(1) EP_CASE(2) EP_CASE(4) EP_CASE(7) EP_CASE(8) EP_CASE(14) EP_CASE(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef EP_CASE
+    return hipGetLastError();
+}
+
+// Vectors per lane: the largest allowed count <= limit that divides the
+// row's 64-vector chunks, else the largest <= limit and <= the chunk count.
+int choose_vpl(int nvec, int limit) {
+    static const int cand[] = {16, 14, 8, 7, 4, 2, 1};
+    const int q = (nvec + 63) / 64;
+    for (int c : cand)
+        if (c <= limit && c <= q && q % c == 0 && nvec % 64 == 0) return c;
+    for (int c : cand)
+        if (c <= limit && c <= q) return c;
+    return 1;
+}
+
+hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
+    int vpl = choose_vpl(k.nvec, vpl_limit);
+    if (mode == kModeCast && k.group_lanes == 0) {
+        // one scale per row: the whole row must sit in one wave
+        const int q = (k.nvec + 63) / 64;
+        vpl = q <= 1 ? 1 : q <= 2 ? 2 : q <= 4 ? 4 : q <= 7 ? 7 : q <= 8 ? 8 : q <= 14 ? 14 : 16;
+        if (q > 16) return hipErrorInvalidValue;
+    }
+    k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
+    if (k.wpr < 1) k.wpr = 1;
+    const int64_t waves = (int64_t)k.T * k.wpr;
+    k.n_tok_blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+    const int64_t grid = (int64_t)k.n_tok_blocks + (int64_t)k.E * k.pad_slices;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    switch (mode) {
+        case kModeCopy16: return launch_mode<kModeCopy16>(k, vpl, (int)grid, stream);
+        case kModeCopyFp8: return launch_mode<kModeCopyFp8>(k, vpl, (int)grid, stream);
+        default: return launch_mode<kModeCast>(k, vpl, (int)grid, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
+    DispatchK k = {};
+    k.x = (const uint8_t *)a.x;
+    k.x_scales = a.x_scales;
+    k.w = a.topk_weights;
+    k.dst = a.dst;
+    k.counts = a.counts;
+    k.offsets = a.offsets;
+    k.status = a.status;
+    k.recv = (uint8_t *)a.recv;
+    k.recv_scales = a.recv_scales;
+    k.recv_w = a.recv_w;
+    k.recv_rows = a.recv_rows;
+    k.T = a.T;
+    k.K = a.K;
+    k.E = a.E;
+    k.C = a.C;
+    if (a.mode == kModeCopy16) {
+        k.in_row_bytes = k.out_row_bytes = a.hidden * 2;
+        k.nvec = a.hidden / 8;
+    } else if (a.mode == kModeCopyFp8) {
+        k.in_row_bytes = k.out_row_bytes = a.hidden;
+        k.nvec = a.hidden / 16;
+        k.ng = a.hidden / a.group;
+    } else {
+        k.in_row_bytes = a.hidden * 2;
+        k.out_row_bytes = a.hidden;
+        k.nvec = a.hidden / 8;
+        k.ng = a.hidden / a.group;
+        k.group_lanes = a.group == a.hidden ? 0 : a.group / 8;
+    }
+    k.zero_padding = a.zero_padding;
+    int maxpad = a.C > 0 ? a.C : a.A - 1;
+    if (!a.zero_padding && !a.recv_w) maxpad = 0;
+    if (maxpad > 0) k.pad_slices = a.zero_padding ? (maxpad + 3) / 4 : 1;
+    return run(k, a.mode, EP_DISPATCH_VPL, stream);
+}
+
+hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, uint8_t *q, float *scales,
+                           hipStream_t stream) {
+    DispatchK k = {};
+    k.x = (const uint8_t *)x;
+    k.dst = nullptr;
+    k.status = nullptr;
+    k.recv = q;
+    k.recv_scales = scales;
+    k.recv_rows = T;
+    k.T = T;
+    k.K = 1;
+    k.in_row_bytes = hidden * 2;
+    k.out_row_bytes = hidden;
+    k.nvec = hidden / 8;
+    k.ng = hidden / group;
+    k.group_lanes = group == hidden ? 0 : group / 8;
+    return run(k, kModeCast, EP_DISPATCH_VPL, stream);
+}
+
+}  // namespace ep

@@ -1,0 +1,71 @@
+// Host-side launchers shared between the kernel files and the C ABI (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ep.h"
+
+namespace ep {
+
+// Tiling of the layout pass, chosen on the host from the shapes alone.
+struct LayoutPlan {
+    int T, K, E, A, P, C;
+    int64_t max_rows;
+    int tile_tokens;   // tokens per count tile (one workgroup)
+    int num_tiles;     // ceil(T / tile_tokens)
+    int block;         // threads per count workgroup (multiple of 64)
+    int chunks_per_wave;
+    size_t ws_tile_counts;  // byte offsets inside the workspace
+    size_t ws_tile_part;
+    size_t ws_tile_flags;
+    size_t ws_bytes;
+};
+
+bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan);
+
+hipError_t launch_layout(const LayoutPlan &plan, const int64_t *topk_idx, const ep_layout *layout,
+                         int32_t *cum_stats, void *workspace, hipStream_t stream);
+
+struct DispatchArgs {
+    const void *x;
+    const float *x_scales;
+    const float *topk_weights;
+    const int32_t *dst;            // [T*K]
+    const int32_t *counts;         // [E]
+    const int32_t *offsets;        // [E+1]
+    int32_t *status;
+    void *recv;
+    float *recv_scales;
+    float *recv_w;
+    int64_t recv_rows;
+    int T, K, E, A, C;
+    int hidden;
+    int group;                     // fp8 scale group (0 when bf16 -> bf16)
+    int mode;                      // 0 copy bf16, 1 copy fp8 (+scales), 2 cast bf16 -> fp8
+    int zero_padding;
+};
+
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream);
+
+struct CombineArgs {
+    const void *y;
+    int64_t y_rows;
+    const float *w;
+    const void *bias0;
+    const void *bias1;
+    const int32_t *dst;
+    int32_t *status;
+    const float *recv_w;
+    float *combined_w;
+    void *out;
+    int T, K, hidden;
+};
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
+
+hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, uint8_t *q, float *scales,
+                           hipStream_t stream);
+
+}  // namespace ep

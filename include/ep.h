@@ -1,0 +1,208 @@
+/*
+ * ep.h - C ABI of the MI355X (gfx950) MoE expert-parallel layout / dispatch /
+ * combine library (libep.so).
+ *
+ * One GPU's share of DeepEP-style token dispatch and combine: derive a
+ * receive layout from top-k routing, permute token rows into an
+ * expert-ordered, alignment-padded receive buffer, and reduce expert outputs
+ * back to their source tokens.  Sources, cited by page title:
+ *
+ *   [API]  "DeepEP test target API reference" (DeepEP v2 test page):
+ *          2.1 dispatch() and its parameter table, 2.2 combine(),
+ *          3.1 V1 Buffer.dispatch() layout tensors, 3.2 V1 combine (no
+ *          weights), 4.1 refs (ordered accumulation), 4.2 math (align,
+ *          per-token cast to float8_e4m3fn).
+ *   [RUST] "spark_model/layers/ep_dispatch.rs": partition of (token, expert,
+ *          weight) pairs by expert ownership; length checks.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named in the comments as "device" point to GPU memory the
+ *     caller allocated (hipMalloc, or a framework allocator); "host" pointers
+ *     point to CPU memory read before the call returns.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued on it and the call returns without synchronising.  No call
+ *     allocates or frees memory, and the library keeps no state between calls.
+ *   - Argument errors the host can see return a negative ep_status before
+ *     anything is enqueued.  Errors only the device can see set bits in
+ *     layout->status (EP_DEV_*), read by the caller after synchronising.
+ *   - Counts, offsets and slots are int32; callers keep T*K, R < 2^31.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = -1,  /* bad size, null required pointer, misalignment */
+    EP_ERR_UNSUPPORTED = -2,  /* valid but outside this build's limits        */
+    EP_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required   */
+    EP_ERR_LAUNCH = -4        /* the HIP runtime refused a launch             */
+} ep_status;
+
+/* Bits OR-ed into layout->status by the device. */
+enum {
+    EP_DEV_BAD_EXPERT = 1,     /* an id outside [-1, E): the pair is ignored    */
+    EP_DEV_CAPACITY = 2,       /* fixed capacity: an expert got more than C     */
+    EP_DEV_RECV_OVERFLOW = 4   /* a slot >= the rows the caller allocated       */
+};
+
+enum { EP_DTYPE_BF16 = 0, EP_DTYPE_FP8_E4M3 = 1 };
+
+/* Limits of this build. */
+enum { EP_MAX_EXPERTS = 4096, EP_MAX_PARTITIONS = 1024, EP_MAX_TOPK = 256 };
+
+/* Shape of one layout ([API] 2.1 parameter table: num_experts,
+ * expert_alignment, num_max_tokens_per_rank; 3.1 num_tokens_per_rank). */
+typedef struct ep_layout_params {
+    int32_t num_tokens;        /* T >= 0                                          */
+    int32_t num_topk;          /* K >= 1                                          */
+    int32_t num_experts;       /* E in [1, EP_MAX_EXPERTS]                        */
+    int32_t expert_alignment;  /* A >= 1: each expert's rows padded to a multiple */
+    int32_t num_partitions;    /* P in [1, EP_MAX_PARTITIONS], E % P == 0;        */
+                               /* partition q owns experts [q*E/P, (q+1)*E/P)     */
+    int32_t capacity;          /* 0: compact padded layout; C > 0: fixed-capacity */
+                               /* ("expand") layout, expert e owns rows           */
+                               /* [e*C, (e+1)*C); requires C % A == 0             */
+    int64_t max_recv_rows;     /* rows of src_of_slot the caller allocated        */
+} ep_layout_params;
+
+/* The layout ("handle", [API] 2.1 return values and 3.1 layout tensors):
+ * caller-owned device buffers, written by ep_get_layout and read by
+ * ep_dispatch / ep_combine. */
+typedef struct ep_layout {
+    int32_t *num_tokens_per_expert;     /* [E]   pairs routed to each expert          */
+    int32_t *expert_offset;             /* [E+1] first receive row of each expert;   */
+                                        /*       [E] = R, the receive rows in use     */
+    int32_t *num_tokens_per_partition;  /* [P]   tokens with >= 1 pair in partition   */
+    uint8_t *is_token_in_partition;     /* [T*P] 0/1                                  */
+    int32_t *dst_slot;                  /* [T*K] receive row of pair (t,k), or -1     */
+    int32_t *src_of_slot;               /* [max_recv_rows] t*K+k, or -1 for padding   */
+    int32_t *status;                    /* [1]   EP_DEV_* bits                        */
+} ep_layout;
+
+/* Bytes of device workspace ep_get_layout needs for these params (host call,
+ * no GPU work).  Returns 0 when the params are invalid. */
+size_t ep_get_layout_workspace_bytes(const ep_layout_params *params);
+
+/* Worst-case receive rows for these params (host call): E*C in fixed mode,
+ * else T*K + min(E, T*K)*(A-1).  Buffers of this many rows never overflow. */
+int64_t ep_worst_case_recv_rows(const ep_layout_params *params);
+
+/* ep_get_layout - derive the receive layout from top-k routing.
+ * ([API] 2.1: V2 derives the layout from topk_idx; 3.1: the V1 layout
+ *  tensors num_tokens_per_expert / is_token_in_rank / num_tokens_per_rank;
+ *  4.2 align; [RUST] partition by expert range, token-major then k order.)
+ *
+ *   topk_idx   device int64 [T, K], row-major; -1 = no expert.
+ *   params     host; shape of the layout.
+ *   layout     host struct of device buffers (all seven required, except that
+ *              arrays with zero elements may be NULL).
+ *   cumulative_expert_stats  device int32 [E] or NULL: += per-expert counts
+ *              ([API] 2.1 cumulative_local_expert_recv_stats).
+ *   workspace  device, >= ep_get_layout_workspace_bytes(params) bytes, 16-byte
+ *              aligned; contents need no initialisation and are scratch.
+ *
+ * Computes count[e] = #{(t,k): idx = e}; padded[e] = align(count[e], A);
+ * expert_offset = exclusive scan of padded (compact) or e*C (fixed);
+ * dst_slot[t,k] = expert_offset[e] + j where j is the rank of (t,k) among
+ * the pairs of e in ascending t*K+k order (-1 for idx = -1, for an invalid
+ * id, and for pairs with j >= C in fixed mode); src_of_slot[s] = t*K+k for
+ * used slots and -1 for padding slots (slots >= max_recv_rows are not
+ * written); partition membership and per-partition token counts.
+ * layout->status is overwritten with EP_DEV_BAD_EXPERT / EP_DEV_CAPACITY /
+ * EP_DEV_RECV_OVERFLOW (R > max_recv_rows).  T = 0 is valid.
+ * Errors: EP_ERR_INVALID_ARG (null pointer, T < 0, K < 1, E < 1, A < 1,
+ * P < 1, E % P != 0, C < 0, C % A != 0, fixed mode with E*C > max_recv_rows,
+ * int32 overflow of T*K or of the worst-case rows), EP_ERR_UNSUPPORTED
+ * (E > EP_MAX_EXPERTS, P > EP_MAX_PARTITIONS, K > EP_MAX_TOPK),
+ * EP_ERR_WORKSPACE. */
+int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,
+                  const ep_layout *layout, int32_t *cumulative_expert_stats,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* ep_dispatch - permute token rows into the receive buffer.
+ * ([API] 2.1: x is bf16 [T, hidden] or the pair (fp8 codes, scales); recv_x
+ *  has the input's type; do_zero_padding; 4.2 per-token cast to e4m3.)
+ *
+ *   x            device [T, hidden]: bf16 (x_dtype EP_DTYPE_BF16) or e4m3 codes
+ *                (EP_DTYPE_FP8_E4M3); 16-byte aligned.
+ *   x_scales     device float [T, hidden/scale_group] when x is fp8, else NULL.
+ *   recv_dtype   == x_dtype, or EP_DTYPE_FP8_E4M3 with bf16 x: the rows are
+ *                cast on the fly, exactly as ep_cast_fp8 followed by an fp8
+ *                dispatch would do.
+ *   hidden       channels per row; multiple of 8 (bf16) or 16 (fp8 rows).
+ *   scale_group  G, channels per fp32 scale when fp8 is involved: a power of
+ *                two in [16, 512] dividing hidden, or hidden itself (one scale
+ *                per token).  Ignored for bf16 -> bf16.
+ *   topk_weights device float [T, K] or NULL.
+ *   params, layout  as produced by ep_get_layout for the same routing.
+ *   recv_x       device [num_recv_rows, hidden] of recv_dtype; 16-byte aligned.
+ *   recv_scales  device float [num_recv_rows, hidden/G] when recv is fp8.
+ *   recv_topk_weights device float [num_recv_rows] or NULL: weight of the pair
+ *                in each row (1 when topk_weights is NULL), 0 for padding rows.
+ *   num_recv_rows rows allocated for recv_x / recv_scales / recv_topk_weights;
+ *                rows past it are skipped and EP_DEV_RECV_OVERFLOW is set.
+ *   zero_padding 1: padding rows (and their scales) are written with zeros;
+ *                0: their bytes are left as they were.
+ * recv_x[dst_slot[t,k]] = x[t] byte for byte (fp8: codes and scale row).
+ * Errors: EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED (a scale_group outside the
+ * set above). */
+int ep_dispatch(const void *x, int x_dtype, const float *x_scales, int recv_dtype,
+                int32_t hidden, int32_t scale_group, const float *topk_weights,
+                const ep_layout_params *params, const ep_layout *layout,
+                void *recv_x, float *recv_scales, float *recv_topk_weights,
+                int64_t num_recv_rows, int zero_padding, void *stream);
+
+/* ep_combine - gather expert outputs back to their tokens and reduce.
+ * ([API] 2.2: weighted reduction back to the source, bias 0/1/2 tensors,
+ *  returns combined_x bf16 [T, hidden] and combined_topk_weights; 3.2: V1
+ *  combine is an unweighted sum; 4.1: ordered accumulation.)
+ *
+ *   y            device bf16 [num_y_rows, hidden] (the receive layout's rows);
+ *                16-byte aligned; hidden % 8 == 0.
+ *   topk_weights device float [T, K], or NULL for the unweighted sum.
+ *   bias0, bias1 device bf16 [T, hidden] or NULL.
+ *   recv_topk_weights      device float [num_y_rows] or NULL (input).
+ *   combined_topk_weights  device float [T, K] or NULL (output):
+ *                recv_topk_weights[dst_slot[t,k]] for kept pairs, else 0;
+ *                requires recv_topk_weights.
+ *   out          device bf16 [T, hidden].
+ * out[t,c] = bf16_rne(acc) where acc = 0; acc += bias0; acc += bias1; then for
+ * k = 0..K-1 with dst_slot[t,k] >= 0: acc = fmaf(w[t,k], y[dst_slot[t,k], c], acc)
+ * in fp32.  No atomics: the result is deterministic and does not depend on
+ * which other tokens are in the batch.  Slots >= num_y_rows are skipped and
+ * set EP_DEV_RECV_OVERFLOW. */
+int ep_combine(const void *y, int32_t hidden, int64_t num_y_rows,
+               const float *topk_weights, const void *bias0, const void *bias1,
+               const ep_layout_params *params, const ep_layout *layout,
+               const float *recv_topk_weights, float *combined_topk_weights,
+               void *out, void *stream);
+
+/* ep_cast_fp8 - per (token, group) cast of bf16 rows to OCP e4m3
+ * ([API] 4.2 per_token_cast_to_fp8, with one scale per group of G channels;
+ *  G = hidden is the page's one-scale-per-token form).
+ *
+ *   x       device bf16 [T, hidden], 16-byte aligned, hidden % 16 == 0.
+ *   group   G: a power of two in [16, 512] dividing hidden, or hidden.
+ *   x_fp8   device uint8 [T, hidden], 16-byte aligned (e4m3fn codes).
+ *   scales  device float [T, hidden/G].
+ * amax = max |x| over the group; s = max(amax, 1e-4f) / 448 (fp32, nearest);
+ * code = e4m3_rne(x / s) (fp32 nearest division, ties to even, sign kept on
+ * underflow).  Decode: x ~= float(code) * s. */
+int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group,
+                uint8_t *x_fp8, float *scales, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *ep_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every symbol include/ep.h declares, and
+rejects bad arguments on the host before any GPU work (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_ep_get_layout_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ep.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_\w+)\s*\(", src)))
+
+
+def test_header_declarations_match_binding():
+    assert _declared() == sorted(_abi.EXPORTS)
+
+
+def test_library_exports_every_symbol():
+    lib = _abi.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def _params(T=16, K=2, E=8, A=1, P=1, C=0, rows=None):
+    p = _abi.LayoutParams(T, K, E, A, P, C, 0)
+    p.max_recv_rows = rows if rows is not None else _abi.load().ep_worst_case_recv_rows(ctypes.byref(p))
+    return p
+
+
+def test_worst_case_rows():
+    lib = _abi.load()
+    assert lib.ep_worst_case_recv_rows(ctypes.byref(_params(4096, 8, 256, 128))) == 32768 + 256 * 127
+    assert lib.ep_worst_case_recv_rows(ctypes.byref(_params(2, 2, 256, 128))) == 4 + 4 * 127
+    assert lib.ep_worst_case_recv_rows(ctypes.byref(_params(128, 8, 256, 1, C=128))) == 32768
+
+
+def test_workspace_bytes():
+    lib = _abi.load()
+    n = lib.ep_get_layout_workspace_bytes(ctypes.byref(_params(4096, 8, 256, 128)))
+    assert n > 0 and n % 256 == 0
+    assert lib.ep_get_layout_workspace_bytes(ctypes.byref(_params(E=6, P=4))) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(E=6, P=4), _abi.EP_ERR_INVALID_ARG),        # E % P != 0
+    (dict(A=0), _abi.EP_ERR_INVALID_ARG),             # A < 1
+    (dict(K=0), _abi.EP_ERR_INVALID_ARG),
+    (dict(T=-1), _abi.EP_ERR_INVALID_ARG),
+    (dict(C=6, A=4), _abi.EP_ERR_INVALID_ARG),        # C % A != 0
+    (dict(C=4, rows=10), _abi.EP_ERR_INVALID_ARG),    # E*C > max_recv_rows
+    (dict(E=8192, P=1), _abi.EP_ERR_UNSUPPORTED),
+    (dict(K=300, E=512), _abi.EP_ERR_UNSUPPORTED),
+])
+def test_get_layout_rejects_bad_params_before_launch(kw, code):
+    lib = _abi.load()
+    p = _params(**kw)
+    lay = _abi.LayoutPtrs(*([8] * 7))       # never dereferenced: rejected first
+    rc = lib.ep_get_layout(ctypes.c_void_p(16), ctypes.byref(p), ctypes.byref(lay), None,
+                           ctypes.c_void_p(256), 1 << 20, None)
+    assert rc == code
+
+
+def test_get_layout_rejects_null_buffers_and_small_workspace():
+    lib = _abi.load()
+    p = _params()
+    lay = _abi.LayoutPtrs(16, 16, 16, 16, 16, 16, None)   # status missing
+    assert lib.ep_get_layout(ctypes.c_void_p(16), ctypes.byref(p), ctypes.byref(lay), None,
+                             ctypes.c_void_p(256), 1 << 20, None) == _abi.EP_ERR_INVALID_ARG
+    lay = _abi.LayoutPtrs(*([16] * 7))
+    assert lib.ep_get_layout(None, ctypes.byref(p), ctypes.byref(lay), None,
+                             ctypes.c_void_p(256), 1 << 20, None) == _abi.EP_ERR_INVALID_ARG
+    assert lib.ep_get_layout(ctypes.c_void_p(16), ctypes.byref(p), ctypes.byref(lay), None,
+                             ctypes.c_void_p(256), 16, None) == _abi.EP_ERR_WORKSPACE
+    assert lib.ep_get_layout(ctypes.c_void_p(16), ctypes.byref(p), ctypes.byref(lay), None,
+                             ctypes.c_void_p(260), 1 << 20, None) == _abi.EP_ERR_WORKSPACE
+
+
+def test_dispatch_rejects_bad_arguments():
+    lib = _abi.load()
+    p = _params(T=4, K=2, E=8)
+    lay = _abi.LayoutPtrs(*([16] * 7))
+    bf, f8 = _abi.EP_DTYPE_BF16, _abi.EP_DTYPE_FP8_E4M3
+
+    def call(x=16, xd=bf, xs=None, rd=bf, H=64, G=128, rs=None, rows=8):
+        return lib.ep_dispatch(ctypes.c_void_p(x), xd, xs, rd, H, G, None, ctypes.byref(p),
+                               ctypes.byref(lay), ctypes.c_void_p(16), rs, None, rows, 0, None)
+    assert call(H=60) == _abi.EP_ERR_INVALID_ARG              # hidden % 8
+    assert call(x=24) == _abi.EP_ERR_INVALID_ARG              # x misaligned
+    assert call(xd=f8, rd=bf) == _abi.EP_ERR_INVALID_ARG      # fp8 -> bf16 is not a mode
+    assert call(rd=f8, H=128, G=128) == _abi.EP_ERR_INVALID_ARG   # fp8 recv without scales
+    assert call(rd=f8, H=120, G=8, rs=16) == _abi.EP_ERR_INVALID_ARG   # hidden % 16
+    assert call(rd=f8, H=192, G=96, rs=16) == _abi.EP_ERR_UNSUPPORTED  # group not a power of 2
+    assert call(rd=f8, H=128, G=1024, rs=16) == _abi.EP_ERR_UNSUPPORTED
+    assert call(xd=f8, rd=f8, H=128, rs=16) == _abi.EP_ERR_INVALID_ARG  # fp8 x without scales
+    assert call(rows=-1) == _abi.EP_ERR_INVALID_ARG
+
+
+def test_combine_and_cast_reject_bad_arguments():
+    lib = _abi.load()
+    p = _params(T=4, K=2, E=8)
+    lay = _abi.LayoutPtrs(*([16] * 7))
+    assert lib.ep_combine(ctypes.c_void_p(16), 12, 8, None, None, None, ctypes.byref(p),
+                          ctypes.byref(lay), None, None, ctypes.c_void_p(16), None) == _abi.EP_ERR_INVALID_ARG
+    assert lib.ep_combine(ctypes.c_void_p(16), 64, 8, None, ctypes.c_void_p(8), None,
+                          ctypes.byref(p), ctypes.byref(lay), None, None, ctypes.c_void_p(16),
+                          None) == _abi.EP_ERR_INVALID_ARG       # misaligned bias
+    assert lib.ep_combine(ctypes.c_void_p(16), 64, 8, None, None, None, ctypes.byref(p),
+                          ctypes.byref(lay), None, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                          None) == _abi.EP_ERR_INVALID_ARG       # combined weights need recv weights
+    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 4, 100, 128, ctypes.c_void_p(16),
+                           ctypes.c_void_p(16), None) == _abi.EP_ERR_INVALID_ARG
+    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 4, 384, 96, ctypes.c_void_p(16),
+                           ctypes.c_void_p(16), None) == _abi.EP_ERR_UNSUPPORTED
+    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 0, 128, 128, None, None, None) == _abi.EP_OK
+
+
+def test_status_strings():
+    lib = _abi.load()
+    for code in (0, -1, -2, -3, -4, 7):
+        assert lib.ep_status_string(code)

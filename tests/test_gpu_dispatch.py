@@ -1,0 +1,187 @@
+"""GPU parity of ep_dispatch (bf16 rows, fp8 rows, fused cast, zero padding,
+fixed capacity) and ep_cast_fp8 against the oracle: bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import ep_inputs
+import oracle
+from gpu_util import announce, bf16_bits, bf16_to_dev, fp8_bits, fp8_to_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x5A5A
+
+
+def _setup(gpu, w, A=None, C=None, P=None):
+    A = w.expert_alignment if A is None else A
+    C = w.capacity if C is None else C
+    P = w.num_partitions if P is None else P
+    lay = gpu.ep_get_layout(to_dev(w.topk_idx), w.num_experts, A, P, C)
+    ref = oracle.get_layout(w.topk_idx, w.num_experts, A, P, C, rows_cap=lay.max_recv_rows)
+    return lay, ref
+
+
+@pytest.mark.parametrize("T,H,E,K,A,zero", [
+    (64, 256, 8, 2, 1, False),
+    (1000, 7168, 256, 8, 128, False),
+    (1000, 7168, 256, 8, 128, True),
+    (333, 1000, 32, 4, 3, True),     # ragged row: 125 vectors
+    (129, 8, 16, 3, 4, True),        # one vector per row
+    (65, 16384, 64, 2, 2, True),     # row wider than one wave chunk
+    (50, 2056, 128, 8, 1, False),
+])
+def test_dispatch_bf16(gpu, T, H, E, K, A, zero):
+    announce("dispatch bf16", T, H, E, K, A, zero)
+    w = ep_inputs.make_workload("prefill", T=T, H=H, E=E, K=K, A=A, drop_p=0.05)
+    lay, ref = _setup(gpu, w)
+    rows = lay.max_recv_rows
+    recv = torch.full((rows, H), 0, dtype=torch.bfloat16, device="cuda:0")
+    recv.view(torch.int16).fill_(SENTINEL)
+    recv, _, rw = gpu.ep_dispatch(bf16_to_dev(w.x), lay, to_dev(w.topk_weights),
+                                  zero_padding=zero, out=(recv, None, None))
+    init = np.full((ref.R, H), SENTINEL, np.uint16)
+    exp, _, exp_w = oracle.dispatch(w.x, ref, w.topk_weights, zero_padding=zero, recv_init=init)
+    got = bf16_bits(recv[:ref.R])
+    np.testing.assert_array_equal(got, exp)
+    np.testing.assert_array_equal(rw[:ref.R].cpu().numpy(), exp_w)
+    assert (bf16_bits(recv[ref.R:]) == SENTINEL).all()    # rows past R untouched
+    assert lay.check() == 0
+
+
+def test_dispatch_unweighted_recv_weights_are_one(gpu):
+    w = ep_inputs.make_workload("prefill", T=200, H=64, A=4)
+    lay, ref = _setup(gpu, w)
+    rw = torch.full((lay.max_recv_rows,), 7.0, dtype=torch.float32, device="cuda:0")
+    recv, _, rw = gpu.ep_dispatch(bf16_to_dev(w.x), lay, None, out=(None, None, rw))
+    exp_recv, _, exp_w = oracle.dispatch(w.x, ref, None)
+    used = ref.src_of_slot >= 0
+    np.testing.assert_array_equal(bf16_bits(recv[:ref.R])[used], exp_recv[used])
+    np.testing.assert_array_equal(rw[:ref.R].cpu().numpy(), exp_w)
+    assert set(np.unique(exp_w)) <= {0.0, 1.0}
+
+
+def test_dispatch_fixed_capacity_decode_full(gpu):
+    w = ep_inputs.make_workload("decode")
+    lay, ref = _setup(gpu, w)
+    recv = torch.empty((lay.max_recv_rows, w.hidden), dtype=torch.bfloat16, device="cuda:0")
+    recv.view(torch.int16).fill_(SENTINEL)
+    recv, _, rw = gpu.ep_dispatch(bf16_to_dev(w.x), lay, to_dev(w.topk_weights), zero_padding=True,
+                                  out=(recv, None, None))
+    exp, _, exp_w = oracle.dispatch(w.x, ref, w.topk_weights, zero_padding=True)
+    np.testing.assert_array_equal(bf16_bits(recv), exp)
+    np.testing.assert_array_equal(rw.cpu().numpy(), exp_w)
+
+
+def test_dispatch_capacity_overflow_drops_pairs(gpu):
+    w = ep_inputs.make_workload("decode", H=128)
+    lay, ref = _setup(gpu, w, C=4)
+    recv, _, _ = gpu.ep_dispatch(bf16_to_dev(w.x), lay, to_dev(w.topk_weights), zero_padding=True)
+    exp, _, _ = oracle.dispatch(w.x, ref, w.topk_weights, zero_padding=True)
+    np.testing.assert_array_equal(bf16_bits(recv), exp)
+    with pytest.raises(RuntimeError):
+        lay.check()
+
+
+def test_dispatch_recv_rows_bound(gpu):
+    """Receive buffers shorter than R: rows past them are skipped and flagged."""
+    w = ep_inputs.make_workload("prefill", T=300, H=64, A=8)
+    lay, ref = _setup(gpu, w)
+    n = ref.R // 2
+    recv, _, rw = gpu.ep_dispatch(bf16_to_dev(w.x), lay, to_dev(w.topk_weights), num_recv_rows=n,
+                                  zero_padding=True)
+    assert recv.shape[0] == n
+    exp, _, exp_w = oracle.dispatch(w.x, ref, w.topk_weights, zero_padding=True)
+    np.testing.assert_array_equal(bf16_bits(recv), exp[:n])
+    np.testing.assert_array_equal(rw.cpu().numpy(), exp_w[:n])
+    assert int(lay.status.item()) & oracle.RECV_OVERFLOW
+
+
+@pytest.mark.parametrize("G", [128, 16, 64, 512, "H"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_dispatch_fp8(gpu, G, fused):
+    T, H = 700, 7168 if G != "H" else 2048
+    G = H if G == "H" else G
+    announce("dispatch fp8", G, fused)
+    w = ep_inputs.make_workload("fp8", T=T, H=H, drop_p=0.03)
+    lay, ref = _setup(gpu, w)
+    q_ref, s_ref = oracle.cast_fp8(w.x, G)
+    if fused:
+        recv, rs, rw = gpu.ep_dispatch(bf16_to_dev(w.x), lay, to_dev(w.topk_weights),
+                                       recv_fp8=True, scale_group=G, zero_padding=True)
+    else:
+        recv, rs, rw = gpu.ep_dispatch((fp8_to_dev(q_ref), to_dev(s_ref)), lay,
+                                       to_dev(w.topk_weights), zero_padding=True)
+    exp, exp_s, exp_w = oracle.dispatch(q_ref, ref, w.topk_weights, x_scales=s_ref,
+                                        zero_padding=True)
+    np.testing.assert_array_equal(fp8_bits(recv[:ref.R]), exp)
+    np.testing.assert_array_equal(rs[:ref.R].cpu().numpy().view(np.uint32), exp_s.view(np.uint32))
+    np.testing.assert_array_equal(rw[:ref.R].cpu().numpy(), exp_w)
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128, 256, 512, "H"])
+def test_cast_fp8_groups(gpu, G):
+    H = 7168 if G != "H" else 4096
+    G = H if G == "H" else G
+    x = ep_inputs.bf16_normal(ep_inputs.make_rng(G), (257, H))
+    x[3, :G] = 0                              # floor
+    x[4, 7] = 0x7F7F                          # huge value in a group
+    x[5, :G] = 0x8001                         # negative subnormals only
+    x[6, 1::2] = 0x0001
+    announce("cast", G)
+    q, s = gpu.ep_cast_fp8(bf16_to_dev(x), G)
+    rq, rs = oracle.cast_fp8(x, G)
+    np.testing.assert_array_equal(fp8_bits(q), rq)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_cast_fp8_every_bf16_pattern(gpu):
+    """All finite bf16 patterns, each in groups whose amax is set by one of
+    several leading values, so every pattern is cast under many scales."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = bits[(bits & 0x7F80) != 0x7F80]
+    mags = np.abs(oracle.bf16_to_float(finite))
+    rows = []
+    for lead in (0x7F7F, 0x4380, 0x3F80, 0x3400, 0x0080):
+        lead_v = abs(float(oracle.bf16_to_float(np.array([lead], np.uint16))[0]))
+        vals = finite[mags <= lead_v]
+        pad = (-len(vals)) % 127
+        vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, 127)
+        rows.append(np.concatenate([np.full((len(vals), 1), lead, np.uint16), vals], axis=1))
+    groups = np.concatenate(rows)
+    groups = np.concatenate([groups, np.zeros(((-len(groups)) % 8, 128), np.uint16)])
+    x = groups.reshape(-1, 128 * 8)
+    q, s = gpu.ep_cast_fp8(bf16_to_dev(x), 128)
+    rq, rs = oracle.cast_fp8(x, 128)
+    np.testing.assert_array_equal(fp8_bits(q), rq)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_fused_equals_cast_then_dispatch_on_gpu(gpu):
+    w = ep_inputs.make_workload("fp8", T=513)
+    lay, ref = _setup(gpu, w)
+    x = bf16_to_dev(w.x)
+    q, s = gpu.ep_cast_fp8(x, 128)
+    a, a_s, _ = gpu.ep_dispatch((q, s), lay, zero_padding=True)
+    b, b_s, _ = gpu.ep_dispatch(x, lay, recv_fp8=True, zero_padding=True)
+    assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    assert torch.equal(a_s, b_s)
+
+
+def test_dispatch_reused_layout(gpu):
+    """A layout (handle) reused for a second dispatch with new rows."""
+    w = ep_inputs.make_workload("prefill", T=400, H=512)
+    lay, ref = _setup(gpu, w)
+    x2 = ep_inputs.bf16_normal(w.rng, (400, 512))
+    gpu.ep_dispatch(bf16_to_dev(w.x), lay)
+    recv, _, _ = gpu.ep_dispatch(bf16_to_dev(x2), lay, zero_padding=True)
+    exp, _, _ = oracle.dispatch(x2, ref, zero_padding=True)
+    np.testing.assert_array_equal(bf16_bits(recv[:ref.R]), exp)
+
+
+def test_dispatch_empty(gpu):
+    lay = gpu.ep_get_layout(torch.zeros((0, 8), dtype=torch.int64, device="cuda:0"), 256, 128)
+    recv, _, _ = gpu.ep_dispatch(torch.zeros((0, 7168), dtype=torch.bfloat16, device="cuda:0"),
+                                 lay, zero_padding=True)
+    torch.cuda.synchronize()
+    assert lay.num_recv_rows() == 0
