@@ -109,6 +109,8 @@ int ep_dispatch(const void *x, int x_dtype, const float *x_scales, int recv_dtyp
     a.x_scales = x_scales;
     a.topk_weights = topk_weights;
     a.dst = layout->dst_slot;
+    a.src_of_slot = layout->src_of_slot;
+    a.src_rows = p->max_recv_rows;
     a.counts = layout->num_tokens_per_expert;
     a.offsets = layout->expert_offset;
     a.status = layout->status;

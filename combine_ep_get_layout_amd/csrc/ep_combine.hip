@@ -21,7 +21,10 @@
 #include "ep_internal.h"
 
 #ifndef EP_COMBINE_VPL
-#define EP_COMBINE_VPL 8
+#define EP_COMBINE_VPL 2    // 16-byte vectors per lane per row chunk
+#endif
+#ifndef EP_COMBINE_U
+#define EP_COMBINE_U 8      // rows in flight per wave (0: by VPL)
 #endif
 
 namespace ep {
@@ -72,7 +75,8 @@ __device__ __forceinline__ void fma_bf16x8(float *acc, float w, ep_u32x4 v) {
 
 template <int VPL>
 __global__ void __launch_bounds__(kBlock) combine_kernel(CombineK a) {
-    constexpr int U = VPL >= 16 ? 1 : (VPL >= 8 ? 2 : (VPL >= 4 ? 4 : 8));
+    constexpr int U = EP_COMBINE_U > 0 ? EP_COMBINE_U
+                                       : (VPL >= 16 ? 1 : (VPL >= 8 ? 2 : (VPL >= 4 ? 4 : 8)));
     const int lane = __lane_id();
     const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
     const int t = gw / a.wpr;

@@ -108,10 +108,25 @@ __device__ __forceinline__ float scale_of(float amax) {
     return ap / 448.0f;
 }
 
+#ifndef EP_USE_NT_STORE
+#define EP_USE_NT_STORE 1
+#endif
+#ifndef EP_USE_NT_LOAD
+#define EP_USE_NT_LOAD 1
+#endif
+
+// Streaming accesses: rows are touched once per call, so they are issued with
+// the non-temporal hint and do not displace the routing tables in L2.
 template <typename T>
-__device__ __forceinline__ void store_nt(T *p, T v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt(T *p, T v) {
+    if (EP_USE_NT_STORE) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 template <typename T>
-__device__ __forceinline__ T load_nt(const T *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ T load_nt(const T *p) {
+    if (EP_USE_NT_LOAD) return __builtin_nontemporal_load(p);
+    return *p;
+}
 
 }  // namespace ep

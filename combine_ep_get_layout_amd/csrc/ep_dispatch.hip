@@ -24,6 +24,15 @@
 #ifndef EP_DISPATCH_VPL
 #define EP_DISPATCH_VPL 16
 #endif
+#ifndef EP_CAST_VPL
+#define EP_CAST_VPL 4
+#endif
+#ifndef EP_DISPATCH_ORDER
+#define EP_DISPATCH_ORDER 0   // 0: per token row, 1: per (token, k) pair, 2: per receive slot
+#endif
+#ifndef EP_DISPATCH_NT_STORE
+#define EP_DISPATCH_NT_STORE 0   // plain stores measured faster for the receive rows
+#endif
 
 namespace ep {
 
@@ -36,6 +45,8 @@ struct DispatchK {
     const float *x_scales;
     const float *w;
     const int32_t *dst;       // NULL: identity (cast only), slot = t, K = 1
+    const int32_t *src_of_slot;
+    int64_t src_rows;
     const int32_t *counts;
     const int32_t *offsets;
     int32_t *status;
@@ -58,6 +69,13 @@ struct DispatchK {
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / 64;
 
+// Receive-row stores: non-temporal or plain, one switch for every mode.
+template <typename T>
+__device__ __forceinline__ void row_store(T *p, T v) {
+    if (EP_DISPATCH_NT_STORE) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 __device__ __forceinline__ void pad_rows(const DispatchK &a, int pb) {
     const int e = pb / a.pad_slices;
     const int sl = pb - e * a.pad_slices;
@@ -78,7 +96,7 @@ __device__ __forceinline__ void pad_rows(const DispatchK &a, int pb) {
     const ep_u32x4 z = {0u, 0u, 0u, 0u};
     for (int64_t r = beg + sl; r < end; r += a.pad_slices) {
         ep_u32x4 *row = (ep_u32x4 *)(a.recv + r * (int64_t)a.out_row_bytes);
-        for (int v = threadIdx.x; v < nv_out; v += kBlock) store_nt(row + v, z);
+        for (int v = threadIdx.x; v < nv_out; v += kBlock) row_store(row + v, z);
         if (a.recv_scales)
             for (int j = threadIdx.x; j < a.ng; j += kBlock) a.recv_scales[r * a.ng + j] = 0.0f;
         if (a.recv_w && threadIdx.x == 0) a.recv_w[r] = 0.0f;
@@ -148,7 +166,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
 #pragma unroll
                 for (int i = 0; i < VPL; ++i) {
                     const int vi = v0 + i * 64 + lane;
-                    if (vi < a.nvec) store_nt(dstrow + vi, q[i]);
+                    if (vi < a.nvec) row_store(dstrow + vi, q[i]);
                 }
                 float *srow = a.recv_scales + (int64_t)slot * a.ng;
                 if (a.group_lanes > 0) {
@@ -169,7 +187,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
 #pragma unroll
                 for (int i = 0; i < VPL; ++i) {
                     const int vi = v0 + i * 64 + lane;
-                    if (vi < a.nvec) store_nt(dstrow + vi, v[i]);
+                    if (vi < a.nvec) row_store(dstrow + vi, v[i]);
                 }
                 if (MODE == kModeCopyFp8 && ci == 0) {
                     const float *ss = a.x_scales + (int64_t)t * a.ng;
@@ -181,11 +199,110 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
     }
 }
 
+// Copy modes, one wave per (pair, chunk): the wave reads its chunk of the
+// token row (the K waves of one token hit L2/MALL after the first) and writes
+// one destination.  More, shorter waves keep more stores in flight.
+template <int VPL, int MODE>
+__global__ void __launch_bounds__(kBlock) dispatch_pair_kernel(DispatchK a) {
+    if ((int)blockIdx.x >= a.n_tok_blocks) {
+        pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        return;
+    }
+    const int lane = __lane_id();
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int64_t pair = gw / a.wpr;
+    const int ci = (int)(gw - pair * a.wpr);
+    if (pair >= (int64_t)a.T * a.K) return;
+    const int t = (int)(pair / a.K);
+    int slot = a.dst[pair];
+    if ((int64_t)slot >= a.recv_rows) {
+        if (lane == 0 && ci == 0) atomicOr(a.status, kDevRecvOverflow);
+        slot = -1;
+    }
+    slot = wave_uniform(slot);
+    if (ci == 0 && a.recv_w && slot >= 0 && lane == 0) a.recv_w[slot] = a.w ? a.w[pair] : 1.0f;
+    if (slot < 0) return;
+    const int v0 = ci * VPL * 64;
+    ep_u32x4 v[VPL];
+    const ep_u32x4 *src = (const ep_u32x4 *)(a.x + (int64_t)t * a.in_row_bytes);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int vi = v0 + i * 64 + lane;
+        if (vi < a.nvec) v[i] = src[vi];
+    }
+    ep_u32x4 *dstrow = (ep_u32x4 *)(a.recv + (int64_t)slot * a.out_row_bytes);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int vi = v0 + i * 64 + lane;
+        if (vi < a.nvec) row_store(dstrow + vi, v[i]);
+    }
+    if (MODE == kModeCopyFp8 && ci == 0) {
+        const float *ss = a.x_scales + (int64_t)t * a.ng;
+        float *sd = a.recv_scales + (int64_t)slot * a.ng;
+        for (int j = lane; j < a.ng; j += 64) sd[j] = ss[j];
+    }
+}
+
+// Copy modes, one wave per (receive slot, chunk), in slot order: the stores
+// of neighbouring waves land on neighbouring rows, and each token row is
+// re-read K times from L2 / the memory-side cache instead of HBM.  Padding
+// slots are zeroed (and their weights cleared) inline.
+template <int VPL, int MODE>
+__global__ void __launch_bounds__(kBlock) dispatch_slot_kernel(DispatchK a) {
+    const int lane = __lane_id();
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int64_t slot = gw / a.wpr;
+    const int ci = (int)(gw - slot * a.wpr);
+    const int64_t R = a.offsets[a.E];
+    if (slot == 0 && ci == 0 && lane == 0 && R > a.recv_rows) atomicOr(a.status, kDevRecvOverflow);
+    if (slot >= R || slot >= a.recv_rows || slot >= a.src_rows) return;
+    const int src = wave_uniform(a.src_of_slot[slot]);
+    const int v0 = ci * VPL * 64;
+    ep_u32x4 *dstrow = (ep_u32x4 *)(a.recv + slot * a.out_row_bytes);
+    if (src < 0) {
+        if (ci == 0 && lane == 0 && a.recv_w) a.recv_w[slot] = 0.0f;
+        if (!a.zero_padding) return;
+        const ep_u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int vi = v0 + i * 64 + lane;
+            if (vi < a.nvec) row_store(dstrow + vi, z);
+        }
+        if (MODE == kModeCopyFp8 && ci == 0)
+            for (int j = lane; j < a.ng; j += 64) a.recv_scales[slot * a.ng + j] = 0.0f;
+        return;
+    }
+    const int t = src / a.K;
+    if (ci == 0 && lane == 0 && a.recv_w) a.recv_w[slot] = a.w ? a.w[src] : 1.0f;
+    ep_u32x4 v[VPL];
+    const ep_u32x4 *srow = (const ep_u32x4 *)(a.x + (int64_t)t * a.in_row_bytes);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int vi = v0 + i * 64 + lane;
+        if (vi < a.nvec) v[i] = srow[vi];
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int vi = v0 + i * 64 + lane;
+        if (vi < a.nvec) row_store(dstrow + vi, v[i]);
+    }
+    if (MODE == kModeCopyFp8 && ci == 0) {
+        const float *ss = a.x_scales + (int64_t)t * a.ng;
+        float *sd = a.recv_scales + slot * a.ng;
+        for (int j = lane; j < a.ng; j += 64) sd[j] = ss[j];
+    }
+}
+
 template <int MODE>
-hipError_t launch_mode(const DispatchK &k, int vpl, int grid, hipStream_t stream) {
-#define EP_CASE(V)                                                                        \
-    case V:                                                                               \
-        hipLaunchKernelGGL((dispatch_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
+hipError_t launch_mode(const DispatchK &k, int vpl, int grid, int order, hipStream_t stream) {
+#define EP_CASE(V)                                                                              \
+    case V:                                                                                     \
+        if (order == 1)                                                                         \
+            hipLaunchKernelGGL((dispatch_pair_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
+        else if (order == 2)                                                                    \
+            hipLaunchKernelGGL((dispatch_slot_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
+        else                                                                                    \
+            hipLaunchKernelGGL((dispatch_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
         break;
     switch (vpl) {
         EP_CASE(1) EP_CASE(2) EP_CASE(4) EP_CASE(7) EP_CASE(8) EP_CASE(14) EP_CASE(16)
@@ -208,7 +325,7 @@ int choose_vpl(int nvec, int limit) {
 }
 
 hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
-    int vpl = choose_vpl(k.nvec, vpl_limit);
+    int vpl = choose_vpl(k.nvec, mode == kModeCast ? EP_CAST_VPL : vpl_limit);
     if (mode == kModeCast && k.group_lanes == 0) {
         // one scale per row: the whole row must sit in one wave
         const int q = (k.nvec + 63) / 64;
@@ -217,15 +334,20 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     }
     k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
     if (k.wpr < 1) k.wpr = 1;
-    const int64_t waves = (int64_t)k.T * k.wpr;
+    const int order = (mode != kModeCast && k.dst != nullptr) ? EP_DISPATCH_ORDER : 0;
+    int64_t waves = (int64_t)k.T * (order == 1 ? k.K : 1) * k.wpr;
+    if (order == 2) {
+        waves = (k.recv_rows < k.src_rows ? k.recv_rows : k.src_rows) * k.wpr;
+        k.pad_slices = 0;
+    }
     k.n_tok_blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
     const int64_t grid = (int64_t)k.n_tok_blocks + (int64_t)k.E * k.pad_slices;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     switch (mode) {
-        case kModeCopy16: return launch_mode<kModeCopy16>(k, vpl, (int)grid, stream);
-        case kModeCopyFp8: return launch_mode<kModeCopyFp8>(k, vpl, (int)grid, stream);
-        default: return launch_mode<kModeCast>(k, vpl, (int)grid, stream);
+        case kModeCopy16: return launch_mode<kModeCopy16>(k, vpl, (int)grid, order, stream);
+        case kModeCopyFp8: return launch_mode<kModeCopyFp8>(k, vpl, (int)grid, order, stream);
+        default: return launch_mode<kModeCast>(k, vpl, (int)grid, 0, stream);
     }
 }
 
@@ -237,6 +359,8 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     k.x_scales = a.x_scales;
     k.w = a.topk_weights;
     k.dst = a.dst;
+    k.src_of_slot = a.src_of_slot;
+    k.src_rows = a.src_rows;
     k.counts = a.counts;
     k.offsets = a.offsets;
     k.status = a.status;

@@ -16,6 +16,7 @@ struct LayoutPlan {
     int tile_tokens;   // tokens per count tile (one workgroup)
     int num_tiles;     // ceil(T / tile_tokens)
     int block;         // threads per count workgroup (multiple of 64)
+    bool fused;        // count and slots in one cooperative launch when it fits
     int chunks_per_wave;
     size_t ws_tile_counts;  // byte offsets inside the workspace
     size_t ws_tile_part;
@@ -33,6 +34,8 @@ struct DispatchArgs {
     const float *x_scales;
     const float *topk_weights;
     const int32_t *dst;            // [T*K]
+    const int32_t *src_of_slot;    // [src_rows]
+    int64_t src_rows;              // the layout's max_recv_rows
     const int32_t *counts;         // [E]
     const int32_t *offsets;        // [E+1]
     int32_t *status;

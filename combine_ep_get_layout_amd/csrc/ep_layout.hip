@@ -1,27 +1,36 @@
 // Layout pass: routing histogram, padded per-expert offsets and the
 // source -> destination slot map.
 //
-// Defines what the DeepEP v2 test page ("DeepEP test target API reference",
+// Computes what the DeepEP v2 test page ("DeepEP test target API reference",
 // sec. 2.1 dispatch parameters, sec. 3.1 V1 layout tensors, sec. 4.2 align)
-// calls the layout derived from topk_idx, with the pairs of one expert kept in
-// token-major, then k, order (the scan order of "spark_model/layers/
-// ep_dispatch.rs").  Two kernels:
+// describes as the layout derived from topk_idx, with the pairs of one expert
+// kept in token-major, then k, order (the scan order of "spark_model/layers/
+// ep_dispatch.rs").  Two phases over tiles of consecutive tokens:
 //
-//   count  one workgroup per tile of tokens.  Each wave walks its share of
-//          the tile's flat (t, k) pairs in 64-pair chunks, in order.  Pairs of
-//          one chunk that name the same expert are found with one ballot per
-//          bit of the expert id (no atomics, so ranks are deterministic); the
-//          lowest lane of each group bumps the wave's LDS counter for that
-//          expert.  A per-expert scan over the waves turns wave-local ranks
-//          into tile ranks.  Outputs: per-tile counts [tiles, E], per-pair
-//          (expert, tile rank) packed into dst_slot, partition membership and
-//          per-tile partition counts.
-//   slots  one workgroup per tile again.  Each workgroup reduces the
-//          [tiles, E] counts column-wise (totals and the prefix of the tiles
-//          before its own), scans align(count, A) over experts into offsets,
-//          and rewrites its own pairs' packed ranks into receive slots,
-//          filling src_of_slot.  Workgroup 0 also publishes the per-expert
-//          counts, offsets, partition totals, cumulative stats and status.
+//   count  each wave walks its share of the tile's flat (t, k) pairs in
+//          64-pair chunks, in order.  Pairs of one chunk that name the same
+//          expert are found with one ballot per bit of the expert id (no
+//          atomics, so ranks are deterministic); the lowest lane of each group
+//          bumps the wave's LDS counter for that expert.  A per-expert scan
+//          over the waves turns wave-local ranks into tile ranks.  Outputs:
+//          per-tile counts [tiles, E], partition membership and per-tile
+//          partition counts; each pair's (expert, tile rank) stays with the
+//          thread that found it.
+//   slots  each tile reduces the [tiles, E] counts column-wise (totals and
+//          the prefix over the tiles before it), scans align(count, A) over
+//          experts into offsets, and turns its pairs' ranks into receive
+//          slots, filling src_of_slot.  Designated tiles also publish the
+//          per-expert counts and offsets, the partition totals, the
+//          cumulative stats and the status word.
+//
+// When the tiles fit on the chip at once (the usual case) both phases run in
+// one cooperative launch with a grid barrier between them, so the pair ranks
+// never leave registers.  Otherwise (E above kMaxFusedExperts, a grid too big
+// to be co-resident, or a stream under graph capture) they run as two
+// kernels and the ranks travel through dst_slot, packed as
+// (e << kRankBits) | rank.
+#include <hip/hip_cooperative_groups.h>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -29,49 +38,94 @@ namespace ep {
 
 namespace {
 
-__global__ void __launch_bounds__(1024)
-layout_count_kernel(const int64_t *__restrict__ idx, int T, int K, int E, int P, int m,
-                    int tile_tokens, int32_t *__restrict__ packed, uint8_t *__restrict__ in_part,
-                    int32_t *__restrict__ tile_counts, int32_t *__restrict__ tile_part,
-                    int32_t *__restrict__ tile_flags) {
-    extern __shared__ int32_t lds[];
-    __shared__ int32_t s_flag;
-    const int NW = blockDim.x >> 6;
-    int32_t *wcnt = lds;           // [NW][E]
-    int32_t *pcnt = lds + NW * E;  // [P]
+constexpr int kCountBlock = 256;   // count workgroup of the two-kernel tiling: 4 waves
+constexpr int kSlotsBlock = 1024;  // slots workgroup, and the fused tiling: 16 waves
+constexpr int kReduceBatch = 8;    // loads in flight per thread in column_sums
+constexpr int kMaxFusedExperts = 512;
+#ifndef EP_LAYOUT_FUSED
+#define EP_LAYOUT_FUSED 0      // cooperative single launch (measured slower to launch)
+#endif
+#ifndef EP_LAYOUT_WAVES
+#define EP_LAYOUT_WAVES 4      // waves per count tile in the two-kernel path
+#endif
+constexpr int kRedInts = 2 * 4 * kSlotsBlock;
+
+struct CountArgs {
+    const int64_t *idx;
+    int T, K, E, P, m;
+    int tile_tokens;
+    int tile_pairs_max;
+    uint8_t *in_part;
+    int32_t *tile_counts;
+    int32_t *tile_part;
+    int32_t *tile_flags;
+};
+
+struct SlotsArgs {
+    int T, K, E, A, P, C;
+    int tile_tokens;
+    int num_tiles;
+    int64_t max_rows;
+    const int32_t *tile_counts;
+    const int32_t *tile_part;
+    const int32_t *tile_flags;
+    int32_t *count_out;
+    int32_t *offset_out;
+    int32_t *part_out;
+    int32_t *dst;
+    int32_t *src_of_slot;
+    int32_t *status;
+    int32_t *cum_stats;
+};
+
+// Count phase for tile blockIdx.x.  LDS: [waves][E] counters, [tile pairs]
+// expert ids, [P] partition counters.  On return rank[c] / ex[c] hold the
+// tile rank and expert of pair (wave * cpw + c) * 64 + lane (ex = -1: none).
+__device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
+                            int rank[kMaxChunksPerWave], int ex[kMaxChunksPerWave], int &cpw) {
+    const int nw = blockDim.x >> 6;
+    const int E = a.E;
+    int32_t *wcnt = lds;                   // [nw][E]
+    int32_t *pe = lds + nw * E;            // [tile pairs]
+    int32_t *pcnt = pe + a.tile_pairs_max; // [P]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int tile = blockIdx.x;
-    const int t0 = tile * tile_tokens;
-    const int t1 = min(T, t0 + tile_tokens);
-    const int64_t p0 = (int64_t)t0 * K;
-    const int npairs = (t1 - t0) * K;
+    const int t0 = tile * a.tile_tokens;
+    const int t1 = min(a.T, t0 + a.tile_tokens);
+    const int64_t p0 = (int64_t)t0 * a.K;
+    const int npairs = (t1 - t0) * a.K;
     const int nchunks = (npairs + 63) >> 6;
-    const int cpw = (nchunks + NW - 1) / NW;
+    cpw = (nchunks + nw - 1) / nw;
 
-    for (int i = tid; i < NW * E; i += blockDim.x) wcnt[i] = 0;
-    for (int i = tid; i < P; i += blockDim.x) pcnt[i] = 0;
-    if (tid == 0) s_flag = 0;
+    // Issue every routing load of this wave before touching LDS.
+    int64_t raw[kMaxChunksPerWave];
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerWave; ++c) {
+        const int p = (w * cpw + c) * 64 + lane;
+        raw[c] = (c < cpw && p < npairs) ? a.idx[p0 + p] : -1;
+    }
+    for (int i = tid; i < nw * E; i += blockDim.x) wcnt[i] = 0;
+    for (int i = tid; i < a.P; i += blockDim.x) pcnt[i] = 0;
+    if (tid == 0) *s_flag = 0;
     __syncthreads();
 
     const int bits = E > 1 ? 32 - __clz(E - 1) : 0;
     int32_t *mycnt = wcnt + w * E;
     int flag = 0;
-    int rank[kMaxChunksPerWave];
-    int ex[kMaxChunksPerWave];
 #pragma unroll
     for (int c = 0; c < kMaxChunksPerWave; ++c) {
         rank[c] = 0;
         ex[c] = -1;
         if (c < cpw) {
             const int p = (w * cpw + c) * 64 + lane;
+            const int64_t v = raw[c];
             int e = -1;
-            if (p < npairs) {
-                const int64_t v = idx[p0 + p];
-                if (v >= 0 && v < E) e = (int)v;
-                else if (v != -1) flag = 1;
-            }
+            if (v >= 0 && v < E) e = (int)v;
+            else if (v != -1) flag = 1;
+            if (p < npairs) pe[p] = e;
+            // Lanes naming the same expert: intersect one ballot per id bit.
             const uint64_t active = __ballot(e >= 0);
             uint64_t match = active;
             for (int b = 0; b < bits; ++b) {
@@ -88,8 +142,7 @@ layout_count_kernel(const int64_t *__restrict__ idx, int T, int K, int E, int P,
                 old = mycnt[e];
                 mycnt[e] = old + n;
             }
-            const int base = __shfl(old, leader);
-            rank[c] = base + r;
+            rank[c] = __shfl(old, leader) + r;
             ex[c] = e;
         }
     }
@@ -98,35 +151,28 @@ layout_count_kernel(const int64_t *__restrict__ idx, int T, int K, int E, int P,
     // Per-expert exclusive scan over the waves: wave bases inside the tile.
     for (int e = tid; e < E; e += blockDim.x) {
         int run = 0;
-        for (int ww = 0; ww < NW; ++ww) {
+        for (int ww = 0; ww < nw; ++ww) {
             const int c = wcnt[ww * E + e];
             wcnt[ww * E + e] = run;
             run += c;
         }
-        tile_counts[(int64_t)tile * E + e] = run;
+        a.tile_counts[(int64_t)tile * E + e] = run;
     }
     __syncthreads();
-
 #pragma unroll
-    for (int c = 0; c < kMaxChunksPerWave; ++c) {
-        if (c < cpw) {
-            const int p = (w * cpw + c) * 64 + lane;
-            if (p < npairs) {
-                const int e = ex[c];
-                packed[p0 + p] = e >= 0 ? ((e << kRankBits) | (rank[c] + mycnt[e])) : -1;
-            }
-        }
-    }
+    for (int c = 0; c < kMaxChunksPerWave; ++c)
+        if (c < cpw && ex[c] >= 0) rank[c] += mycnt[ex[c]];
 
-    // Partition membership, one thread per token of the tile.
+    // Partition membership, one thread per token, from the ids staged in LDS.
+    const int K = a.K, P = a.P, m = a.m;
     for (int tt = tid; tt < t1 - t0; tt += blockDim.x) {
-        const int64_t t = t0 + tt;
-        uint8_t *row = in_part + t * P;
+        uint8_t *row = a.in_part + (int64_t)(t0 + tt) * P;
+        const int32_t *ids = pe + tt * K;
         if (P <= 64) {
             uint64_t mask = 0;
             for (int k = 0; k < K; ++k) {
-                const int64_t v = idx[t * K + k];
-                if (v >= 0 && v < E) mask |= 1ull << (int)(v / m);
+                const int e = ids[k];
+                if (e >= 0) mask |= 1ull << (e / m);
             }
             for (int q = 0; q < P; ++q) row[q] = (uint8_t)((mask >> q) & 1ull);
             while (mask) {
@@ -137,19 +183,89 @@ layout_count_kernel(const int64_t *__restrict__ idx, int T, int K, int E, int P,
         } else {
             for (int q = 0; q < P; ++q) {
                 int hit = 0;
-                for (int k = 0; k < K; ++k) {
-                    const int64_t v = idx[t * K + k];
-                    hit |= (v >= q * (int64_t)m && v < (q + 1) * (int64_t)m);
-                }
+                for (int k = 0; k < K; ++k) hit |= (ids[k] >= 0 && ids[k] / m == q);
                 row[q] = (uint8_t)hit;
                 if (hit) atomicAdd(&pcnt[q], 1);
             }
         }
     }
-    if (flag) atomicOr(&s_flag, kDevBadExpert);
+    if (flag) atomicOr(s_flag, kDevBadExpert);
     __syncthreads();
-    for (int q = tid; q < P; q += blockDim.x) tile_part[(int64_t)tile * P + q] = pcnt[q];
-    if (tid == 0) tile_flags[tile] = s_flag;
+    for (int q = tid; q < P; q += blockDim.x) a.tile_part[(int64_t)tile * P + q] = pcnt[q];
+    if (tid == 0) a.tile_flags[tile] = *s_flag;
+}
+
+// Column sums of a row-major [rows, cols] int32 matrix in global memory:
+// tot[c] = sum over all rows, pre[c] = sum over rows < my_row (both LDS).
+// Threads split the columns (4 at a time when cols % 4 == 0) and stride over
+// the rows in batches of kReduceBatch independent loads, so the whole matrix
+// is requested in a few round trips; at most 16 partials per column are
+// combined through red (LDS, kRedInts ints).  Ends with a barrier.
+__device__ void column_sums(const int32_t *__restrict__ mat, int rows, int cols, int my_row,
+                            int32_t *tot, int32_t *pre, int32_t *red) {
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int vec = (cols & 3) == 0 ? 4 : 1;
+    const int Q = cols / vec;                           // column groups
+    const int G = Q <= nt ? min(nt / Q, 16) : 1;        // row strides (partials per column)
+    for (int q0 = 0; q0 < Q; q0 += nt) {
+        const int span = Q <= nt ? Q : nt;
+        const int g = tid / span;
+        const int q = q0 + tid - g * span;
+        int at[4] = {0, 0, 0, 0}, ap[4] = {0, 0, 0, 0};
+        if (g < G && q < Q) {
+            for (int r0 = g; r0 < rows; r0 += G * kReduceBatch) {
+                int v[kReduceBatch][4];
+#pragma unroll
+                for (int u = 0; u < kReduceBatch; ++u) {
+                    const int r = r0 + u * G;
+                    if (r < rows) {
+                        const int32_t *src = mat + (int64_t)r * cols + q * vec;
+                        if (vec == 4) {
+                            const int4 x = *(const int4 *)src;
+                            v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+                        } else {
+                            v[u][0] = src[0]; v[u][1] = v[u][2] = v[u][3] = 0;
+                        }
+                    } else {
+                        v[u][0] = v[u][1] = v[u][2] = v[u][3] = 0;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kReduceBatch; ++u) {
+                    const int r = r0 + u * G;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        at[j] += v[u][j];
+                        ap[j] += r < my_row ? v[u][j] : 0;
+                    }
+                }
+            }
+        }
+        if (G > 1) {
+            if (g < G && q < Q)
+                for (int j = 0; j < vec; ++j) {
+                    red[g * cols + q * vec + j] = at[j];
+                    red[(G + g) * cols + q * vec + j] = ap[j];
+                }
+            __syncthreads();
+            for (int c = tid; c < cols; c += nt) {
+                int s = 0, sp = 0;
+                for (int g2 = 0; g2 < G; ++g2) {
+                    s += red[g2 * cols + c];
+                    sp += red[(G + g2) * cols + c];
+                }
+                tot[c] = s;
+                pre[c] = sp;
+            }
+        } else if (q < Q) {
+            for (int j = 0; j < vec; ++j) {
+                tot[q * vec + j] = at[j];
+                pre[q * vec + j] = ap[j];
+            }
+        }
+    }
+    __syncthreads();
 }
 
 // Exclusive scan in place over a[0..n) in LDS; every thread of the block
@@ -193,64 +309,39 @@ __device__ int block_exclusive_scan(int32_t *a, int n, int32_t *s_wave) {
     return total;
 }
 
-__global__ void __launch_bounds__(1024)
-layout_slots_kernel(int T, int K, int E, int A, int P, int C, int tile_tokens, int num_tiles,
-                    int64_t max_rows, const int32_t *__restrict__ tile_counts,
-                    const int32_t *__restrict__ tile_part, const int32_t *__restrict__ tile_flags,
-                    int32_t *__restrict__ count_out, int32_t *__restrict__ offset_out,
-                    int32_t *__restrict__ part_out, int32_t *__restrict__ dst,
-                    int32_t *__restrict__ src_of_slot, int32_t *__restrict__ status,
-                    int32_t *__restrict__ cum_stats) {
-    extern __shared__ int32_t lds[];
-    __shared__ int32_t s_wave[17];
-    __shared__ int32_t s_flags;
-    int32_t *s_tot = lds;               // [E]
-    int32_t *s_base = lds + E;          // [E]
-    int32_t *s_off = lds + 2 * E;       // [E+1]
-    int32_t *s_red = lds + 3 * E + 1;   // [2][G][E] when G > 1
+// Slots phase for tile blockIdx.x (blockDim == kSlotsBlock).  pv[i] holds a
+// packed (e << kRankBits) | tile rank (or -1) for flat pair pidx[i] (or -1).
+// The tiles that publish results are distinct where possible, so their extra
+// global reads overlap instead of queueing in one workgroup.
+__device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_wave, int32_t *s_flags,
+                            const int pv[4], const int64_t pidx[4]) {
+    const int E = a.E, P = a.P, C = a.C, A = a.A;
+    int32_t *s_tot = lds;                    // [E]
+    int32_t *s_base = s_tot + E;             // [E]
+    int32_t *s_off = s_base + E;             // [E+1]
+    int32_t *s_ptot = s_off + E + 1;         // [P]
+    int32_t *s_pdummy = s_ptot + P;          // [P]
+    int32_t *s_red = s_pdummy + P;           // [kRedInts]
     const int tid = threadIdx.x;
     const int tile = blockIdx.x;
-    const int G = E <= (int)blockDim.x ? (int)blockDim.x / E : 1;
+    const int nt = a.num_tiles > 0 ? a.num_tiles : 1;
+    const bool pub_counts = tile == 0;
+    const bool pub_status = tile == 1 % nt;
+    const bool pub_parts = tile == 2 % nt;
+    const bool pub_stats = tile == 3 % nt;
 
-    // Column totals over all tiles, and the prefix over tiles before ours.
-    if (G > 1) {
-        const int g = tid / E;
-        const int e = tid - g * E;
-        if (g < G) {
-            int tot = 0, pre = 0;
-            for (int tl = g; tl < num_tiles; tl += G) {
-                const int c = tile_counts[(int64_t)tl * E + e];
-                tot += c;
-                pre += tl < tile ? c : 0;
-            }
-            s_red[g * E + e] = tot;
-            s_red[(G + g) * E + e] = pre;
-        }
-        __syncthreads();
-        for (int e2 = tid; e2 < E; e2 += blockDim.x) {
-            int tot = 0, pre = 0;
-            for (int g2 = 0; g2 < G; ++g2) {
-                tot += s_red[g2 * E + e2];
-                pre += s_red[(G + g2) * E + e2];
-            }
-            s_tot[e2] = tot;
-            s_base[e2] = pre;
-        }
-    } else {
-        for (int e = tid; e < E; e += blockDim.x) {
-            int tot = 0, pre = 0;
-            for (int tl = 0; tl < num_tiles; ++tl) {
-                const int c = tile_counts[(int64_t)tl * E + e];
-                tot += c;
-                pre += tl < tile ? c : 0;
-            }
-            s_tot[e] = tot;
-            s_base[e] = pre;
-        }
+    int fl = 0;
+    if (pub_status) {
+        if (tid == 0) *s_flags = 0;
+        for (int tl = tid; tl < a.num_tiles; tl += blockDim.x) fl |= a.tile_flags[tl];
     }
-    __syncthreads();
+    int stats[4] = {0, 0, 0, 0};
+    if (pub_stats && a.cum_stats)
+        for (int i = 0; i < 4; ++i)
+            if (tid + i * (int)blockDim.x < E) stats[i] = a.cum_stats[tid + i * blockDim.x];
 
-    // Offsets: exclusive scan of align(count, A), or e*C in fixed mode.
+    column_sums(a.tile_counts, a.num_tiles, E, tile, s_tot, s_base, s_red);
+
     int R;
     if (C == 0) {
         for (int e = tid; e < E; e += blockDim.x) s_off[e] = (s_tot[e] + A - 1) / A * A;
@@ -263,61 +354,124 @@ layout_slots_kernel(int T, int K, int E, int A, int P, int C, int tile_tokens, i
     }
     __syncthreads();
 
-    if (tile == 0) {
-        if (tid == 0) s_flags = 0;
-        __syncthreads();
-        int fl = 0;
-        for (int tl = tid; tl < num_tiles; tl += blockDim.x) fl |= tile_flags[tl];
+    if (pub_counts) {
         for (int e = tid; e < E; e += blockDim.x) {
-            const int c = s_tot[e];
-            count_out[e] = c;
-            offset_out[e] = s_off[e];
-            if (cum_stats) cum_stats[e] += c;
-            if (C > 0 && c > C) fl |= kDevCapacity;
+            a.count_out[e] = s_tot[e];
+            a.offset_out[e] = s_off[e];
         }
-        if (tid == 0) {
-            offset_out[E] = R;
-            if ((int64_t)R > max_rows) fl |= kDevRecvOverflow;
+        if (tid == 0) a.offset_out[E] = R;
+    }
+    if (pub_stats && a.cum_stats) {
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + i * (int)blockDim.x;
+            if (e < E) a.cum_stats[e] = stats[i] + s_tot[e];
         }
-        for (int q = tid; q < P; q += blockDim.x) {
-            int s = 0;
-            for (int tl = 0; tl < num_tiles; ++tl) s += tile_part[(int64_t)tl * P + q];
-            part_out[q] = s;
-        }
-        if (fl) atomicOr(&s_flags, fl);
+    }
+    if (pub_status) {
+        for (int e = tid; e < E; e += blockDim.x)
+            if (C > 0 && s_tot[e] > C) fl |= kDevCapacity;
+        if (tid == 0 && (int64_t)R > a.max_rows) fl |= kDevRecvOverflow;
+        if (fl) atomicOr(s_flags, fl);
         __syncthreads();
-        if (tid == 0) *status = s_flags;
+        if (tid == 0) *a.status = *s_flags;
+    }
+    if (pub_parts) {
+        column_sums(a.tile_part, a.num_tiles, P, 0, s_ptot, s_pdummy, s_red);
+        for (int q = tid; q < P; q += blockDim.x) a.part_out[q] = s_ptot[q];
     }
 
     // Slots of this tile's pairs.
-    const int t0 = tile * tile_tokens;
-    const int t1 = min(T, t0 + tile_tokens);
-    const int64_t p0 = (int64_t)t0 * K;
-    const int64_t p1 = (int64_t)t1 * K;
-    for (int64_t p = p0 + tid; p < p1; p += blockDim.x) {
-        const int v = dst[p];
-        if (v < 0) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int v = pv[i];
+        const int64_t p = pidx[i];
+        if (p < 0) continue;
+        if (v < 0) {
+            a.dst[p] = -1;
+            continue;
+        }
         const int e = v >> kRankBits;
         const int j = s_base[e] + (v & ((1 << kRankBits) - 1));
         if (C > 0 && j >= C) {
-            dst[p] = -1;
+            a.dst[p] = -1;
             continue;
         }
         const int slot = s_off[e] + j;
-        dst[p] = slot;
-        if ((int64_t)slot < max_rows) src_of_slot[slot] = (int32_t)p;
+        a.dst[p] = slot;
+        if ((int64_t)slot < a.max_rows) a.src_of_slot[slot] = (int32_t)p;
     }
 
     // Padding slots of the experts this workgroup owns (e = tile mod tiles).
-    const int owner_step = num_tiles > 0 ? num_tiles : 1;
-    for (int e = tile; e < E; e += owner_step) {
+    for (int e = tile; e < E; e += nt) {
         const int c = s_tot[e];
         const int used = C > 0 ? min(c, C) : c;
         const int64_t beg = (int64_t)s_off[e] + used;
         int64_t end = C > 0 ? (int64_t)s_off[e] + C : (int64_t)s_off[e + 1];
-        if (end > max_rows) end = max_rows;
-        for (int64_t s = beg + tid; s < end; s += blockDim.x) src_of_slot[s] = -1;
+        if (end > a.max_rows) end = a.max_rows;
+        for (int64_t s = beg + tid; s < end; s += blockDim.x) a.src_of_slot[s] = -1;
     }
+}
+
+__global__ void __launch_bounds__(kSlotsBlock)
+layout_count_kernel(CountArgs a, int32_t *__restrict__ packed) {
+    extern __shared__ int32_t lds[];
+    __shared__ int32_t s_flag;
+    int rank[kMaxChunksPerWave], ex[kMaxChunksPerWave], cpw;
+    count_phase(a, lds, &s_flag, rank, ex, cpw);
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * a.tile_tokens;
+    const int npairs = (min(a.T, t0 + a.tile_tokens) - t0) * a.K;
+    const int64_t p0 = (int64_t)t0 * a.K;
+#pragma unroll
+    for (int c = 0; c < kMaxChunksPerWave; ++c) {
+        const int p = (w * cpw + c) * 64 + lane;
+        if (c < cpw && p < npairs)
+            packed[p0 + p] = ex[c] >= 0 ? ((ex[c] << kRankBits) | rank[c]) : -1;
+    }
+}
+
+__global__ void __launch_bounds__(kSlotsBlock) layout_slots_kernel(SlotsArgs a) {
+    extern __shared__ int32_t lds[];
+    __shared__ int32_t s_wave[kSlotsBlock / 64 + 1];
+    __shared__ int32_t s_flags;
+    const int t0 = blockIdx.x * a.tile_tokens;
+    const int64_t p0 = (int64_t)t0 * a.K;
+    const int npairs = a.num_tiles > 0 ? (min(a.T, t0 + a.tile_tokens) - t0) * a.K : 0;
+    int pv[4];
+    int64_t pidx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = threadIdx.x + i * kSlotsBlock;
+        pidx[i] = p < npairs ? p0 + p : -1;
+        pv[i] = p < npairs ? a.dst[p0 + p] : -1;
+    }
+    slots_phase(a, lds, s_wave, &s_flags, pv, pidx);
+}
+
+__global__ void __launch_bounds__(kSlotsBlock) layout_fused_kernel(CountArgs ca, SlotsArgs sa) {
+    extern __shared__ int32_t lds[];
+    __shared__ int32_t s_wave[kSlotsBlock / 64 + 1];
+    __shared__ int32_t s_flag;
+    int rank[kMaxChunksPerWave], ex[kMaxChunksPerWave], cpw;
+    count_phase(ca, lds, &s_flag, rank, ex, cpw);
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * ca.tile_tokens;
+    const int npairs = (min(ca.T, t0 + ca.tile_tokens) - t0) * ca.K;
+    const int64_t p0 = (int64_t)t0 * ca.K;
+    int pv[4];
+    int64_t pidx[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int p = (w * cpw + c) * 64 + lane;
+        const bool ok = c < kMaxChunksPerWave && c < cpw && p < npairs;
+        pidx[c] = ok ? p0 + p : -1;
+        pv[c] = ok && ex[c] >= 0 ? ((ex[c] << kRankBits) | rank[c]) : -1;
+    }
+    // Every tile's counts are in memory before any tile reads them.
+    cooperative_groups::this_grid().sync();
+    slots_phase(sa, lds, s_wave, &s_flag, pv, pidx);
 }
 
 }  // namespace
@@ -333,15 +487,19 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
     L.P = p->num_partitions;
     L.C = p->capacity;
     L.max_rows = p->max_recv_rows;
-    int nw = 12288 / L.E;
-    nw = nw > 16 ? 16 : (nw < 1 ? 1 : nw);
-    L.block = nw * 64;
     const int64_t pairs = (int64_t)L.T * L.K;
-    const int64_t target_tile_pairs = (pairs + 31) / 32;
-    int64_t cpw = (target_tile_pairs + (int64_t)nw * 64 - 1) / ((int64_t)nw * 64);
+    L.fused = EP_LAYOUT_FUSED && L.E <= kMaxFusedExperts;
+    L.block = (L.fused || (EP_LAYOUT_WAVES == 16 && L.E <= kMaxFusedExperts)) ? kSlotsBlock
+                                                                          : kCountBlock;
+    const int64_t per_round = L.block;   // pairs when every wave takes one 64-pair chunk
+    // Chunks per wave: enough tiles to spread the count over the chip, few
+    // enough that each tile reduces the [tiles, E] count matrix in one or two
+    // round trips (16-wave tiles: ~32 of them; 4-wave tiles: ~256).
+    const int64_t target_tiles = L.block == kSlotsBlock ? 32 : 256;
+    int64_t cpw = (pairs + target_tiles * per_round - 1) / (target_tiles * per_round);
     cpw = cpw < 1 ? 1 : (cpw > kMaxChunksPerWave ? kMaxChunksPerWave : cpw);
     L.chunks_per_wave = (int)cpw;
-    int tt = (int)((int64_t)nw * 64 * cpw / L.K);
+    const int tt = (int)(per_round * cpw / L.K);
     if (tt < 1) return false;
     L.tile_tokens = tt;
     L.num_tiles = L.T > 0 ? (L.T + tt - 1) / tt : 0;
@@ -357,27 +515,63 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
 hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_layout *lay,
                          int32_t *cum_stats, void *workspace, hipStream_t stream) {
     char *ws = (char *)workspace;
-    int32_t *tile_counts = (int32_t *)(ws + L.ws_tile_counts);
-    int32_t *tile_part = (int32_t *)(ws + L.ws_tile_part);
-    int32_t *tile_flags = (int32_t *)(ws + L.ws_tile_flags);
-    const int m = L.E / L.P;
+    CountArgs ca;
+    ca.idx = topk_idx;
+    ca.T = L.T;
+    ca.K = L.K;
+    ca.E = L.E;
+    ca.P = L.P;
+    ca.m = L.E / L.P;
+    ca.tile_tokens = L.tile_tokens;
+    ca.tile_pairs_max = L.tile_tokens * L.K;
+    ca.in_part = lay->is_token_in_partition;
+    ca.tile_counts = (int32_t *)(ws + L.ws_tile_counts);
+    ca.tile_part = (int32_t *)(ws + L.ws_tile_part);
+    ca.tile_flags = (int32_t *)(ws + L.ws_tile_flags);
+    SlotsArgs sa;
+    sa.T = L.T;
+    sa.K = L.K;
+    sa.E = L.E;
+    sa.A = L.A;
+    sa.P = L.P;
+    sa.C = L.C;
+    sa.tile_tokens = L.tile_tokens;
+    sa.num_tiles = L.num_tiles;
+    sa.max_rows = L.max_rows;
+    sa.tile_counts = ca.tile_counts;
+    sa.tile_part = ca.tile_part;
+    sa.tile_flags = ca.tile_flags;
+    sa.count_out = lay->num_tokens_per_expert;
+    sa.offset_out = lay->expert_offset;
+    sa.part_out = lay->num_tokens_per_partition;
+    sa.dst = lay->dst_slot;
+    sa.src_of_slot = lay->src_of_slot;
+    sa.status = lay->status;
+    sa.cum_stats = cum_stats;
+
+    const size_t lds_count = ((size_t)(L.block / 64) * L.E + ca.tile_pairs_max + L.P) * 4;
+    const size_t lds_slots = ((size_t)3 * L.E + 1 + 2 * L.P + kRedInts) * 4;
+
+    if (L.fused && L.num_tiles > 0) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
+            const size_t lds = lds_count > lds_slots ? lds_count : lds_slots;
+            void *args[] = {&ca, &sa};
+            const hipError_t err = hipLaunchCooperativeKernel(
+                (const void *)layout_fused_kernel, dim3(L.num_tiles), dim3(kSlotsBlock), args,
+                (unsigned)lds, stream);
+            if (err == hipSuccess) return hipSuccess;
+            (void)hipGetLastError();   // not co-resident: two launches instead
+        }
+    }
     if (L.num_tiles > 0) {
-        const size_t lds = ((size_t)(L.block / 64) * L.E + L.P) * sizeof(int32_t);
-        hipLaunchKernelGGL(layout_count_kernel, dim3(L.num_tiles), dim3(L.block), lds, stream,
-                           topk_idx, L.T, L.K, L.E, L.P, m, L.tile_tokens, lay->dst_slot,
-                           lay->is_token_in_partition, tile_counts, tile_part, tile_flags);
-        hipError_t err = hipGetLastError();
+        hipLaunchKernelGGL(layout_count_kernel, dim3(L.num_tiles), dim3(L.block), lds_count, stream,
+                           ca, lay->dst_slot);
+        const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    const int slots_block = 1024;
-    const int G = L.E <= slots_block ? slots_block / L.E : 1;
-    const size_t lds2 = (size_t)(3 * L.E + 1 + (G > 1 ? 2 * G * L.E : 0)) * sizeof(int32_t);
-    const int grid2 = L.num_tiles > 0 ? L.num_tiles : 1;
-    hipLaunchKernelGGL(layout_slots_kernel, dim3(grid2), dim3(slots_block), lds2, stream, L.T, L.K,
-                       L.E, L.A, L.P, L.C, L.tile_tokens, L.num_tiles, L.max_rows, tile_counts,
-                       tile_part, tile_flags, lay->num_tokens_per_expert, lay->expert_offset,
-                       lay->num_tokens_per_partition, lay->dst_slot, lay->src_of_slot, lay->status,
-                       cum_stats);
+    hipLaunchKernelGGL(layout_slots_kernel, dim3(L.num_tiles > 0 ? L.num_tiles : 1),
+                       dim3(kSlotsBlock), lds_slots, stream, sa);
     return hipGetLastError();
 }
 
