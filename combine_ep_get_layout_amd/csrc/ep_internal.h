@@ -18,9 +18,8 @@ struct LayoutPlan {
     int block;         // threads per count workgroup (multiple of 64)
     bool fused;        // count and slots in one cooperative launch when it fits
     int chunks_per_wave;
-    size_t ws_tile_counts;  // byte offsets inside the workspace
-    size_t ws_tile_part;
-    size_t ws_tile_flags;
+    int row_stride;         // ints per tile row: E + P + 1 rounded up to 4
+    size_t ws_tile_counts;  // byte offset inside the workspace
     size_t ws_bytes;
 };
 

@@ -13,11 +13,11 @@
 //          atomics, so ranks are deterministic); the lowest lane of each group
 //          bumps the wave's LDS counter for that expert.  A per-expert scan
 //          over the waves turns wave-local ranks into tile ranks.  Outputs:
-//          per-tile counts [tiles, E], partition membership and per-tile
-//          partition counts; each pair's (expert, tile rank) stays with the
-//          thread that found it.
-//   slots  each tile reduces the [tiles, E] counts column-wise (totals and
-//          the prefix over the tiles before it), scans align(count, A) over
+//          partition membership and one row per tile of [E expert counts |
+//          P partition token counts | bad-id flag]; each pair's (expert, tile
+//          rank) stays with the thread that found it.
+//   slots  each tile reduces the per-tile rows column-wise (totals and the
+//          prefix over the tiles before it) in one pass, scans align(count, A) over
 //          experts into offsets, and turns its pairs' ranks into receive
 //          slots, filling src_of_slot.  Designated tiles also publish the
 //          per-expert counts and offsets, the partition totals, the
@@ -45,6 +45,9 @@ constexpr int kMaxFusedExperts = 512;
 #ifndef EP_LAYOUT_FUSED
 #define EP_LAYOUT_FUSED 0      // cooperative single launch (measured slower to launch)
 #endif
+#ifndef EP_LAYOUT_NT_HANDOFF
+#define EP_LAYOUT_NT_HANDOFF 0  // bit 0: streaming stores of tile rows, bit 1: streaming loads
+#endif
 #ifndef EP_LAYOUT_WAVES
 #define EP_LAYOUT_WAVES 4      // waves per count tile in the two-kernel path
 #endif
@@ -56,9 +59,8 @@ struct CountArgs {
     int tile_tokens;
     int tile_pairs_max;
     uint8_t *in_part;
-    int32_t *tile_counts;
-    int32_t *tile_part;
-    int32_t *tile_flags;
+    int32_t *tile_counts;   // [tiles, W]: E expert counts | P partition counts | bad-id flag
+    int W;                  // row stride of tile_counts, a multiple of 4
 };
 
 struct SlotsArgs {
@@ -67,8 +69,7 @@ struct SlotsArgs {
     int num_tiles;
     int64_t max_rows;
     const int32_t *tile_counts;
-    const int32_t *tile_part;
-    const int32_t *tile_flags;
+    int W;
     int32_t *count_out;
     int32_t *offset_out;
     int32_t *part_out;
@@ -149,6 +150,7 @@ __device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
     __syncthreads();
 
     // Per-expert exclusive scan over the waves: wave bases inside the tile.
+    int32_t *row_out = a.tile_counts + (int64_t)tile * a.W;
     for (int e = tid; e < E; e += blockDim.x) {
         int run = 0;
         for (int ww = 0; ww < nw; ++ww) {
@@ -156,7 +158,11 @@ __device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
             wcnt[ww * E + e] = run;
             run += c;
         }
-        a.tile_counts[(int64_t)tile * E + e] = run;
+#if EP_LAYOUT_NT_HANDOFF & 1
+        __builtin_nontemporal_store(run, row_out + e);
+#else
+        row_out[e] = run;
+#endif
     }
     __syncthreads();
 #pragma unroll
@@ -189,10 +195,10 @@ __device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
             }
         }
     }
-    if (flag) atomicOr(s_flag, kDevBadExpert);
+    if (flag) atomicOr(s_flag, 1);
     __syncthreads();
-    for (int q = tid; q < P; q += blockDim.x) a.tile_part[(int64_t)tile * P + q] = pcnt[q];
-    if (tid == 0) a.tile_flags[tile] = *s_flag;
+    for (int q = tid; q < P; q += blockDim.x) row_out[E + q] = pcnt[q];
+    for (int c = E + P + tid; c < a.W; c += blockDim.x) row_out[c] = c == E + P ? *s_flag : 0;
 }
 
 // Column sums of a row-major [rows, cols] int32 matrix in global memory:
@@ -222,7 +228,11 @@ __device__ void column_sums(const int32_t *__restrict__ mat, int rows, int cols,
                     if (r < rows) {
                         const int32_t *src = mat + (int64_t)r * cols + q * vec;
                         if (vec == 4) {
-                            const int4 x = *(const int4 *)src;
+#if EP_LAYOUT_NT_HANDOFF & 2
+                            const ep_u32x4 x = __builtin_nontemporal_load((const ep_u32x4 *)src);
+#else
+                            const ep_u32x4 x = *(const ep_u32x4 *)src;
+#endif
                             v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
                         } else {
                             v[u][0] = src[0]; v[u][1] = v[u][2] = v[u][3] = 0;
@@ -268,116 +278,84 @@ __device__ void column_sums(const int32_t *__restrict__ mat, int rows, int cols,
     __syncthreads();
 }
 
-// Exclusive scan in place over a[0..n) in LDS; every thread of the block
-// calls it.  Returns the total.  s_wave needs blockDim/64 + 1 entries.
-__device__ int block_exclusive_scan(int32_t *a, int n, int32_t *s_wave) {
-    const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
-    const int per = (n + nthreads - 1) / nthreads;
-    const int beg = min(n, tid * per);
+// Exclusive scan in place over a[0..n) in LDS by wave 0 alone (each lane
+// owns a contiguous run of ceil(n/64) entries); returns the total to wave 0.
+// The caller synchronises the block afterwards.
+__device__ int wave_exclusive_scan(int32_t *a, int n) {
+    const int lane = threadIdx.x & 63;
+    const int per = (n + 63) >> 6;
+    const int beg = min(n, lane * per);
     const int end = min(n, beg + per);
     int local = 0;
     for (int i = beg; i < end; ++i) local += a[i];
-    const int lane = tid & 63;
-    const int w = tid >> 6;
     int x = local;
     for (int o = 1; o < 64; o <<= 1) {
         const int y = __shfl_up(x, o);
         if (lane >= o) x += y;
     }
-    if (lane == 63) s_wave[w] = x;
-    __syncthreads();
-    const int nw = nthreads >> 6;
-    if (tid == 0) {
-        int run = 0;
-        for (int i = 0; i < nw; ++i) {
-            const int c = s_wave[i];
-            s_wave[i] = run;
-            run += c;
-        }
-        s_wave[nw] = run;
-    }
-    __syncthreads();
-    int excl = s_wave[w] + x - local;
+    int excl = x - local;
     for (int i = beg; i < end; ++i) {
         const int c = a[i];
         a[i] = excl;
         excl += c;
     }
-    const int total = s_wave[nw];
-    __syncthreads();
-    return total;
+    return __shfl(x, 63);
 }
 
 // Slots phase for tile blockIdx.x (blockDim == kSlotsBlock).  pv[i] holds a
 // packed (e << kRankBits) | tile rank (or -1) for flat pair pidx[i] (or -1).
 // The tiles that publish results are distinct where possible, so their extra
 // global reads overlap instead of queueing in one workgroup.
-__device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_wave, int32_t *s_flags,
+__device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_flags,
                             const int pv[4], const int64_t pidx[4]) {
-    const int E = a.E, P = a.P, C = a.C, A = a.A;
-    int32_t *s_tot = lds;                    // [E]
-    int32_t *s_base = s_tot + E;             // [E]
-    int32_t *s_off = s_base + E;             // [E+1]
-    int32_t *s_ptot = s_off + E + 1;         // [P]
-    int32_t *s_pdummy = s_ptot + P;          // [P]
-    int32_t *s_red = s_pdummy + P;           // [kRedInts]
+    const int E = a.E, P = a.P, C = a.C, A = a.A, W = a.W;
+    int32_t *s_tot = lds;                    // [W]  column totals
+    int32_t *s_base = s_tot + W;             // [W]  totals over the tiles before this one
+    int32_t *s_off = s_base + W;             // [E+1]
+    int32_t *s_red = s_off + E + 1;          // [kRedInts]
     const int tid = threadIdx.x;
     const int tile = blockIdx.x;
     const int nt = a.num_tiles > 0 ? a.num_tiles : 1;
     const bool pub_counts = tile == 0;
     const bool pub_status = tile == 1 % nt;
-    const bool pub_parts = tile == 2 % nt;
-    const bool pub_stats = tile == 3 % nt;
+    const bool pub_stats = tile == 2 % nt;
 
-    int fl = 0;
-    if (pub_status) {
-        if (tid == 0) *s_flags = 0;
-        for (int tl = tid; tl < a.num_tiles; tl += blockDim.x) fl |= a.tile_flags[tl];
-    }
-    int stats[4] = {0, 0, 0, 0};
-    if (pub_stats && a.cum_stats)
-        for (int i = 0; i < 4; ++i)
-            if (tid + i * (int)blockDim.x < E) stats[i] = a.cum_stats[tid + i * blockDim.x];
-
-    column_sums(a.tile_counts, a.num_tiles, E, tile, s_tot, s_base, s_red);
+    column_sums(a.tile_counts, a.num_tiles, W, tile, s_tot, s_base, s_red);
 
     int R;
     if (C == 0) {
         for (int e = tid; e < E; e += blockDim.x) s_off[e] = (s_tot[e] + A - 1) / A * A;
         __syncthreads();
-        R = block_exclusive_scan(s_off, E, s_wave);
-        if (tid == 0) s_off[E] = R;
+        if (tid < 64) {
+            const int total = wave_exclusive_scan(s_off, E);
+            if (tid == 0) s_off[E] = total;
+        }
     } else {
         for (int e = tid; e <= E; e += blockDim.x) s_off[e] = e * C;
-        R = E * C;
     }
     __syncthreads();
+    R = s_off[E];
 
     if (pub_counts) {
         for (int e = tid; e < E; e += blockDim.x) {
             a.count_out[e] = s_tot[e];
             a.offset_out[e] = s_off[e];
         }
+        for (int q = tid; q < P; q += blockDim.x) a.part_out[q] = s_tot[E + q];
         if (tid == 0) a.offset_out[E] = R;
     }
-    if (pub_stats && a.cum_stats) {
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + i * (int)blockDim.x;
-            if (e < E) a.cum_stats[e] = stats[i] + s_tot[e];
-        }
-    }
+    if (pub_stats && a.cum_stats)
+        for (int e = tid; e < E; e += blockDim.x) a.cum_stats[e] += s_tot[e];
     if (pub_status) {
+        if (tid == 0) *s_flags = s_tot[E + P] > 0 ? kDevBadExpert : 0;
+        __syncthreads();
+        int fl = 0;
         for (int e = tid; e < E; e += blockDim.x)
             if (C > 0 && s_tot[e] > C) fl |= kDevCapacity;
         if (tid == 0 && (int64_t)R > a.max_rows) fl |= kDevRecvOverflow;
         if (fl) atomicOr(s_flags, fl);
         __syncthreads();
         if (tid == 0) *a.status = *s_flags;
-    }
-    if (pub_parts) {
-        column_sums(a.tile_part, a.num_tiles, P, 0, s_ptot, s_pdummy, s_red);
-        for (int q = tid; q < P; q += blockDim.x) a.part_out[q] = s_ptot[q];
     }
 
     // Slots of this tile's pairs.
@@ -433,7 +411,6 @@ layout_count_kernel(CountArgs a, int32_t *__restrict__ packed) {
 
 __global__ void __launch_bounds__(kSlotsBlock) layout_slots_kernel(SlotsArgs a) {
     extern __shared__ int32_t lds[];
-    __shared__ int32_t s_wave[kSlotsBlock / 64 + 1];
     __shared__ int32_t s_flags;
     const int t0 = blockIdx.x * a.tile_tokens;
     const int64_t p0 = (int64_t)t0 * a.K;
@@ -446,12 +423,11 @@ __global__ void __launch_bounds__(kSlotsBlock) layout_slots_kernel(SlotsArgs a) 
         pidx[i] = p < npairs ? p0 + p : -1;
         pv[i] = p < npairs ? a.dst[p0 + p] : -1;
     }
-    slots_phase(a, lds, s_wave, &s_flags, pv, pidx);
+    slots_phase(a, lds, &s_flags, pv, pidx);
 }
 
 __global__ void __launch_bounds__(kSlotsBlock) layout_fused_kernel(CountArgs ca, SlotsArgs sa) {
     extern __shared__ int32_t lds[];
-    __shared__ int32_t s_wave[kSlotsBlock / 64 + 1];
     __shared__ int32_t s_flag;
     int rank[kMaxChunksPerWave], ex[kMaxChunksPerWave], cpw;
     count_phase(ca, lds, &s_flag, rank, ex, cpw);
@@ -471,7 +447,7 @@ __global__ void __launch_bounds__(kSlotsBlock) layout_fused_kernel(CountArgs ca,
     }
     // Every tile's counts are in memory before any tile reads them.
     cooperative_groups::this_grid().sync();
-    slots_phase(sa, lds, s_wave, &s_flag, pv, pidx);
+    slots_phase(sa, lds, &s_flag, pv, pidx);
 }
 
 }  // namespace
@@ -504,10 +480,9 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
     L.tile_tokens = tt;
     L.num_tiles = L.T > 0 ? (L.T + tt - 1) / tt : 0;
     const size_t nt = (size_t)(L.num_tiles > 0 ? L.num_tiles : 1);
+    L.row_stride = (L.E + L.P + 1 + 3) & ~3;
     L.ws_tile_counts = 0;
-    L.ws_tile_part = align256(nt * L.E * 4);
-    L.ws_tile_flags = L.ws_tile_part + align256(nt * L.P * 4);
-    L.ws_bytes = L.ws_tile_flags + align256(nt * 4);
+    L.ws_bytes = align256(nt * L.row_stride * 4);
     *plan = L;
     return true;
 }
@@ -526,8 +501,7 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     ca.tile_pairs_max = L.tile_tokens * L.K;
     ca.in_part = lay->is_token_in_partition;
     ca.tile_counts = (int32_t *)(ws + L.ws_tile_counts);
-    ca.tile_part = (int32_t *)(ws + L.ws_tile_part);
-    ca.tile_flags = (int32_t *)(ws + L.ws_tile_flags);
+    ca.W = L.row_stride;
     SlotsArgs sa;
     sa.T = L.T;
     sa.K = L.K;
@@ -539,8 +513,7 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     sa.num_tiles = L.num_tiles;
     sa.max_rows = L.max_rows;
     sa.tile_counts = ca.tile_counts;
-    sa.tile_part = ca.tile_part;
-    sa.tile_flags = ca.tile_flags;
+    sa.W = L.row_stride;
     sa.count_out = lay->num_tokens_per_expert;
     sa.offset_out = lay->expert_offset;
     sa.part_out = lay->num_tokens_per_partition;
@@ -550,7 +523,7 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     sa.cum_stats = cum_stats;
 
     const size_t lds_count = ((size_t)(L.block / 64) * L.E + ca.tile_pairs_max + L.P) * 4;
-    const size_t lds_slots = ((size_t)3 * L.E + 1 + 2 * L.P + kRedInts) * 4;
+    const size_t lds_slots = ((size_t)2 * L.row_stride + L.E + 1 + kRedInts) * 4;
 
     if (L.fused && L.num_tiles > 0) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
