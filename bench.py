@@ -12,11 +12,11 @@ algorithmic bytes (what the method must move: each token row read once,
 every valid (token, expert) row written once, and the reverse for combine,
 plus the routing tables); `tokens_per_s` is the same step counted in tokens.
 The headline region runs the K steps back to back between two events on
-the launch stream.  Per-kernel durations come from a second pass over the
-same K steps with HIP events recorded on the launch stream between the
-calls (each event record leaves a few microseconds of idle GPU time, so they
-stay out of the headline region); `roofline` reports the longer of the two
-row kernels against MI355X's 8 TB/s HBM peak.  `cpu_baseline` times the CPU
+the launch stream.  Per-kernel durations come from HIP events on the same
+stream around K back-to-back launches of each operation (an event record
+between launches would leave a few microseconds of idle GPU time);
+`roofline` reports the longer of the two row kernels against MI355X's 8 TB/s
+HBM peak.  `cpu_baseline` times the CPU
 oracle (single thread) on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -67,6 +67,78 @@ def load_traffic(name):
     return data.get("kernels", {}).get(name)
 
 
+def other_workloads(ep, torch, dev, steps):
+    """Per-operation timings for the fp8, decode, skewed and tiny workloads
+    (K back-to-back launches between two events; algorithmic bytes per op)."""
+    import ep_inputs
+
+    def per_op(fn, nbytes, T):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        r = {"us": round(ms * 1e3, 2), "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        if nbytes:
+            r["GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            r["hbm_frac"] = round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        return r
+
+    out = {}
+    for name in ("fp8", "decode", "skewed", "tiny"):
+        w = ep_inputs.make_workload(name)
+        T, H, E, K, A = w.num_tokens, w.hidden, w.num_experts, w.num_topk, w.expert_alignment
+        idx = torch.from_numpy(w.topk_idx).to(dev)
+        wts = torch.from_numpy(w.topk_weights).to(dev)
+        x = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
+        lay = ep.ep_get_layout(idx, E, A, w.num_partitions, w.capacity)
+        rows = lay.max_recv_rows
+        R = lay.num_recv_rows()
+        N = int((w.topk_idx >= 0).sum())
+        y = torch.randn((rows, H), device=dev).to(torch.bfloat16)
+        res = {"T": T, "H": H, "E": E, "K": K, "A": A, "P": w.num_partitions,
+               "C": w.capacity, "N": N, "R": R}
+        lb, rb, cb = algorithmic_bytes(T, H, K, N, R)
+        res["layout"] = per_op(lambda: ep.ep_get_layout(idx, E, A, w.num_partitions, w.capacity,
+                                                        layout=lay), lb, T)
+        out_c = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        if name == "fp8":
+            G = w.fp8_group
+            q, sc = ep.ep_cast_fp8(x, G)
+            recv8 = torch.empty((rows, H), dtype=torch.float8_e4m3fn, device=dev)
+            rs = torch.empty((rows, H // G), dtype=torch.float32, device=dev)
+            rw = torch.empty(rows, dtype=torch.float32, device=dev)
+            srow = H // G * 4
+            res["cast_fp8"] = per_op(lambda: ep.ep_cast_fp8(x, G, out=(q, sc)),
+                                     T * H * 2 + T * H + T * srow, T)
+            res["dispatch_fp8"] = per_op(lambda: ep.ep_dispatch((q, sc), lay, wts, out=(recv8, rs, rw)),
+                                         T * (H + srow) + N * (H + srow) + T * K * 8 + R * 4, T)
+            res["dispatch_fused_cast"] = per_op(
+                lambda: ep.ep_dispatch(x, lay, wts, recv_fp8=True, out=(recv8, rs, rw)),
+                T * H * 2 + N * (H + srow) + T * K * 8 + R * 4, T)
+        else:
+            recv = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+            rw = torch.empty(rows, dtype=torch.float32, device=dev)
+            zero = w.zero_padding
+            nb = rb + ((R - N) * H * 2 if zero else 0)
+            res["dispatch"] = per_op(lambda: ep.ep_dispatch(x, lay, wts, zero_padding=zero,
+                                                            out=(recv, None, rw)), nb, T)
+            if zero:
+                res["dispatch"]["valid_row_GBps"] = round(rb / (res["dispatch"]["us"] * 1e-6) / 1e9, 1)
+            del recv
+        res["combine"] = per_op(lambda: ep.ep_combine(y, lay, wts, out=out_c), cb, T)
+        assert lay.check() == 0
+        out[name] = res
+        del y, x, lay
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle, as it stands, on a token prefix of the same workload."""
     import oracle
@@ -104,6 +176,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before timing, run one plain device copy of MIB MiB (a known-size "
+                         "reference for HBM byte counters under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU's share only; --gpus {args.gpus} is not "
@@ -134,19 +210,21 @@ def main():
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    def step():
         ep.ep_get_layout(idx, E, A, w.num_partitions, w.capacity, layout=lay)
-        if ev is not None:
-            ev[1].record()
         ep.ep_dispatch(x, lay, wts, out=(recv, None, recv_w))
-        if ev is not None:
-            ev[2].record()
         ep.ep_combine(y, lay, wts, out=out)
-        if ev is not None:
-            ev[3].record()
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src_c = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty(n, dtype=torch.uint8, device=dev)
+        evict = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        evict.fill_(0)          # push src out of L2 and the memory-side cache
+        torch.cuda.synchronize()
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c, evict
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -162,14 +240,23 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = t_begin.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    # per-kernel pass: the same steps with events between the calls
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    lay_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
-    dis_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
-    com_ms = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
+    # per-operation pass: each operation launched K times back to back between two
+    # events on the launch stream (no event between launches, so no idle gaps)
+    def per_op(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    lay_ms = per_op(lambda: ep.ep_get_layout(idx, E, A, w.num_partitions, w.capacity, layout=lay))
+    dis_ms = per_op(lambda: ep.ep_dispatch(x, lay, wts, out=(recv, None, recv_w)))
+    com_ms = per_op(lambda: ep.ep_combine(y, lay, wts, out=out))
     assert lay.check() == 0
 
     lb, rb, cb = algorithmic_bytes(T, H, K, N, R)
@@ -200,6 +287,10 @@ def main():
                         for kk, vv in v.items()} for k, v in kern.items()},
         "wall_s_timed": round(wall, 4),
     }
+    if not args.no_other_workloads:
+        del recv, y
+        torch.cuda.empty_cache()
+        res["other_workloads"] = other_workloads(ep, torch, dev, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)
