@@ -30,6 +30,9 @@
 #ifndef EP_DISPATCH_ORDER
 #define EP_DISPATCH_ORDER 0   // 0: per token row, 1: per (token, k) pair, 2: per receive slot
 #endif
+#ifndef EP_DISPATCH_TPW
+#define EP_DISPATCH_TPW 2        // tokens per wave in the copy modes (2: measured best)
+#endif
 #ifndef EP_DISPATCH_NT_STORE
 #define EP_DISPATCH_NT_STORE 0   // plain stores measured faster for the receive rows
 #endif
@@ -199,6 +202,75 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
     }
 }
 
+// Copy modes, TPW consecutive tokens per wave (same row chunk): the next
+// token's row is requested before the current one is stored, so reads of x
+// overlap the K-fold stores instead of all arriving in one burst up front.
+template <int VPL, int MODE, int TPW>
+__global__ void __launch_bounds__(kBlock) dispatch_multi_kernel(DispatchK a) {
+    if ((int)blockIdx.x >= a.n_tok_blocks) {
+        pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        return;
+    }
+    const int lane = __lane_id();
+    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int g = gw / a.wpr;
+    const int ci = gw - g * a.wpr;
+    const int t0 = g * TPW;
+    if (t0 >= a.T) return;
+    const int v0 = ci * VPL * 64;
+    ep_u32x4 v[2][VPL];
+    {
+        const ep_u32x4 *src = (const ep_u32x4 *)(a.x + (int64_t)t0 * a.in_row_bytes);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int vi = v0 + i * 64 + lane;
+            v[0][i] = vi < a.nvec ? load_nt(src + vi) : ep_u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const int t = t0 + j;
+        if (t >= a.T) break;
+        if (j + 1 < TPW && t + 1 < a.T) {
+            const ep_u32x4 *src = (const ep_u32x4 *)(a.x + (int64_t)(t + 1) * a.in_row_bytes);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int vi = v0 + i * 64 + lane;
+                v[(j + 1) & 1][i] = vi < a.nvec ? load_nt(src + vi) : ep_u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        for (int kb = 0; kb < a.K; kb += 64) {
+            int my_slot = -1;
+            float my_w = 1.0f;
+            if (kb + lane < a.K) {
+                my_slot = a.dst[(int64_t)t * a.K + kb + lane];
+                if (a.w) my_w = a.w[(int64_t)t * a.K + kb + lane];
+            }
+            if ((int64_t)my_slot >= a.recv_rows) {
+                atomicOr(a.status, kDevRecvOverflow);
+                my_slot = -1;
+            }
+            if (ci == 0 && a.recv_w && my_slot >= 0) a.recv_w[my_slot] = my_w;
+            const int kn = min(64, a.K - kb);
+            for (int k = 0; k < kn; ++k) {
+                const int slot = lane_read(my_slot, k);
+                if (slot < 0) continue;
+                ep_u32x4 *dstrow = (ep_u32x4 *)(a.recv + (int64_t)slot * a.out_row_bytes);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int vi = v0 + i * 64 + lane;
+                    if (vi < a.nvec) row_store(dstrow + vi, v[j & 1][i]);
+                }
+                if (MODE == kModeCopyFp8 && ci == 0) {
+                    const float *ss = a.x_scales + (int64_t)t * a.ng;
+                    float *sd = a.recv_scales + (int64_t)slot * a.ng;
+                    for (int jj = lane; jj < a.ng; jj += 64) sd[jj] = ss[jj];
+                }
+            }
+        }
+    }
+}
+
 // Copy modes, one wave per (pair, chunk): the wave reads its chunk of the
 // token row (the K waves of one token hit L2/MALL after the first) and writes
 // one destination.  More, shorter waves keep more stores in flight.
@@ -297,7 +369,10 @@ template <int MODE>
 hipError_t launch_mode(const DispatchK &k, int vpl, int grid, int order, hipStream_t stream) {
 #define EP_CASE(V)                                                                              \
     case V:                                                                                     \
-        if (order == 1)                                                                         \
+        if (order == 3)                                                                         \
+            hipLaunchKernelGGL((dispatch_multi_kernel<V, MODE, (MODE == kModeCast ? 1 : EP_DISPATCH_TPW)>), \
+                               dim3(grid), dim3(kBlock), 0, stream, k);                        \
+        else if (order == 1)                                                                    \
             hipLaunchKernelGGL((dispatch_pair_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
         else if (order == 2)                                                                    \
             hipLaunchKernelGGL((dispatch_slot_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
@@ -334,8 +409,10 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     }
     k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
     if (k.wpr < 1) k.wpr = 1;
-    const int order = (mode != kModeCast && k.dst != nullptr) ? EP_DISPATCH_ORDER : 0;
+    int order = (mode != kModeCast && k.dst != nullptr) ? EP_DISPATCH_ORDER : 0;
+    if (order == 0 && mode != kModeCast && k.dst != nullptr && EP_DISPATCH_TPW > 1) order = 3;
     int64_t waves = (int64_t)k.T * (order == 1 ? k.K : 1) * k.wpr;
+    if (order == 3) waves = (((int64_t)k.T + EP_DISPATCH_TPW - 1) / EP_DISPATCH_TPW) * k.wpr;
     if (order == 2) {
         waves = (k.recv_rows < k.src_rows ? k.recv_rows : k.src_rows) * k.wpr;
         k.pad_slices = 0;
