@@ -223,3 +223,97 @@ def div_f32(a, b):
 def bf16_to_float(bits):
     """bf16 bit patterns (uint16) widened to float32 (exact)."""
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def partition_layout(topk_idx, num_experts, num_partitions, partitions_per_group=None):
+    """Non-expanded (per-rank) receive layout.  Returns a Layout dict with
+    in_part [T,P], tok_per_part [P], part_offset [P+1], token_slot [T,P],
+    tok_per_group [P/G], Rp."""
+    lib = _load()
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    E, P = int(num_experts), int(num_partitions)
+    G = P if partitions_per_group is None else int(partitions_per_group)
+    in_part = np.zeros(max(T * P, 1), np.uint8)
+    tpp = np.zeros(P, np.int32)
+    off = np.zeros(P + 1, np.int32)
+    slot = np.zeros(max(T * P, 1), np.int32)
+    tpg = np.zeros(max(P // G, 1), np.int32)
+    Rp = ctypes.c_int64(0)
+    rc = lib.oracle_partition_layout(_p(idx), _i64(T), _i64(K), _i64(E), _i64(P), _i64(G),
+                                     _p(in_part), _p(tpp), _p(off), _p(slot), _p(tpg),
+                                     ctypes.byref(Rp))
+    if rc != 0:
+        raise ValueError("oracle_partition_layout: invalid arguments")
+    return Layout(in_part=in_part[:T * P].reshape(T, P), tok_per_part=tpp, part_offset=off,
+                  token_slot=slot[:T * P].reshape(T, P), tok_per_group=tpg[:P // G],
+                  Rp=int(Rp.value), P=P, E=E)
+
+
+def dispatch_partitioned(x_rows, topk_idx, play, topk_weights=None, x_scales=None,
+                         recv_init=None):
+    """recv[token_slot[t,q]] = x[t]; per row the local expert ids (-1 when the
+    pair is elsewhere) and weights.  Returns (recv, recv_scales, recv_idx, recv_w)."""
+    lib = _load()
+    x = np.ascontiguousarray(x_rows)
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    Rp = play.Rp
+    row_bytes = x[0].nbytes if T else x.itemsize * int(np.prod(x.shape[1:]))
+    recv = (np.zeros((Rp,) + x.shape[1:], x.dtype) if recv_init is None
+            else np.array(recv_init, dtype=x.dtype, copy=True))
+    xs = _c(x_scales, np.float32)
+    recv_s, srow = None, 0
+    if xs is not None:
+        srow = xs.shape[1] * 4
+        recv_s = np.zeros((Rp, xs.shape[1]), np.float32)
+    recv_idx = np.zeros((max(Rp, 1), K), np.int64)
+    recv_w = np.zeros((max(Rp, 1), K), np.float32)
+    w = _c(topk_weights, np.float32)
+    lib.oracle_dispatch_partitioned(_p(x), _i64(row_bytes), _p(xs), _i64(srow), _p(idx), _p(w),
+                                    _i64(T), _i64(K), _i64(play.E), _i64(play.P),
+                                    _p(np.ascontiguousarray(play.token_slot, np.int32)), _i64(Rp),
+                                    _p(recv), _p(recv_s), _p(recv_idx), _p(recv_w))
+    return recv, recv_s, recv_idx[:Rp], recv_w[:Rp]
+
+
+def _combine_part(fn, out_dtype, y, token_slot, bias0, bias1, tokens):
+    y = _c(y, np.uint16)
+    H = y.shape[1]
+    ts = _c(token_slot, np.int32)
+    T, P = ts.shape
+    b0, b1, tk = _c(bias0, np.uint16), _c(bias1, np.uint16), _c(tokens, np.int64)
+    n = T if tk is None else tk.shape[0]
+    out = np.zeros((n, H), out_dtype)
+    fn(_p(y), _i64(H), _p(b0), _p(b1), _i64(T), _i64(P), _p(ts), _p(tk), _i64(n), _p(out))
+    return out
+
+
+def combine_partitioned_f32(y, token_slot, bias0=None, bias1=None, tokens=None):
+    return _combine_part(_load().oracle_combine_partitioned_f32, np.uint16, y, token_slot,
+                         bias0, bias1, tokens)
+
+
+def combine_partitioned_f64(y, token_slot, bias0=None, bias1=None, tokens=None):
+    return _combine_part(_load().oracle_combine_partitioned_f64, np.float64, y, token_slot,
+                         bias0, bias1, tokens)
+
+
+def combine_reduced_f32(y, topk_idx, dst, num_experts, num_partitions, topk_weights=None,
+                        bias0=None, bias1=None, tokens=None):
+    """Two-level combine: per-partition fp32 partial rounded to bf16, then the
+    partials summed over partitions in ascending order (with the biases first)."""
+    lib = _load()
+    y = _c(y, np.uint16)
+    H = y.shape[1]
+    idx = _c(topk_idx, np.int64)
+    dst = _c(dst, np.int32)
+    T, K = dst.shape
+    w, b0, b1, tk = (_c(topk_weights, np.float32), _c(bias0, np.uint16), _c(bias1, np.uint16),
+                     _c(tokens, np.int64))
+    n = T if tk is None else tk.shape[0]
+    out = np.zeros((n, H), np.uint16)
+    lib.oracle_combine_reduced_f32(_p(y), _i64(H), _p(idx), _p(w), _p(b0), _p(b1), _i64(T),
+                                   _i64(K), _i64(num_experts), _i64(num_partitions), _p(dst),
+                                   _p(tk), _i64(n), _p(out))
+    return out

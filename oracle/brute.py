@@ -88,3 +88,23 @@ def combine_exact(y_rows, dst, w=None, bias0=None, bias1=None):
             row.append(acc)
         out.append(row)
     return out
+
+
+def partition_layout(idx, E, P, G=None):
+    """Per-rank receive lists: partition q receives, once each and in token
+    order, every token with at least one expert in [q*m, (q+1)*m)."""
+    G = P if G is None else G
+    m = E // P
+    T = len(idx)
+    members = [sorted({t for t in range(T) for e in idx[t] if 0 <= e < E and e // m == q})
+               for q in range(P)]
+    offset = [0]
+    for q in range(P):
+        offset.append(offset[-1] + len(members[q]))
+    token_slot = [[-1] * P for _ in range(T)]
+    for q in range(P):
+        for j, t in enumerate(members[q]):
+            token_slot[t][q] = offset[q] + j
+    groups = [len({t for q in range(n * G, (n + 1) * G) for t in members[q]}) for n in range(P // G)]
+    return dict(members=members, part_offset=offset, token_slot=token_slot,
+                tok_per_part=[len(mm) for mm in members], tok_per_group=groups, Rp=offset[-1])

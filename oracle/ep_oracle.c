@@ -393,3 +393,160 @@ void oracle_div_f32_n(const float *a, const float *b, int64_t n, float *out)
         out[i] = q;
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* Partition ("rank") receive layout, the non-expanded form: [API] sec. 2.1
+ * (do_expand = False: a token travels once to every rank that owns one of
+ * its experts; recv_topk_idx / recv_topk_weights come with it), sec. 3.1
+ * (is_token_in_rank, num_tokens_per_rank, num_tokens_per_rdma_rank).
+ * Readings: partition q's rows are [part_offset[q], part_offset[q+1]) with
+ * part_offset the exclusive scan of the per-partition token counts, tokens
+ * in ascending t, no padding; a group is G consecutive partitions (G = P:
+ * one group) and counts the tokens that reach any partition in it.
+ *   token_slot [T*P]: receive row of (t, q), or -1.                       */
+int oracle_partition_layout(const int64_t *idx, int64_t T, int64_t K, int64_t E, int64_t P,
+                            int64_t G, uint8_t *in_part, int32_t *tok_per_part,
+                            int32_t *part_offset, int32_t *token_slot,
+                            int32_t *tok_per_group, int64_t *Rp_out)
+{
+    if (T < 0 || K < 1 || E < 1 || P < 1 || E % P != 0 || G < 1 || P % G != 0) return OR_EINVAL;
+    int64_t m = E / P;
+    for (int64_t q = 0; q < P; ++q) tok_per_part[q] = 0;
+    for (int64_t n = 0; n < P / G; ++n) tok_per_group[n] = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t q = 0; q < P; ++q) in_part[t * P + q] = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t e = idx[t * K + k];
+            if (e < 0 || e >= E) continue;
+            in_part[t * P + e / m] = 1;
+        }
+        for (int64_t q = 0; q < P; ++q) tok_per_part[q] += in_part[t * P + q];
+        for (int64_t n = 0; n < P / G; ++n) {
+            int hit = 0;
+            for (int64_t q = n * G; q < (n + 1) * G; ++q) hit |= in_part[t * P + q];
+            tok_per_group[n] += hit;
+        }
+    }
+    part_offset[0] = 0;
+    for (int64_t q = 0; q < P; ++q) part_offset[q + 1] = part_offset[q] + tok_per_part[q];
+    int32_t *cursor = (int32_t *)calloc((size_t)P, sizeof(int32_t));
+    if (!cursor) return OR_EINVAL;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t q = 0; q < P; ++q)
+            token_slot[t * P + q] = in_part[t * P + q] ? part_offset[q] + cursor[q]++ : -1;
+    free(cursor);
+    *Rp_out = part_offset[P];
+    return OR_OK;
+}
+
+/* Non-expanded dispatch: recv[token_slot[t,q]] = x[t] (and its scales);
+ * recv_idx[row, k] = e - q*m when pair (t,k) belongs to partition q (its
+ * expert's id local to the partition), else -1; recv_w[row, k] = w[t,k]
+ * (1 without weights) for local pairs, else 0.                            */
+void oracle_dispatch_partitioned(const uint8_t *x, int64_t row_bytes, const uint8_t *xs,
+                                 int64_t srow_bytes, const int64_t *idx, const float *w,
+                                 int64_t T, int64_t K, int64_t E, int64_t P,
+                                 const int32_t *token_slot, int64_t Rp, uint8_t *recv,
+                                 uint8_t *recv_s, int64_t *recv_idx, float *recv_w)
+{
+    int64_t m = E / P;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t q = 0; q < P; ++q) {
+            int64_t row = token_slot[t * P + q];
+            if (row < 0 || row >= Rp) continue;
+            memcpy(recv + row * row_bytes, x + t * row_bytes, (size_t)row_bytes);
+            if (xs && recv_s)
+                memcpy(recv_s + row * srow_bytes, xs + t * srow_bytes, (size_t)srow_bytes);
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t e = idx[t * K + k];
+                int local = e >= 0 && e < E && e / m == q;
+                if (recv_idx) recv_idx[row * K + k] = local ? e - q * m : -1;
+                if (recv_w) recv_w[row * K + k] = local ? (w ? w[t * K + k] : 1.0f) : 0.0f;
+            }
+        }
+    }
+}
+
+/* Combine for the non-expanded layout ([API] sec. 3.2: a plain sum; the
+ * rows already carry their partition's weighted expert sum):
+ * acc = 0; acc += bias0; acc += bias1; for q ascending with a row:
+ * acc += y[row]; out = bf16(acc).  float64 variant for the tolerance.    */
+void oracle_combine_partitioned_f32(const uint16_t *y, int64_t H, const uint16_t *bias0,
+                                    const uint16_t *bias1, int64_t T, int64_t P,
+                                    const int32_t *token_slot, const int64_t *tokens,
+                                    int64_t n_out, uint16_t *out)
+{
+    int64_t n = tokens ? n_out : T;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        for (int64_t c = 0; c < H; ++c) {
+            volatile float acc = 0.0f;
+            if (bias0) acc = acc + oracle_bf16_to_float(bias0[t * H + c]);
+            if (bias1) acc = acc + oracle_bf16_to_float(bias1[t * H + c]);
+            for (int64_t q = 0; q < P; ++q) {
+                int64_t row = token_slot[t * P + q];
+                if (row < 0) continue;
+                acc = acc + oracle_bf16_to_float(y[row * H + c]);
+            }
+            out[i * H + c] = oracle_bf16_from_float(acc);
+        }
+    }
+}
+
+void oracle_combine_partitioned_f64(const uint16_t *y, int64_t H, const uint16_t *bias0,
+                                    const uint16_t *bias1, int64_t T, int64_t P,
+                                    const int32_t *token_slot, const int64_t *tokens,
+                                    int64_t n_out, double *out)
+{
+    int64_t n = tokens ? n_out : T;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        for (int64_t c = 0; c < H; ++c) {
+            double acc = 0.0;
+            if (bias0) acc += (double)oracle_bf16_to_float(bias0[t * H + c]);
+            if (bias1) acc += (double)oracle_bf16_to_float(bias1[t * H + c]);
+            for (int64_t q = 0; q < P; ++q) {
+                int64_t row = token_slot[t * P + q];
+                if (row >= 0) acc += (double)oracle_bf16_to_float(y[row * H + c]);
+            }
+            out[i * H + c] = acc;
+        }
+    }
+}
+
+/* "Reduced" combine on the expanded layout ([API] sec. 2.2: reduced combine,
+ * multi-level reduction under allow_multiple_reduction).  Reading: level 1
+ * sums a token's pairs inside each partition (k ascending, fp32 fmaf from
+ * 0) and rounds that partial to bf16, the dtype a partial travels in;
+ * level 2 adds bias0, bias1, then the partials for q ascending (fp32), and
+ * rounds to bf16.  The float64 reference is oracle_combine_f64.            */
+void oracle_combine_reduced_f32(const uint16_t *y, int64_t H, const int64_t *idx,
+                                const float *w, const uint16_t *bias0, const uint16_t *bias1,
+                                int64_t T, int64_t K, int64_t E, int64_t P, const int32_t *dst,
+                                const int64_t *tokens, int64_t n_out, uint16_t *out)
+{
+    int64_t m = E / P;
+    int64_t n = tokens ? n_out : T;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        for (int64_t c = 0; c < H; ++c) {
+            volatile float acc = 0.0f;
+            if (bias0) acc = acc + oracle_bf16_to_float(bias0[t * H + c]);
+            if (bias1) acc = acc + oracle_bf16_to_float(bias1[t * H + c]);
+            for (int64_t q = 0; q < P; ++q) {
+                int any = 0;
+                volatile float part = 0.0f;
+                for (int64_t k = 0; k < K; ++k) {
+                    int64_t e = idx[t * K + k];
+                    int64_t slot = dst[t * K + k];
+                    if (e < 0 || e >= E || e / m != q || slot < 0) continue;
+                    any = 1;
+                    float wk = w ? w[t * K + k] : 1.0f;
+                    part = fmaf(wk, oracle_bf16_to_float(y[slot * H + c]), part);
+                }
+                if (any) acc = acc + oracle_bf16_to_float(oracle_bf16_from_float(part));
+            }
+            out[i * H + c] = oracle_bf16_from_float(acc);
+        }
+    }
+}
