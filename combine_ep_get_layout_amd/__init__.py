@@ -8,6 +8,10 @@ library's gfx950 kernels.  The functions carry the C entry points' names:
   ep_dispatch(x, layout, ...)                      -> (recv_x, recv_scales, recv_topk_weights)
   ep_combine(y, layout, ...)                       -> (combined_x, combined_topk_weights)
   ep_cast_fp8(x, group=128)                        -> (x_fp8, scales)
+  ep_dispatch_partitioned(x, layout, topk_idx, ...) -> (recv_x, recv_scales, recv_topk_idx,
+                                                        recv_topk_weights)
+  ep_combine_partitioned(y, layout, ...)            -> combined_x
+  ep_combine_reduced(y, layout, topk_idx, ...)      -> combined_x
 
 Semantics follow the DeepEP v2 test page ("DeepEP test target API
 reference", sec. 2.1 dispatch, 2.2 combine, 3.1-3.2 the V1 layout tensors and
@@ -26,6 +30,7 @@ from ._abi import (EP_DEV_BAD_EXPERT, EP_DEV_CAPACITY, EP_DEV_RECV_OVERFLOW, EpE
                    LayoutParams, LayoutPtrs)
 
 __all__ = ["load_library", "Layout", "ep_get_layout", "ep_dispatch", "ep_combine", "ep_cast_fp8",
+           "ep_dispatch_partitioned", "ep_combine_partitioned", "ep_combine_reduced",
            "worst_case_recv_rows", "EpError", "EP_DEV_BAD_EXPERT", "EP_DEV_CAPACITY",
            "EP_DEV_RECV_OVERFLOW"]
 
@@ -50,7 +55,7 @@ def _need_cuda(t: torch.Tensor, name: str):
 
 
 def worst_case_recv_rows(num_tokens, num_topk, num_experts, expert_alignment=1, capacity=0) -> int:
-    p = LayoutParams(num_tokens, num_topk, num_experts, expert_alignment, 1, capacity, 0)
+    p = LayoutParams(num_tokens, num_topk, num_experts, expert_alignment, 1, capacity, 0, 0)
     return int(load_library().ep_worst_case_recv_rows(ctypes.byref(p)))
 
 
@@ -59,9 +64,11 @@ class Layout:
 
     Tensors: num_tokens_per_expert [E], expert_offset [E+1] (R at [E]),
     num_tokens_per_partition [P], is_token_in_partition [T, P] uint8,
-    dst_slot [T, K], src_of_slot [max_recv_rows], status [1]."""
+    dst_slot [T, K], src_of_slot [max_recv_rows], status [1]; with the
+    partition layout also partition_offset [P+1], token_slot [T, P] and
+    num_tokens_per_group [P/G] (else None)."""
 
-    def __init__(self, params: LayoutParams, device):
+    def __init__(self, params: LayoutParams, device, partition_layout: bool = False):
         T, K, E, P = params.num_tokens, params.num_topk, params.num_experts, params.num_partitions
         i32 = dict(dtype=torch.int32, device=device)
         self.params = params
@@ -73,6 +80,12 @@ class Layout:
         self.dst_slot = torch.empty((T, K), **i32)
         self.src_of_slot = torch.empty(max(params.max_recv_rows, 1), **i32)
         self.status = torch.zeros(1, **i32)
+        self.partition_offset = self.token_slot = self.num_tokens_per_group = None
+        if partition_layout:
+            G = params.partitions_per_group or P
+            self.partition_offset = torch.empty(P + 1, **i32)
+            self.token_slot = torch.empty((T, P), **i32)
+            self.num_tokens_per_group = torch.empty(P // G, **i32)
         nbytes = load_library().ep_get_layout_workspace_bytes(ctypes.byref(params))
         self.workspace = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -92,11 +105,23 @@ class Layout:
     def max_recv_rows(self) -> int:
         return int(self.params.max_recv_rows)
 
+    @property
+    def num_partitions(self):
+        return self.params.num_partitions
+
     def ptrs(self) -> LayoutPtrs:
+        opt = [None if t is None else t.data_ptr()
+               for t in (self.partition_offset, self.token_slot, self.num_tokens_per_group)]
         return LayoutPtrs(self.num_tokens_per_expert.data_ptr(), self.expert_offset.data_ptr(),
                           self.num_tokens_per_partition.data_ptr(),
                           self.is_token_in_partition.data_ptr(), self.dst_slot.data_ptr(),
-                          self.src_of_slot.data_ptr(), self.status.data_ptr())
+                          self.src_of_slot.data_ptr(), self.status.data_ptr(), *opt)
+
+    def num_partition_rows(self) -> int:
+        """Rp, rows of the non-expanded partition layout (synchronises)."""
+        if self.partition_offset is None:
+            raise ValueError("layout was built without the partition layout")
+        return int(self.partition_offset[-1].item())
 
     def num_recv_rows(self) -> int:
         """R, the receive rows in use (synchronises: the page's do_cpu_sync)."""
@@ -118,10 +143,14 @@ def ep_get_layout(topk_idx: torch.Tensor, num_experts: int, expert_alignment: in
                   num_partitions: int = 1, capacity: int = 0,
                   max_recv_rows: Optional[int] = None,
                   cumulative_expert_stats: Optional[torch.Tensor] = None,
-                  layout: Optional[Layout] = None) -> Layout:
+                  layout: Optional[Layout] = None, partition_layout: bool = False,
+                  partitions_per_group: int = 0) -> Layout:
     """Derive the receive layout from topk_idx (int64 [T, K], -1 = none).
-    capacity > 0 selects the fixed-capacity ("expand") layout.  A `layout` of
-    the same shape may be passed in to be rewritten in place."""
+    capacity > 0 selects the fixed-capacity ("expand") layout.
+    partition_layout=True also derives the non-expanded per-partition layout
+    (token_slot etc., P <= 64); partitions_per_group sets G for
+    num_tokens_per_group (0: one group).  A `layout` of the same shape may be
+    passed in to be rewritten in place."""
     lib = load_library()
     _need_cuda(topk_idx, "topk_idx")
     if topk_idx.dtype != torch.int64 or topk_idx.dim() != 2:
@@ -130,13 +159,15 @@ def ep_get_layout(topk_idx: torch.Tensor, num_experts: int, expert_alignment: in
     if max_recv_rows is None:
         max_recv_rows = worst_case_recv_rows(T, K, num_experts, expert_alignment, capacity)
     params = LayoutParams(T, K, num_experts, expert_alignment, num_partitions, capacity,
-                          int(max_recv_rows))
+                          partitions_per_group, int(max_recv_rows))
     if layout is None:
-        layout = Layout(params, topk_idx.device)
-    elif (layout.params.num_tokens, layout.params.num_topk, layout.params.num_experts,
-          layout.params.num_partitions, layout.params.max_recv_rows) != (T, K, num_experts,
-                                                                         num_partitions,
-                                                                         int(max_recv_rows)):
+        layout = Layout(params, topk_idx.device, partition_layout)
+    elif ((layout.params.num_tokens, layout.params.num_topk, layout.params.num_experts,
+           layout.params.num_partitions, layout.params.max_recv_rows,
+           layout.params.partitions_per_group or num_partitions)
+          != (T, K, num_experts, num_partitions, int(max_recv_rows),
+              partitions_per_group or num_partitions)
+          or (layout.token_slot is not None) != partition_layout):
         raise ValueError("layout buffers do not match these shapes")
     else:
         layout.params = params
@@ -274,3 +305,126 @@ def ep_cast_fp8(x: torch.Tensor, group: int = 128,
     rc = lib.ep_cast_fp8(_ptr(x), T, H, group, _ptr(q), _ptr(s), _stream(x.device))
     _abi.check("ep_cast_fp8", rc)
     return q, s
+
+
+def _x_and_dtypes(x, recv_fp8, scale_group):
+    x_scales = None
+    if isinstance(x, (tuple, list)):
+        x, x_scales = x
+    _need_cuda(x, "x")
+    H = x.shape[1]
+    if _is_fp8(x):
+        if x_scales is None:
+            raise ValueError("fp8 x needs its scales")
+        _need_cuda(x_scales, "x_scales")
+        return x, x_scales, H // x_scales.shape[1], _abi.EP_DTYPE_FP8_E4M3, _abi.EP_DTYPE_FP8_E4M3
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16 or fp8")
+    recv = _abi.EP_DTYPE_FP8_E4M3 if recv_fp8 else _abi.EP_DTYPE_BF16
+    return x, None, scale_group, _abi.EP_DTYPE_BF16, recv
+
+
+def ep_dispatch_partitioned(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]],
+                            layout: Layout, topk_idx: torch.Tensor,
+                            topk_weights: Optional[torch.Tensor] = None, recv_fp8: bool = False,
+                            scale_group: int = 128, num_recv_rows: Optional[int] = None):
+    """Non-expanded dispatch: token t's row goes once to every partition q
+    that owns one of its experts, at layout.token_slot[t, q].  Returns
+    (recv_x, recv_scales or None, recv_topk_idx int64 [rows, K] with the
+    partition-local expert id or -1, recv_topk_weights float32 [rows, K] or
+    None).  rows defaults to T*P, the worst case."""
+    lib = load_library()
+    if layout.token_slot is None:
+        raise ValueError("layout was built without partition_layout=True")
+    x, x_scales, scale_group, x_dtype, recv_dtype = _x_and_dtypes(x, recv_fp8, scale_group)
+    T, H = x.shape
+    K = layout.num_topk
+    if T != layout.num_tokens:
+        raise ValueError("x rows != layout tokens")
+    _need_cuda(topk_idx, "topk_idx")
+    rows = T * layout.num_partitions if num_recv_rows is None else int(num_recv_rows)
+    dev = x.device
+    fp8_out = recv_dtype == _abi.EP_DTYPE_FP8_E4M3
+    recv_x = torch.empty((rows, H), dtype=torch.float8_e4m3fn if fp8_out else torch.bfloat16,
+                         device=dev)
+    recv_s = torch.empty((rows, H // scale_group), dtype=torch.float32, device=dev) \
+        if fp8_out else None
+    recv_i = torch.empty((rows, K), dtype=torch.int64, device=dev)
+    recv_w = None
+    if topk_weights is not None:
+        _need_cuda(topk_weights, "topk_weights")
+        recv_w = torch.empty((rows, K), dtype=torch.float32, device=dev)
+    params = layout.params
+    ptrs = layout.ptrs()
+    rc = lib.ep_dispatch_partitioned(_ptr(x), x_dtype, _ptr(x_scales), recv_dtype, H, scale_group,
+                                     _ptr(topk_idx), _ptr(topk_weights), ctypes.byref(params),
+                                     ctypes.byref(ptrs), _ptr(recv_x), _ptr(recv_s), _ptr(recv_i),
+                                     _ptr(recv_w), rows, _stream(dev))
+    _abi.check("ep_dispatch_partitioned", rc)
+    return recv_x, recv_s, recv_i, recv_w
+
+
+def _biases(bias, T, H):
+    b0 = b1 = None
+    if isinstance(bias, (tuple, list)):
+        b0, b1 = (list(bias) + [None, None])[:2]
+    elif bias is not None:
+        b0 = bias
+    for name, b in (("bias0", b0), ("bias1", b1)):
+        if b is not None:
+            _need_cuda(b, name)
+            if b.dtype != torch.bfloat16 or tuple(b.shape) != (T, H):
+                raise ValueError(f"{name} must be bf16 [T, H]")
+    return b0, b1
+
+
+def ep_combine_partitioned(y: torch.Tensor, layout: Layout,
+                           bias: Union[None, torch.Tensor, Tuple[torch.Tensor, torch.Tensor]] = None,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Plain sum of the partitions' rows back to the tokens (fp32, partition
+    order, bias first, bf16 round to nearest even)."""
+    lib = load_library()
+    if layout.token_slot is None:
+        raise ValueError("layout was built without partition_layout=True")
+    _need_cuda(y, "y")
+    if y.dtype != torch.bfloat16:
+        raise ValueError("y must be bf16")
+    rows, H = y.shape
+    T = layout.num_tokens
+    b0, b1 = _biases(bias, T, H)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    params = layout.params
+    ptrs = layout.ptrs()
+    rc = lib.ep_combine_partitioned(_ptr(y), H, rows, _ptr(b0), _ptr(b1), ctypes.byref(params),
+                                    ctypes.byref(ptrs), _ptr(out), _stream(y.device))
+    _abi.check("ep_combine_partitioned", rc)
+    return out
+
+
+def ep_combine_reduced(y: torch.Tensor, layout: Layout, topk_idx: torch.Tensor,
+                       topk_weights: Optional[torch.Tensor] = None,
+                       bias: Union[None, torch.Tensor, Tuple[torch.Tensor, torch.Tensor]] = None,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Two-level combine on the expanded layout: each partition's weighted
+    pairs summed in fp32 and rounded to bf16, then the partials (and bias)
+    summed in fp32 in partition order and rounded to bf16."""
+    lib = load_library()
+    _need_cuda(y, "y")
+    _need_cuda(topk_idx, "topk_idx")
+    if y.dtype != torch.bfloat16:
+        raise ValueError("y must be bf16")
+    rows, H = y.shape
+    T = layout.num_tokens
+    b0, b1 = _biases(bias, T, H)
+    if topk_weights is not None:
+        _need_cuda(topk_weights, "topk_weights")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    params = layout.params
+    ptrs = layout.ptrs()
+    rc = lib.ep_combine_reduced(_ptr(y), H, rows, _ptr(topk_idx), _ptr(topk_weights), _ptr(b0),
+                                _ptr(b1), ctypes.byref(params), ctypes.byref(ptrs), _ptr(out),
+                                _stream(y.device))
+    _abi.check("ep_combine_reduced", rc)
+    return out

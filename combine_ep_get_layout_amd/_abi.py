@@ -23,24 +23,28 @@ EP_DTYPE_FP8_E4M3 = 1
 EP_MAX_EXPERTS = 4096
 EP_MAX_PARTITIONS = 1024
 EP_MAX_TOPK = 256
+EP_MAX_SLOT_PARTITIONS = 64
 
 # Every symbol include/ep.h declares.
 EXPORTS = ("ep_get_layout_workspace_bytes", "ep_worst_case_recv_rows", "ep_get_layout",
-           "ep_dispatch", "ep_combine", "ep_cast_fp8", "ep_status_string")
+           "ep_dispatch", "ep_combine", "ep_dispatch_partitioned", "ep_combine_partitioned",
+           "ep_combine_reduced", "ep_cast_fp8", "ep_status_string")
 
 
 class LayoutParams(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("num_topk", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("expert_alignment", ctypes.c_int32),
                 ("num_partitions", ctypes.c_int32), ("capacity", ctypes.c_int32),
-                ("max_recv_rows", ctypes.c_int64)]
+                ("partitions_per_group", ctypes.c_int32), ("max_recv_rows", ctypes.c_int64)]
 
 
 class LayoutPtrs(ctypes.Structure):
     _fields_ = [("num_tokens_per_expert", ctypes.c_void_p), ("expert_offset", ctypes.c_void_p),
                 ("num_tokens_per_partition", ctypes.c_void_p),
                 ("is_token_in_partition", ctypes.c_void_p), ("dst_slot", ctypes.c_void_p),
-                ("src_of_slot", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+                ("src_of_slot", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("partition_offset", ctypes.c_void_p), ("token_slot", ctypes.c_void_p),
+                ("num_tokens_per_group", ctypes.c_void_p)]
 
 
 _lib = None
@@ -76,6 +80,16 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ep_combine.argtypes = [vp, i32, i64, vp, vp, vp, P(LayoutParams), P(LayoutPtrs), vp, vp,
                                vp, vp]
     lib.ep_combine.restype = ctypes.c_int
+    lib.ep_dispatch_partitioned.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i32, i32, vp, vp,
+                                            P(LayoutParams), P(LayoutPtrs), vp, vp, vp, vp, i64,
+                                            vp]
+    lib.ep_dispatch_partitioned.restype = ctypes.c_int
+    lib.ep_combine_partitioned.argtypes = [vp, i32, i64, vp, vp, P(LayoutParams), P(LayoutPtrs),
+                                           vp, vp]
+    lib.ep_combine_partitioned.restype = ctypes.c_int
+    lib.ep_combine_reduced.argtypes = [vp, i32, i64, vp, vp, vp, vp, P(LayoutParams),
+                                       P(LayoutPtrs), vp, vp]
+    lib.ep_combine_reduced.restype = ctypes.c_int
     lib.ep_cast_fp8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     lib.ep_cast_fp8.restype = ctypes.c_int
     lib.ep_status_string.argtypes = [ctypes.c_int]

@@ -21,6 +21,9 @@ int check_params(const ep_layout_params *p) {
         p->num_partitions < 1 || p->capacity < 0 || p->max_recv_rows < 0)
         return EP_ERR_INVALID_ARG;
     if (p->num_experts % p->num_partitions != 0) return EP_ERR_INVALID_ARG;
+    if (p->partitions_per_group < 0 ||
+        (p->partitions_per_group > 0 && p->num_partitions % p->partitions_per_group != 0))
+        return EP_ERR_INVALID_ARG;
     if (p->capacity > 0 && p->capacity % p->expert_alignment != 0) return EP_ERR_INVALID_ARG;
     if (p->num_experts > EP_MAX_EXPERTS || p->num_partitions > EP_MAX_PARTITIONS)
         return EP_ERR_UNSUPPORTED;
@@ -65,6 +68,7 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *p, const ep_l
     if (p->num_tokens > 0 && (!topk_idx || !layout->is_token_in_partition || !layout->dst_slot))
         return EP_ERR_INVALID_ARG;
     if (p->max_recv_rows > 0 && !layout->src_of_slot) return EP_ERR_INVALID_ARG;
+    if (layout->token_slot && p->num_partitions > EP_MAX_SLOT_PARTITIONS) return EP_ERR_UNSUPPORTED;
     ep::LayoutPlan plan;
     if (!ep::make_layout_plan(p, &plan)) return EP_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace))
@@ -159,6 +163,121 @@ int ep_combine(const void *y, int32_t hidden, int64_t num_y_rows, const float *t
     c.T = p->num_tokens;
     c.K = p->num_topk;
     c.hidden = hidden;
+    return to_status(ep::launch_combine(c, (hipStream_t)stream));
+}
+
+int ep_dispatch_partitioned(const void *x, int x_dtype, const float *x_scales, int recv_dtype,
+                            int32_t hidden, int32_t scale_group, const int64_t *topk_idx,
+                            const float *topk_weights, const ep_layout_params *p,
+                            const ep_layout *layout, void *recv_x, float *recv_scales,
+                            int64_t *recv_topk_idx, float *recv_topk_weights,
+                            int64_t num_recv_rows, void *stream) {
+    int rc = check_params(p);
+    if (rc != EP_OK) return rc;
+    if (p->num_partitions > EP_MAX_SLOT_PARTITIONS) return EP_ERR_UNSUPPORTED;
+    if (!layout || !layout->status) return EP_ERR_INVALID_ARG;
+    if (p->num_tokens > 0 && !layout->token_slot) return EP_ERR_INVALID_ARG;
+    if (p->num_tokens > 0 && (recv_topk_idx || recv_topk_weights) && !topk_idx)
+        return EP_ERR_INVALID_ARG;
+    if (num_recv_rows < 0 || hidden < 1) return EP_ERR_INVALID_ARG;
+    int mode;
+    if (x_dtype == EP_DTYPE_BF16 && recv_dtype == EP_DTYPE_BF16) mode = 0;
+    else if (x_dtype == EP_DTYPE_FP8_E4M3 && recv_dtype == EP_DTYPE_FP8_E4M3) mode = 1;
+    else if (x_dtype == EP_DTYPE_BF16 && recv_dtype == EP_DTYPE_FP8_E4M3) mode = 2;
+    else return EP_ERR_INVALID_ARG;
+    if (mode == 0 && hidden % 8 != 0) return EP_ERR_INVALID_ARG;
+    if (mode != 0) {
+        if (hidden % 16 != 0) return EP_ERR_INVALID_ARG;
+        if (!valid_group(hidden, scale_group)) return EP_ERR_UNSUPPORTED;
+        if (mode == 2 && scale_group == hidden && hidden > 16 * 64 * 8) return EP_ERR_UNSUPPORTED;
+        if (!recv_scales && num_recv_rows > 0) return EP_ERR_INVALID_ARG;
+        if (mode == 1 && !x_scales && p->num_tokens > 0) return EP_ERR_INVALID_ARG;
+    }
+    if (p->num_tokens > 0 && (!x || !aligned16(x))) return EP_ERR_INVALID_ARG;
+    if (num_recv_rows > 0 && (!recv_x || !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
+    ep::DispatchArgs a = {};
+    a.x = x;
+    a.x_scales = x_scales;
+    a.topk_weights = topk_weights;
+    a.status = layout->status;
+    a.recv = recv_x;
+    a.recv_scales = recv_scales;
+    a.recv_rows = num_recv_rows;
+    a.T = p->num_tokens;
+    a.K = p->num_topk;
+    a.E = p->num_experts;
+    a.A = 1;
+    a.C = 0;
+    a.hidden = hidden;
+    a.group = mode == 0 ? 0 : scale_group;
+    a.mode = mode;
+    a.partitioned = 1;
+    a.P = p->num_partitions;
+    a.token_slot = layout->token_slot;
+    a.topk_idx = topk_idx;
+    a.recv_idx = recv_topk_idx;
+    a.recv_wk = recv_topk_weights;
+    return to_status(ep::launch_dispatch(a, (hipStream_t)stream));
+}
+
+int ep_combine_partitioned(const void *y, int32_t hidden, int64_t num_y_rows, const void *bias0,
+                           const void *bias1, const ep_layout_params *p, const ep_layout *layout,
+                           void *out, void *stream) {
+    int rc = check_params(p);
+    if (rc != EP_OK) return rc;
+    if (p->num_partitions > EP_MAX_SLOT_PARTITIONS) return EP_ERR_UNSUPPORTED;
+    if (!layout || !layout->status || (p->num_tokens > 0 && !layout->token_slot))
+        return EP_ERR_INVALID_ARG;
+    if (hidden < 8 || hidden % 8 != 0 || num_y_rows < 0) return EP_ERR_INVALID_ARG;
+    if (p->num_tokens > 0) {
+        if (!out || !aligned16(out)) return EP_ERR_INVALID_ARG;
+        if (num_y_rows > 0 && (!y || !aligned16(y))) return EP_ERR_INVALID_ARG;
+        if ((bias0 && !aligned16(bias0)) || (bias1 && !aligned16(bias1))) return EP_ERR_INVALID_ARG;
+    }
+    ep::CombineArgs c = {};
+    c.y = y;
+    c.y_rows = num_y_rows;
+    c.bias0 = bias0;
+    c.bias1 = bias1;
+    c.dst = layout->token_slot;
+    c.status = layout->status;
+    c.out = out;
+    c.T = p->num_tokens;
+    c.K = p->num_partitions;
+    c.hidden = hidden;
+    return to_status(ep::launch_combine(c, (hipStream_t)stream));
+}
+
+int ep_combine_reduced(const void *y, int32_t hidden, int64_t num_y_rows, const int64_t *topk_idx,
+                       const float *topk_weights, const void *bias0, const void *bias1,
+                       const ep_layout_params *p, const ep_layout *layout, void *out,
+                       void *stream) {
+    int rc = check_params(p);
+    if (rc != EP_OK) return rc;
+    if (p->num_topk > 64) return EP_ERR_UNSUPPORTED;
+    if (!layout || !layout->status || (p->num_tokens > 0 && (!layout->dst_slot || !topk_idx)))
+        return EP_ERR_INVALID_ARG;
+    if (hidden < 8 || hidden % 8 != 0 || num_y_rows < 0) return EP_ERR_INVALID_ARG;
+    if (p->num_tokens > 0) {
+        if (!out || !aligned16(out)) return EP_ERR_INVALID_ARG;
+        if (num_y_rows > 0 && (!y || !aligned16(y))) return EP_ERR_INVALID_ARG;
+        if ((bias0 && !aligned16(bias0)) || (bias1 && !aligned16(bias1))) return EP_ERR_INVALID_ARG;
+    }
+    ep::CombineArgs c = {};
+    c.y = y;
+    c.y_rows = num_y_rows;
+    c.w = topk_weights;
+    c.bias0 = bias0;
+    c.bias1 = bias1;
+    c.dst = layout->dst_slot;
+    c.status = layout->status;
+    c.out = out;
+    c.T = p->num_tokens;
+    c.K = p->num_topk;
+    c.hidden = hidden;
+    c.topk_idx = topk_idx;
+    c.E = p->num_experts;
+    c.m = p->num_experts / p->num_partitions;
     return to_status(ep::launch_combine(c, (hipStream_t)stream));
 }
 

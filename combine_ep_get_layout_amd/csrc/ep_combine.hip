@@ -46,6 +46,8 @@ struct CombineK {
     int nvec;       // 16-byte vectors per row
     int row_bytes;
     int wpr;
+    const int64_t *idx;   // reduced combine: routing [T, K]
+    int E, m;             // reduced combine: experts, experts per partition
 };
 
 constexpr int kBlock = 256;
@@ -155,6 +157,129 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(CombineK a) {
     }
 }
 
+// Two-level ("reduced") combine.  The token's kept pairs are put in
+// (partition, k) order: each lane ranks its own key against the others and
+// ds_permute moves the lane index to the lane named by that rank.  Rows are
+// then read in that order, U at a time; a partition's fmaf chain starts at 0
+// and is rounded to bf16 before it is added to the running fp32 total, which
+// starts from the biases.  Requires K <= 64.
+template <int VPL>
+__global__ void __launch_bounds__(kBlock) combine_reduced_kernel(CombineK a) {
+    constexpr int U = EP_COMBINE_U > 0 ? EP_COMBINE_U
+                                       : (VPL >= 16 ? 1 : (VPL >= 8 ? 2 : (VPL >= 4 ? 4 : 8)));
+    const int lane = __lane_id();
+    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int t = gw / a.wpr;
+    const int ci = gw - t * a.wpr;
+    if (t >= a.T) return;
+    const int v0 = ci * VPL * 64;
+
+    float acc[VPL][8], part[VPL][8];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            acc[i][j] = 0.0f;
+            part[i][j] = 0.0f;
+        }
+    const uint8_t *biases[2] = {a.b0, a.b1};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        if (!biases[b]) continue;
+        const ep_u32x4 *src = (const ep_u32x4 *)(biases[b] + (int64_t)t * a.row_bytes);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int vi = v0 + i * 64 + lane;
+            if (vi < a.nvec) add_bf16x8(acc[i], load_nt(src + vi));
+        }
+    }
+
+    int my_slot = -1, my_q = 0;
+    float my_w = 1.0f;
+    if (lane < a.K) {
+        my_slot = a.dst[(int64_t)t * a.K + lane];
+        const int64_t e = a.idx[(int64_t)t * a.K + lane];
+        if ((int64_t)my_slot >= a.y_rows) {
+            atomicOr(a.status, kDevRecvOverflow);
+            my_slot = -1;
+        }
+        if (e < 0 || e >= a.E) my_slot = -1;
+        if (my_slot >= 0) {
+            my_q = (int)(e / a.m);
+            if (a.w) my_w = a.w[(int64_t)t * a.K + lane];
+        }
+    }
+    const int key = my_slot >= 0 ? (my_q << 6) | lane : 0x7FFFFFFF;
+    int rank = 0;
+    for (int j = 0; j < a.K; ++j) rank += lane_read(key, j) < key ? 1 : 0;
+    const int nvalid = __popcll(__ballot(my_slot >= 0));
+    // lane r receives the index of the lane whose key ranks r
+    const int order = __builtin_amdgcn_ds_permute(rank << 2, lane);
+
+    int curq = -1;
+    for (int r0 = 0; r0 < nvalid; r0 += U) {
+        ep_u32x4 v[U][VPL];
+        int slot[U], q[U];
+        float wk[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            slot[u] = -1;
+            q[u] = -1;
+            wk[u] = 0.0f;
+            if (r0 + u < nvalid) {
+                const int src_lane = lane_read(order, r0 + u);
+                slot[u] = lane_read(my_slot, src_lane);
+                q[u] = lane_read(my_q, src_lane);
+                wk[u] = lane_read_f(my_w, src_lane);
+                const ep_u32x4 *src = (const ep_u32x4 *)(a.y + (int64_t)slot[u] * a.row_bytes);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int vi = v0 + i * 64 + lane;
+                    v[u][i] = vi < a.nvec ? load_nt(src + vi) : ep_u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (slot[u] < 0) continue;
+            if (q[u] != curq) {
+                if (curq >= 0) {
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            acc[i][j] = acc[i][j] + __uint_as_float(bf16_rne(part[i][j]) << 16);
+                            part[i][j] = 0.0f;
+                        }
+                }
+                curq = q[u];
+            }
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) fma_bf16x8(part[i], wk[u], v[u][i]);
+        }
+    }
+    if (curq >= 0) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = acc[i][j] + __uint_as_float(bf16_rne(part[i][j]) << 16);
+    }
+
+    ep_u32x4 *dst = (ep_u32x4 *)(a.out + (int64_t)t * a.row_bytes);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int vi = v0 + i * 64 + lane;
+        if (vi >= a.nvec) continue;
+        ep_u32x4 o;
+        o.x = bf16_rne(acc[i][0]) | (bf16_rne(acc[i][1]) << 16);
+        o.y = bf16_rne(acc[i][2]) | (bf16_rne(acc[i][3]) << 16);
+        o.z = bf16_rne(acc[i][4]) | (bf16_rne(acc[i][5]) << 16);
+        o.w = bf16_rne(acc[i][6]) | (bf16_rne(acc[i][7]) << 16);
+        store_nt(dst + vi, o);
+    }
+}
+
 int choose_vpl(int nvec, int limit) {
     static const int cand[] = {16, 14, 8, 7, 4, 2, 1};
     const int q = (nvec + 63) / 64;
@@ -183,6 +308,9 @@ hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
     k.K = c.K;
     k.nvec = c.hidden / 8;
     k.row_bytes = c.hidden * 2;
+    k.idx = c.topk_idx;
+    k.E = c.E;
+    k.m = c.m;
     const int vpl = choose_vpl(k.nvec, EP_COMBINE_VPL);
     k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
     if (k.wpr < 1) k.wpr = 1;
@@ -192,7 +320,11 @@ hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
 #define EP_CASE(V)                                                                              \
     case V:                                                                                     \
-        hipLaunchKernelGGL(combine_kernel<V>, dim3((unsigned)grid), dim3(kBlock), 0, stream, k); \
+        if (k.idx)                                                                              \
+            hipLaunchKernelGGL(combine_reduced_kernel<V>, dim3((unsigned)grid), dim3(kBlock), 0, \
+                               stream, k);                                                      \
+        else                                                                                    \
+            hipLaunchKernelGGL(combine_kernel<V>, dim3((unsigned)grid), dim3(kBlock), 0, stream, k); \
         break;
     switch (vpl) {
         EP_CASE(1) EP_CASE(2) EP_CASE(4) EP_CASE(7) EP_CASE(8) EP_CASE(14) EP_CASE(16)

@@ -58,6 +58,11 @@ struct DispatchK {
     float *recv_w;
     int64_t recv_rows;
     int T, K, E, C;
+    int nd;                   // destinations per token: K (expanded) or P (partitioned)
+    const int64_t *idx;       // partitioned: routing [T, K]
+    int64_t *recv_idx;        // partitioned: [rows, K] local expert ids, or NULL
+    float *recv_wk;           // partitioned: [rows, K] weights, or NULL
+    int m;                    // partitioned: experts per partition (0: expanded)
     int nvec;                 // 16-byte vectors per input row
     int in_row_bytes;
     int out_row_bytes;
@@ -77,6 +82,26 @@ template <typename T>
 __device__ __forceinline__ void row_store(T *p, T v) {
     if (EP_DISPATCH_NT_STORE) __builtin_nontemporal_store(v, p);
     else *p = v;
+}
+
+// Per-destination bookkeeping of one lane: the expanded layout records the
+// pair's weight in its row; the partitioned layout records, for the row of
+// (t, q), every pair's partition-local expert id (-1 when elsewhere) and
+// weight (0 when elsewhere).
+__device__ __forceinline__ void record_dest(const DispatchK &a, int t, int q, int slot, float w) {
+    if (slot < 0) return;
+    if (a.m == 0) {
+        if (a.recv_w) a.recv_w[slot] = w;
+        return;
+    }
+    for (int k = 0; k < a.K; ++k) {
+        const int64_t e = a.idx[(int64_t)t * a.K + k];
+        const bool local = e >= 0 && e < a.E && e / a.m == q;
+        if (a.recv_idx) a.recv_idx[(int64_t)slot * a.K + k] = local ? e - (int64_t)q * a.m : -1;
+        if (a.recv_wk)
+            a.recv_wk[(int64_t)slot * a.K + k] =
+                local ? (a.w ? a.w[(int64_t)t * a.K + k] : 1.0f) : 0.0f;
+    }
 }
 
 __device__ __forceinline__ void pad_rows(const DispatchK &a, int pb) {
@@ -117,7 +142,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
     const int t = gw / a.wpr;
     const int ci = gw - t * a.wpr;
     if (t >= a.T) return;
-    const int K = a.dst ? a.K : 1;
+    const int K = a.dst ? a.nd : 1;
     const int v0 = ci * VPL * 64;
 
     // Load this wave's chunk of the row once.
@@ -135,14 +160,14 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
         int my_slot = -1;
         float my_w = 1.0f;
         if (kb + lane < K) {
-            my_slot = a.dst ? a.dst[(int64_t)t * a.K + kb + lane] : t;
-            if (a.w) my_w = a.w[(int64_t)t * a.K + kb + lane];
+            my_slot = a.dst ? a.dst[(int64_t)t * a.nd + kb + lane] : t;
+            if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
         }
         if ((int64_t)my_slot >= a.recv_rows) {
             if (a.status) atomicOr(a.status, kDevRecvOverflow);
             my_slot = -1;
         }
-        if (ci == 0 && a.recv_w && my_slot >= 0) a.recv_w[my_slot] = my_w;
+        if (ci == 0) record_dest(a, t, kb + lane, my_slot, my_w);
         const int kn = min(64, K - kb);
 
         if (MODE == kModeCast) {
@@ -239,19 +264,19 @@ __global__ void __launch_bounds__(kBlock) dispatch_multi_kernel(DispatchK a) {
                 v[(j + 1) & 1][i] = vi < a.nvec ? load_nt(src + vi) : ep_u32x4{0u, 0u, 0u, 0u};
             }
         }
-        for (int kb = 0; kb < a.K; kb += 64) {
+        for (int kb = 0; kb < a.nd; kb += 64) {
             int my_slot = -1;
             float my_w = 1.0f;
-            if (kb + lane < a.K) {
-                my_slot = a.dst[(int64_t)t * a.K + kb + lane];
-                if (a.w) my_w = a.w[(int64_t)t * a.K + kb + lane];
+            if (kb + lane < a.nd) {
+                my_slot = a.dst[(int64_t)t * a.nd + kb + lane];
+                if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
             }
             if ((int64_t)my_slot >= a.recv_rows) {
                 atomicOr(a.status, kDevRecvOverflow);
                 my_slot = -1;
             }
-            if (ci == 0 && a.recv_w && my_slot >= 0) a.recv_w[my_slot] = my_w;
-            const int kn = min(64, a.K - kb);
+            if (ci == 0) record_dest(a, t, kb + lane, my_slot, my_w);
+            const int kn = min(64, a.nd - kb);
             for (int k = 0; k < kn; ++k) {
                 const int slot = lane_read(my_slot, k);
                 if (slot < 0) continue;
@@ -409,7 +434,7 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     }
     k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
     if (k.wpr < 1) k.wpr = 1;
-    int order = (mode != kModeCast && k.dst != nullptr) ? EP_DISPATCH_ORDER : 0;
+    int order = (mode != kModeCast && k.dst != nullptr && k.m == 0) ? EP_DISPATCH_ORDER : 0;
     if (order == 0 && mode != kModeCast && k.dst != nullptr && EP_DISPATCH_TPW > 1) order = 3;
     int64_t waves = (int64_t)k.T * (order == 1 ? k.K : 1) * k.wpr;
     if (order == 3) waves = (((int64_t)k.T + EP_DISPATCH_TPW - 1) / EP_DISPATCH_TPW) * k.wpr;
@@ -449,6 +474,12 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     k.K = a.K;
     k.E = a.E;
     k.C = a.C;
+    k.nd = a.partitioned ? a.P : a.K;
+    k.m = a.partitioned ? a.E / a.P : 0;
+    k.idx = a.topk_idx;
+    k.recv_idx = a.recv_idx;
+    k.recv_wk = a.recv_wk;
+    if (a.partitioned) k.dst = a.token_slot;
     if (a.mode == kModeCopy16) {
         k.in_row_bytes = k.out_row_bytes = a.hidden * 2;
         k.nvec = a.hidden / 8;
@@ -465,7 +496,7 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     }
     k.zero_padding = a.zero_padding;
     int maxpad = a.C > 0 ? a.C : a.A - 1;
-    if (!a.zero_padding && !a.recv_w) maxpad = 0;
+    if ((!a.zero_padding && !a.recv_w) || a.partitioned) maxpad = 0;
     if (maxpad > 0) k.pad_slices = a.zero_padding ? (maxpad + 3) / 4 : 1;
     return run(k, a.mode, EP_DISPATCH_VPL, stream);
 }
@@ -481,6 +512,7 @@ hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, uint8_t 
     k.recv_rows = T;
     k.T = T;
     k.K = 1;
+    k.nd = 1;
     k.in_row_bytes = hidden * 2;
     k.out_row_bytes = hidden;
     k.nvec = hidden / 8;

@@ -18,8 +18,10 @@ struct LayoutPlan {
     int block;         // threads per count workgroup (multiple of 64)
     bool fused;        // count and slots in one cooperative launch when it fits
     int chunks_per_wave;
-    int row_stride;         // ints per tile row: E + P + 1 rounded up to 4
-    size_t ws_tile_counts;  // byte offset inside the workspace
+    int G, NG;              // partitions per group, number of groups
+    int row_stride;         // ints per tile row: E + P + NG + 1 rounded up to 4
+    size_t ws_tile_counts;  // byte offsets inside the workspace
+    size_t ws_tok_mask;
     size_t ws_bytes;
 };
 
@@ -47,6 +49,13 @@ struct DispatchArgs {
     int group;                     // fp8 scale group (0 when bf16 -> bf16)
     int mode;                      // 0 copy bf16, 1 copy fp8 (+scales), 2 cast bf16 -> fp8
     int zero_padding;
+    // partitioned (non-expanded) dispatch
+    int partitioned;
+    int P;
+    const int32_t *token_slot;     // [T*P]
+    const int64_t *topk_idx;       // [T*K]
+    int64_t *recv_idx;             // [rows*K] or NULL
+    float *recv_wk;                // [rows*K] or NULL
 };
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream);
@@ -63,6 +72,9 @@ struct CombineArgs {
     float *combined_w;
     void *out;
     int T, K, hidden;
+    // reduced (two-level) combine: routing and experts per partition
+    const int64_t *topk_idx;
+    int E, m;
 };
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);

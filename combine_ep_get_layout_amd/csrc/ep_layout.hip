@@ -58,9 +58,12 @@ struct CountArgs {
     int T, K, E, P, m;
     int tile_tokens;
     int tile_pairs_max;
+    int G, NG;              // partitions per group, groups
     uint8_t *in_part;
-    int32_t *tile_counts;   // [tiles, W]: E expert counts | P partition counts | bad-id flag
+    int32_t *tile_counts;   // [tiles, W]: E expert counts | P partition counts |
+                            //             NG group counts | bad-id flag
     int W;                  // row stride of tile_counts, a multiple of 4
+    uint64_t *tok_mask;     // [T] partition bit mask per token (P <= 64), or NULL
 };
 
 struct SlotsArgs {
@@ -70,6 +73,11 @@ struct SlotsArgs {
     int64_t max_rows;
     const int32_t *tile_counts;
     int W;
+    int NG;
+    const uint64_t *tok_mask;
+    int32_t *part_offset_out;   // [P+1] or NULL
+    int32_t *token_slot_out;    // [T*P] or NULL
+    int32_t *group_out;         // [NG] or NULL
     int32_t *count_out;
     int32_t *offset_out;
     int32_t *part_out;
@@ -88,7 +96,7 @@ __device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
     const int E = a.E;
     int32_t *wcnt = lds;                   // [nw][E]
     int32_t *pe = lds + nw * E;            // [tile pairs]
-    int32_t *pcnt = pe + a.tile_pairs_max; // [P]
+    int32_t *pcnt = pe + a.tile_pairs_max; // [P] then [NG]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -108,7 +116,7 @@ __device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
         raw[c] = (c < cpw && p < npairs) ? a.idx[p0 + p] : -1;
     }
     for (int i = tid; i < nw * E; i += blockDim.x) wcnt[i] = 0;
-    for (int i = tid; i < a.P; i += blockDim.x) pcnt[i] = 0;
+    for (int i = tid; i < a.P + a.NG; i += blockDim.x) pcnt[i] = 0;
     if (tid == 0) *s_flag = 0;
     __syncthreads();
 
@@ -169,8 +177,10 @@ __device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
     for (int c = 0; c < kMaxChunksPerWave; ++c)
         if (c < cpw && ex[c] >= 0) rank[c] += mycnt[ex[c]];
 
-    // Partition membership, one thread per token, from the ids staged in LDS.
-    const int K = a.K, P = a.P, m = a.m;
+    // Partition and group membership, one thread per token, from the ids
+    // staged in LDS.  Group n is partitions [n*G, (n+1)*G).
+    const int K = a.K, P = a.P, m = a.m, G = a.G, NG = a.NG;
+    int32_t *gcnt = pcnt + P;
     for (int tt = tid; tt < t1 - t0; tt += blockDim.x) {
         uint8_t *row = a.in_part + (int64_t)(t0 + tt) * P;
         const int32_t *ids = pe + tt * K;
@@ -181,24 +191,36 @@ __device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
                 if (e >= 0) mask |= 1ull << (e / m);
             }
             for (int q = 0; q < P; ++q) row[q] = (uint8_t)((mask >> q) & 1ull);
+            if (a.tok_mask) a.tok_mask[t0 + tt] = mask;
+            const uint64_t gm = G == 64 ? ~0ull : ((1ull << G) - 1);
+            for (int n = 0; n < NG; ++n)
+                if ((mask >> (n * G)) & gm) atomicAdd(&gcnt[n], 1);
             while (mask) {
                 const int q = __builtin_ffsll((long long)mask) - 1;
                 atomicAdd(&pcnt[q], 1);
                 mask &= mask - 1;
             }
         } else {
+            int ghit = -1;   // last group counted for this token
             for (int q = 0; q < P; ++q) {
                 int hit = 0;
                 for (int k = 0; k < K; ++k) hit |= (ids[k] >= 0 && ids[k] / m == q);
                 row[q] = (uint8_t)hit;
-                if (hit) atomicAdd(&pcnt[q], 1);
+                if (hit) {
+                    atomicAdd(&pcnt[q], 1);
+                    if (q / G != ghit) {
+                        ghit = q / G;
+                        atomicAdd(&gcnt[ghit], 1);
+                    }
+                }
             }
         }
     }
     if (flag) atomicOr(s_flag, 1);
     __syncthreads();
-    for (int q = tid; q < P; q += blockDim.x) row_out[E + q] = pcnt[q];
-    for (int c = E + P + tid; c < a.W; c += blockDim.x) row_out[c] = c == E + P ? *s_flag : 0;
+    for (int q = tid; q < P + NG; q += blockDim.x) row_out[E + q] = pcnt[q];
+    for (int c = E + P + NG + tid; c < a.W; c += blockDim.x)
+        row_out[c] = c == E + P + NG ? *s_flag : 0;
 }
 
 // Column sums of a row-major [rows, cols] int32 matrix in global memory:
@@ -309,16 +331,26 @@ __device__ int wave_exclusive_scan(int32_t *a, int n) {
 __device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_flags,
                             const int pv[4], const int64_t pidx[4]) {
     const int E = a.E, P = a.P, C = a.C, A = a.A, W = a.W;
+    const int NG = a.NG;
     int32_t *s_tot = lds;                    // [W]  column totals
     int32_t *s_base = s_tot + W;             // [W]  totals over the tiles before this one
     int32_t *s_off = s_base + W;             // [E+1]
-    int32_t *s_red = s_off + E + 1;          // [kRedInts]
+    int32_t *s_poff = s_off + E + 1;         // [P+1] partition offsets
+    int32_t *s_wq = s_poff + P + 1;          // [waves][P] per-wave partition token counts
+    int32_t *s_red = s_wq + (blockDim.x >> 6) * P;   // [kRedInts]
     const int tid = threadIdx.x;
     const int tile = blockIdx.x;
     const int nt = a.num_tiles > 0 ? a.num_tiles : 1;
     const bool pub_counts = tile == 0;
     const bool pub_status = tile == 1 % nt;
     const bool pub_stats = tile == 2 % nt;
+
+    // This tile's token masks for the partition layout: requested first.
+    const bool want_tok = a.token_slot_out != nullptr;
+    const int t0 = tile * a.tile_tokens;
+    const int ntok = a.num_tiles > 0 ? min(a.T, t0 + a.tile_tokens) - t0 : 0;
+    uint64_t tmask = 0;
+    if (want_tok && tid < ntok) tmask = a.tok_mask[t0 + tid];
 
     column_sums(a.tile_counts, a.num_tiles, W, tile, s_tot, s_base, s_red);
 
@@ -333,8 +365,16 @@ __device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_flags,
     } else {
         for (int e = tid; e <= E; e += blockDim.x) s_off[e] = e * C;
     }
+    if ((want_tok || a.part_offset_out) && tid >= 64 && tid < 128) {
+        // a second wave scans the partition token counts meanwhile
+        for (int q = tid - 64; q < P; q += 64) s_poff[q] = s_tot[E + q];
+    }
     __syncthreads();
     R = s_off[E];
+    if ((want_tok || a.part_offset_out) && tid < 64) {
+        const int total = wave_exclusive_scan(s_poff, P);
+        if (tid == 0) s_poff[P] = total;
+    }
 
     if (pub_counts) {
         for (int e = tid; e < E; e += blockDim.x) {
@@ -342,12 +382,14 @@ __device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_flags,
             a.offset_out[e] = s_off[e];
         }
         for (int q = tid; q < P; q += blockDim.x) a.part_out[q] = s_tot[E + q];
+        if (a.group_out)
+            for (int n = tid; n < NG; n += blockDim.x) a.group_out[n] = s_tot[E + P + n];
         if (tid == 0) a.offset_out[E] = R;
     }
     if (pub_stats && a.cum_stats)
         for (int e = tid; e < E; e += blockDim.x) a.cum_stats[e] += s_tot[e];
     if (pub_status) {
-        if (tid == 0) *s_flags = s_tot[E + P] > 0 ? kDevBadExpert : 0;
+        if (tid == 0) *s_flags = s_tot[E + P + NG] > 0 ? kDevBadExpert : 0;
         __syncthreads();
         int fl = 0;
         for (int e = tid; e < E; e += blockDim.x)
@@ -356,6 +398,41 @@ __device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_flags,
         if (fl) atomicOr(s_flags, fl);
         __syncthreads();
         if (tid == 0) *a.status = *s_flags;
+    }
+
+    // Partition layout: a token's row in partition q is the partition's
+    // offset + tokens of q in earlier tiles + earlier waves + earlier lanes.
+    if (want_tok || a.part_offset_out) {
+        __syncthreads();   // s_poff complete
+        if (pub_counts && a.part_offset_out)
+            for (int q = tid; q <= P; q += blockDim.x) a.part_offset_out[q] = s_poff[q];
+    }
+    if (want_tok) {
+        const int lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+        // per-wave token counts of each partition (lanes past the tile have
+        // an empty mask, so they vote 0)
+        for (int q = 0; q < P; ++q) {
+            const uint64_t b = __ballot((tmask >> q) & 1ull);
+            if (lane == 0) s_wq[w * P + q] = __popcll(b);
+        }
+        __syncthreads();
+        for (int q = tid; q < P; q += blockDim.x) {
+            int run = 0;
+            for (int ww = 0; ww < nw; ++ww) {
+                const int c = s_wq[ww * P + q];
+                s_wq[ww * P + q] = run;
+                run += c;
+            }
+        }
+        __syncthreads();
+        int32_t *row = a.token_slot_out + (int64_t)(t0 + tid) * P;
+        for (int q = 0; q < P; ++q) {
+            const int bit = (int)((tmask >> q) & 1ull);
+            const uint64_t b = __ballot(bit);
+            const int rank = __popcll(b & lanes_below());
+            if (tid < ntok)
+                row[q] = bit ? s_poff[q] + s_base[E + q] + s_wq[w * P + q] + rank : -1;
+        }
     }
 
     // Slots of this tile's pairs.
@@ -475,14 +552,18 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
     int64_t cpw = (pairs + target_tiles * per_round - 1) / (target_tiles * per_round);
     cpw = cpw < 1 ? 1 : (cpw > kMaxChunksPerWave ? kMaxChunksPerWave : cpw);
     L.chunks_per_wave = (int)cpw;
-    const int tt = (int)(per_round * cpw / L.K);
+    int tt = (int)(per_round * cpw / L.K);
+    if (tt > kSlotsBlock) tt = kSlotsBlock;   // one slots thread per token of a tile
     if (tt < 1) return false;
     L.tile_tokens = tt;
     L.num_tiles = L.T > 0 ? (L.T + tt - 1) / tt : 0;
     const size_t nt = (size_t)(L.num_tiles > 0 ? L.num_tiles : 1);
-    L.row_stride = (L.E + L.P + 1 + 3) & ~3;
+    L.G = p->partitions_per_group > 0 ? p->partitions_per_group : L.P;
+    L.NG = L.P / L.G;
+    L.row_stride = (L.E + L.P + L.NG + 1 + 3) & ~3;
     L.ws_tile_counts = 0;
-    L.ws_bytes = align256(nt * L.row_stride * 4);
+    L.ws_tok_mask = align256(nt * L.row_stride * 4);
+    L.ws_bytes = L.ws_tok_mask + align256((size_t)(L.T > 0 ? L.T : 1) * 8);
     *plan = L;
     return true;
 }
@@ -502,6 +583,10 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     ca.in_part = lay->is_token_in_partition;
     ca.tile_counts = (int32_t *)(ws + L.ws_tile_counts);
     ca.W = L.row_stride;
+    ca.G = L.G;
+    ca.NG = L.NG;
+    const bool want_part = lay->token_slot != nullptr || lay->partition_offset != nullptr;
+    ca.tok_mask = (want_part && L.P <= 64) ? (uint64_t *)(ws + L.ws_tok_mask) : nullptr;
     SlotsArgs sa;
     sa.T = L.T;
     sa.K = L.K;
@@ -514,6 +599,11 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     sa.max_rows = L.max_rows;
     sa.tile_counts = ca.tile_counts;
     sa.W = L.row_stride;
+    sa.NG = L.NG;
+    sa.tok_mask = ca.tok_mask;
+    sa.part_offset_out = lay->partition_offset;
+    sa.token_slot_out = lay->token_slot;
+    sa.group_out = lay->num_tokens_per_group;
     sa.count_out = lay->num_tokens_per_expert;
     sa.offset_out = lay->expert_offset;
     sa.part_out = lay->num_tokens_per_partition;
@@ -522,8 +612,10 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     sa.status = lay->status;
     sa.cum_stats = cum_stats;
 
-    const size_t lds_count = ((size_t)(L.block / 64) * L.E + ca.tile_pairs_max + L.P) * 4;
-    const size_t lds_slots = ((size_t)2 * L.row_stride + L.E + 1 + kRedInts) * 4;
+    const size_t lds_count =
+        ((size_t)(L.block / 64) * L.E + ca.tile_pairs_max + L.P + L.NG) * 4;
+    const size_t lds_slots = ((size_t)2 * L.row_stride + L.E + 1 + L.P + 1 +
+                              (size_t)(kSlotsBlock / 64) * L.P + kRedInts) * 4;
 
     if (L.fused && L.num_tiles > 0) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;

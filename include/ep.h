@@ -55,7 +55,8 @@ enum {
 enum { EP_DTYPE_BF16 = 0, EP_DTYPE_FP8_E4M3 = 1 };
 
 /* Limits of this build. */
-enum { EP_MAX_EXPERTS = 4096, EP_MAX_PARTITIONS = 1024, EP_MAX_TOPK = 256 };
+enum { EP_MAX_EXPERTS = 4096, EP_MAX_PARTITIONS = 1024, EP_MAX_TOPK = 256,
+       EP_MAX_SLOT_PARTITIONS = 64 };
 
 /* Shape of one layout ([API] 2.1 parameter table: num_experts,
  * expert_alignment, num_max_tokens_per_rank; 3.1 num_tokens_per_rank). */
@@ -69,6 +70,8 @@ typedef struct ep_layout_params {
     int32_t capacity;          /* 0: compact padded layout; C > 0: fixed-capacity */
                                /* ("expand") layout, expert e owns rows           */
                                /* [e*C, (e+1)*C); requires C % A == 0             */
+    int32_t partitions_per_group; /* G: partitions per group (0 = P, one group);  */
+                               /* P % G == 0; [API] 3.1 num_tokens_per_rdma_rank  */
     int64_t max_recv_rows;     /* rows of src_of_slot the caller allocated        */
 } ep_layout_params;
 
@@ -84,6 +87,13 @@ typedef struct ep_layout {
     int32_t *dst_slot;                  /* [T*K] receive row of pair (t,k), or -1     */
     int32_t *src_of_slot;               /* [max_recv_rows] t*K+k, or -1 for padding   */
     int32_t *status;                    /* [1]   EP_DEV_* bits                        */
+    /* Optional (NULL = not computed): the non-expanded partition ("rank")       */
+    /* layout of [API] 2.1 (do_expand = False) and 3.1.  A token is received    */
+    /* once by every partition owning one of its experts, tokens in order.      */
+    int32_t *partition_offset;          /* [P+1] first row of each partition         */
+    int32_t *token_slot;                /* [T*P] row of (t, q) or -1; needs P <= 64  */
+    int32_t *num_tokens_per_group;      /* [P/G] tokens reaching any partition of    */
+                                        /*       the group (num_tokens_per_rdma_rank) */
 } ep_layout;
 
 /* Bytes of device workspace ep_get_layout needs for these params (host call,
@@ -114,7 +124,10 @@ int64_t ep_worst_case_recv_rows(const ep_layout_params *params);
  * the pairs of e in ascending t*K+k order (-1 for idx = -1, for an invalid
  * id, and for pairs with j >= C in fixed mode); src_of_slot[s] = t*K+k for
  * used slots and -1 for padding slots (slots >= max_recv_rows are not
- * written); partition membership and per-partition token counts.
+ * written); partition membership and per-partition token counts; and, for
+ * the optional pointers that are set, the partition layout (offsets,
+ * token_slot, tokens per group of G partitions).  The optional pointers
+ * need P <= EP_MAX_SLOT_PARTITIONS (else EP_ERR_UNSUPPORTED).
  * layout->status is overwritten with EP_DEV_BAD_EXPERT / EP_DEV_CAPACITY /
  * EP_DEV_RECV_OVERFLOW (R > max_recv_rows).  T = 0 is valid.
  * Errors: EP_ERR_INVALID_ARG (null pointer, T < 0, K < 1, E < 1, A < 1,
@@ -183,6 +196,48 @@ int ep_combine(const void *y, int32_t hidden, int64_t num_y_rows,
                const ep_layout_params *params, const ep_layout *layout,
                const float *recv_topk_weights, float *combined_topk_weights,
                void *out, void *stream);
+
+/* ep_dispatch_partitioned - the non-expanded dispatch ([API] 2.1 with
+ * do_expand = False: every token once to each partition (rank) that owns one
+ * of its experts; recv_topk_idx / recv_topk_weights come with the row).
+ * Needs layout->token_slot (from ep_get_layout).  Arguments as ep_dispatch,
+ * plus:
+ *   topk_idx            device int64 [T, K] (the routing the layout came from).
+ *   recv_topk_idx       device int64 [num_recv_rows, K] or NULL: for the row of
+ *                       (t, q), e - q*E/P when pair (t, k) goes to partition q
+ *                       (the expert id local to the partition), else -1.
+ *   recv_topk_weights   device float [num_recv_rows, K] or NULL: w[t,k] (1 when
+ *                       topk_weights is NULL) for local pairs, else 0.
+ * Receive rows are [partition_offset[q], partition_offset[q+1]) for partition
+ * q, tokens ascending; there is no padding.  Errors as ep_dispatch;
+ * EP_ERR_UNSUPPORTED when P > EP_MAX_SLOT_PARTITIONS. */
+int ep_dispatch_partitioned(const void *x, int x_dtype, const float *x_scales, int recv_dtype,
+                            int32_t hidden, int32_t scale_group, const int64_t *topk_idx,
+                            const float *topk_weights, const ep_layout_params *params,
+                            const ep_layout *layout, void *recv_x, float *recv_scales,
+                            int64_t *recv_topk_idx, float *recv_topk_weights,
+                            int64_t num_recv_rows, void *stream);
+
+/* ep_combine_partitioned - combine for the non-expanded layout ([API] 3.2:
+ * a plain sum; each partition's row already holds its weighted expert sum):
+ * out[t] = bf16_rne(acc), acc = 0; acc += bias0; acc += bias1; then for q
+ * ascending with token_slot[t,q] >= 0: acc += y[token_slot[t,q]] (fp32).
+ * y is bf16 [num_y_rows, hidden]; needs layout->token_slot. */
+int ep_combine_partitioned(const void *y, int32_t hidden, int64_t num_y_rows, const void *bias0,
+                           const void *bias1, const ep_layout_params *params,
+                           const ep_layout *layout, void *out, void *stream);
+
+/* ep_combine_reduced - the two-level ("reduced") combine on the expanded
+ * layout ([API] 2.2: reduced combine, multi-level reduction).  Level 1, per
+ * partition q: p_q = fmaf chain from 0 over the token's pairs in q (k
+ * ascending), rounded to bf16 (the dtype a partial travels in).  Level 2:
+ * acc = 0; acc += bias0; acc += bias1; acc += p_q for q ascending (fp32);
+ * out = bf16_rne(acc).  topk_idx is the routing (device int64 [T, K]); the
+ * other arguments are as ep_combine.  EP_ERR_UNSUPPORTED when K > 64. */
+int ep_combine_reduced(const void *y, int32_t hidden, int64_t num_y_rows, const int64_t *topk_idx,
+                       const float *topk_weights, const void *bias0, const void *bias1,
+                       const ep_layout_params *params, const ep_layout *layout, void *out,
+                       void *stream);
 
 /* ep_cast_fp8 - per (token, group) cast of bf16 rows to OCP e4m3
  * ([API] 4.2 per_token_cast_to_fp8, with one scale per group of G channels;

@@ -28,8 +28,8 @@ def test_library_exports_every_symbol():
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
-def _params(T=16, K=2, E=8, A=1, P=1, C=0, rows=None):
-    p = _abi.LayoutParams(T, K, E, A, P, C, 0)
+def _params(T=16, K=2, E=8, A=1, P=1, C=0, rows=None, G=0):
+    p = _abi.LayoutParams(T, K, E, A, P, C, G)
     p.max_recv_rows = rows if rows is not None else _abi.load().ep_worst_case_recv_rows(ctypes.byref(p))
     return p
 
@@ -57,6 +57,8 @@ def test_workspace_bytes():
     (dict(C=4, rows=10), _abi.EP_ERR_INVALID_ARG),    # E*C > max_recv_rows
     (dict(E=8192, P=1), _abi.EP_ERR_UNSUPPORTED),
     (dict(K=300, E=512), _abi.EP_ERR_UNSUPPORTED),
+    (dict(E=8, P=4, G=3), _abi.EP_ERR_INVALID_ARG),   # P % G != 0
+    (dict(E=8, P=4, G=-1), _abi.EP_ERR_INVALID_ARG),
 ])
 def test_get_layout_rejects_bad_params_before_launch(kw, code):
     lib = _abi.load()
@@ -119,6 +121,46 @@ def test_combine_and_cast_reject_bad_arguments():
     assert lib.ep_cast_fp8(ctypes.c_void_p(16), 4, 384, 96, ctypes.c_void_p(16),
                            ctypes.c_void_p(16), None) == _abi.EP_ERR_UNSUPPORTED
     assert lib.ep_cast_fp8(ctypes.c_void_p(16), 0, 128, 128, None, None, None) == _abi.EP_OK
+
+
+def test_partition_layout_limits():
+    lib = _abi.load()
+    p = _params(T=4, K=2, E=128, P=128)
+    lay = _abi.LayoutPtrs(*([16] * 8), 16, None)           # token_slot with P > 64
+    assert lib.ep_get_layout(ctypes.c_void_p(16), ctypes.byref(p), ctypes.byref(lay), None,
+                             ctypes.c_void_p(256), 1 << 20, None) == _abi.EP_ERR_UNSUPPORTED
+
+
+def test_partitioned_calls_reject_bad_arguments():
+    lib = _abi.load()
+    bf = _abi.EP_DTYPE_BF16
+    p = _params(T=4, K=2, E=8, P=4)
+    no_slots = _abi.LayoutPtrs(*([16] * 7))
+    lay = _abi.LayoutPtrs(*([16] * 10))
+
+    def disp(layout, H=64, idx=16, ri=16):
+        return lib.ep_dispatch_partitioned(ctypes.c_void_p(16), bf, None, bf, H, 128,
+                                           ctypes.c_void_p(idx) if idx else None, None,
+                                           ctypes.byref(p), ctypes.byref(layout),
+                                           ctypes.c_void_p(16), None,
+                                           ctypes.c_void_p(ri) if ri else None, None, 16, None)
+    assert disp(no_slots) == _abi.EP_ERR_INVALID_ARG           # no token_slot
+    assert disp(lay, H=60) == _abi.EP_ERR_INVALID_ARG
+    assert disp(lay, idx=0) == _abi.EP_ERR_INVALID_ARG         # recv_topk_idx needs topk_idx
+    assert lib.ep_combine_partitioned(ctypes.c_void_p(16), 64, 16, None, None, ctypes.byref(p),
+                                      ctypes.byref(no_slots), ctypes.c_void_p(16),
+                                      None) == _abi.EP_ERR_INVALID_ARG
+    big = _params(T=4, K=2, E=128, P=128)
+    assert lib.ep_combine_partitioned(ctypes.c_void_p(16), 64, 16, None, None, ctypes.byref(big),
+                                      ctypes.byref(lay), ctypes.c_void_p(16),
+                                      None) == _abi.EP_ERR_UNSUPPORTED
+    assert lib.ep_combine_reduced(ctypes.c_void_p(16), 64, 16, None, None, None, None,
+                                  ctypes.byref(p), ctypes.byref(lay), ctypes.c_void_p(16),
+                                  None) == _abi.EP_ERR_INVALID_ARG   # no topk_idx
+    k100 = _params(T=4, K=100, E=128, P=4)
+    assert lib.ep_combine_reduced(ctypes.c_void_p(16), 64, 16, ctypes.c_void_p(16), None, None,
+                                  None, ctypes.byref(k100), ctypes.byref(lay),
+                                  ctypes.c_void_p(16), None) == _abi.EP_ERR_UNSUPPORTED
 
 
 def test_status_strings():

@@ -163,3 +163,24 @@ def test_reduced_combine_within_tolerance_of_float64():
                                                           w.topk_weights, b0)).astype(np.float64)
     f64 = oracle.combine_f64(y, lay.dst, w.topk_weights, b0)
     assert np.all(np.abs(red - f64) <= 1e-2 + 1e-2 * np.abs(f64))
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_reduced_combine_error_bound(weighted):
+    """With bf16 partials the error against the exact sum is at most
+    2^-9 of each partial's magnitude plus 2^-9 of the result (and fp32
+    rounding far below that): |out - exact| <= 2^-8 (|exact| + S) with
+    S = sum_k |w y|.  Unit weights over 8 pairs exceed a flat 1e-2 bound."""
+    w = ep_inputs.make_workload("skewed", seed=3, T=256, K=8, E=256, A=128, drop_p=0.05,
+                                with_x=False)
+    lay = oracle.get_layout(w.topk_idx, 256, 128, 32)
+    y = ep_inputs.make_y(w.rng, lay.R, 512)
+    wt = w.topk_weights if weighted else None
+    red = oracle.bf16_to_float(oracle.combine_reduced_f32(y, w.topk_idx, lay.dst, 256, 32, wt))
+    f64 = oracle.combine_f64(y, lay.dst, wt)
+    S = oracle.combine_f64(y & np.uint16(0x7FFF), lay.dst, None if wt is None else np.abs(wt))
+    err = np.abs(red.astype(np.float64) - f64)
+    assert np.all(err <= 2.0 ** -8 * (np.abs(f64) + S) + 1e-6)
+    # the bf16 partials do show: some element differs from the one-level combine
+    one = oracle.bf16_to_float(oracle.combine_f32(y, lay.dst, wt))
+    assert np.any(one != red)
