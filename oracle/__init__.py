@@ -52,6 +52,12 @@ def _load():
         _lib.oracle_e4m3_to_float.argtypes = [ctypes.c_uint8]
         _lib.oracle_bf16_to_float.restype = ctypes.c_float
         _lib.oracle_bf16_to_float.argtypes = [ctypes.c_uint16]
+        _lib.oracle_pow2_ceil.restype = ctypes.c_float
+        _lib.oracle_pow2_ceil.argtypes = [ctypes.c_float]
+        _lib.oracle_ue8m0_of.restype = ctypes.c_uint8
+        _lib.oracle_ue8m0_of.argtypes = [ctypes.c_float]
+        _lib.oracle_ue8m0_to_float.restype = ctypes.c_float
+        _lib.oracle_ue8m0_to_float.argtypes = [ctypes.c_uint8]
     return _lib
 
 
@@ -104,8 +110,8 @@ def get_layout(topk_idx, num_experts, expert_alignment=1, num_partitions=1,
 def dispatch(x_rows, layout: Layout, topk_weights=None, x_scales=None, zero_padding=False,
              recv_init=None, scales_init=None):
     """recv[dst[t,k]] = x[t] byte for byte.  x_rows is [T, H] of any dtype
-    (bf16 bits as uint16, fp8 codes as uint8); x_scales [T, H/G] float32 or
-    None.  Returns (recv [R, ...], recv_scales or None, recv_w [R]).  Padding
+    (bf16 bits as uint16, fp8 codes as uint8); x_scales [T, H/G] (float32, or
+    uint8 UE8M0 bytes) or None.  Returns (recv [R, ...], recv_scales or None, recv_w [R]).  Padding
     rows keep recv_init's content (zeros by default) unless zero_padding."""
     lib = _load()
     x = np.ascontiguousarray(x_rows)
@@ -115,13 +121,13 @@ def dispatch(x_rows, layout: Layout, topk_weights=None, x_scales=None, zero_padd
     row_bytes = x[0].nbytes if T else x.itemsize * int(np.prod(x.shape[1:]))
     recv = (np.zeros((R,) + x.shape[1:], x.dtype) if recv_init is None
             else np.array(recv_init, dtype=x.dtype, copy=True))
-    xs = _c(x_scales, np.float32)
+    xs = None if x_scales is None else np.ascontiguousarray(x_scales)   # f32 or UE8M0 bytes
     recv_s = None
     srow = 0
     if xs is not None:
-        srow = xs.shape[1] * 4
-        recv_s = (np.zeros((R, xs.shape[1]), np.float32) if scales_init is None
-                  else np.array(scales_init, dtype=np.float32, copy=True))
+        srow = xs.shape[1] * xs.itemsize
+        recv_s = (np.zeros((R, xs.shape[1]), xs.dtype) if scales_init is None
+                  else np.array(scales_init, dtype=xs.dtype, copy=True))
     recv_w = np.zeros(R, np.float32)
     w = _c(topk_weights, np.float32)
     lib.oracle_dispatch(_p(x), _i64(row_bytes), _p(xs), _i64(srow), _p(w), _i64(T), _i64(K),
@@ -142,6 +148,41 @@ def cast_fp8(x_bits, group=128):
     if rc != 0:
         raise ValueError("oracle_cast_fp8: invalid arguments")
     return q, s
+
+
+def cast_fp8_pow2(x_bits, group=128, ue8m0=False):
+    """Per (token, group) e4m3 cast with the scale rounded up to a power of
+    two.  Returns (codes uint8 [T,H], scales f32 [T,H/G], UE8M0 bytes uint8
+    [T,H/G] or None)."""
+    lib = _load()
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    q = np.zeros((T, H), np.uint8)
+    s = np.zeros((T, H // group), np.float32)
+    e8 = np.zeros((T, H // group), np.uint8) if ue8m0 else None
+    rc = lib.oracle_cast_fp8_pow2(_p(x), _i64(T), _i64(H), _i64(group),
+                                  ctypes.c_int(2 if ue8m0 else 1), _p(q), _p(s), _p(e8))
+    if rc != 0:
+        raise ValueError("oracle_cast_fp8_pow2: invalid arguments")
+    return q, s, e8
+
+
+def pow2_ceil(v):
+    lib = _load()
+    return np.array([lib.oracle_pow2_ceil(ctypes.c_float(float(a))) for a in np.ravel(v)],
+                    np.float32)
+
+
+def ue8m0_of(v):
+    lib = _load()
+    return np.array([lib.oracle_ue8m0_of(ctypes.c_float(float(a))) for a in np.ravel(v)],
+                    np.uint8)
+
+
+def ue8m0_to_float(b):
+    lib = _load()
+    return np.array([lib.oracle_ue8m0_to_float(ctypes.c_uint8(int(a))) for a in np.ravel(b)],
+                    np.float32)
 
 
 def cast_back(q, scales, group=128):
@@ -262,11 +303,11 @@ def dispatch_partitioned(x_rows, topk_idx, play, topk_weights=None, x_scales=Non
     row_bytes = x[0].nbytes if T else x.itemsize * int(np.prod(x.shape[1:]))
     recv = (np.zeros((Rp,) + x.shape[1:], x.dtype) if recv_init is None
             else np.array(recv_init, dtype=x.dtype, copy=True))
-    xs = _c(x_scales, np.float32)
+    xs = None if x_scales is None else np.ascontiguousarray(x_scales)   # f32 or UE8M0 bytes
     recv_s, srow = None, 0
     if xs is not None:
-        srow = xs.shape[1] * 4
-        recv_s = np.zeros((Rp, xs.shape[1]), np.float32)
+        srow = xs.shape[1] * xs.itemsize
+        recv_s = np.zeros((Rp, xs.shape[1]), xs.dtype)
     recv_idx = np.zeros((max(Rp, 1), K), np.int64)
     recv_w = np.zeros((max(Rp, 1), K), np.float32)
     w = _c(topk_weights, np.float32)

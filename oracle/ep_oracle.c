@@ -304,6 +304,61 @@ int oracle_cast_fp8(const uint16_t *x, int64_t T, int64_t H, int64_t G,
     return OR_OK;
 }
 
+/* Low-latency scale formats ([API] 3.3 low_latency_dispatch: round_scale
+ * rounds the scale to a power of two; use_ue8m0 stores it as UE8M0).
+ * Readings: the power of two is the smallest one >= amax'/448 (rounding up
+ * keeps |x| / scale <= 448, so no code overflows), taken on the fp32 quotient;
+ * UE8M0 is an unsigned 8-bit biased exponent b with value 2^(b - 127), one
+ * byte per (token, group).  Codes are E4M3(x / scale) as before; with a
+ * power-of-two scale the division is exact.
+ * fmt 1: fp32 power-of-two scales into scales_f32; fmt 2: UE8M0 bytes into
+ * scales_e8 (and, when non-NULL, the same scales as fp32 into scales_f32). */
+float oracle_pow2_ceil(float s)
+{
+    int e;
+    float m = frexpf(s, &e);          /* s = m * 2^e, m in [0.5, 1) */
+    return m == 0.5f ? s : ldexpf(1.0f, e);
+}
+
+uint8_t oracle_ue8m0_of(float pow2)
+{
+    int e;
+    frexpf(pow2, &e);                 /* pow2 = 0.5 * 2^e = 2^(e-1) */
+    return (uint8_t)(e - 1 + 127);
+}
+
+float oracle_ue8m0_to_float(uint8_t b)
+{
+    return ldexpf(1.0f, (int)b - 127);
+}
+
+int oracle_cast_fp8_pow2(const uint16_t *x, int64_t T, int64_t H, int64_t G, int fmt,
+                         uint8_t *q, float *scales_f32, uint8_t *scales_e8)
+{
+    if (T < 0 || H < 1 || G < 1 || H % G != 0 || (fmt != 1 && fmt != 2)) return OR_EINVAL;
+    int64_t ng = H / G;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t g = 0; g < ng; ++g) {
+            float amax = 0.0f;
+            for (int64_t c = g * G; c < (g + 1) * G; ++c) {
+                float a = fabsf(oracle_bf16_to_float(x[t * H + c]));
+                if (a > amax) amax = a;
+            }
+            volatile float ap = amax > 1e-4f ? amax : 1e-4f;
+            volatile float s0 = ap / 448.0f;
+            float s = oracle_pow2_ceil(s0);
+            if (scales_f32) scales_f32[t * ng + g] = s;
+            if (fmt == 2 && scales_e8) scales_e8[t * ng + g] = oracle_ue8m0_of(s);
+            for (int64_t c = g * G; c < (g + 1) * G; ++c) {
+                volatile float xv = oracle_bf16_to_float(x[t * H + c]);
+                volatile float d = xv / s;
+                q[t * H + c] = oracle_e4m3_from_float(d);
+            }
+        }
+    }
+    return OR_OK;
+}
+
 /* Decode (the page's per_token_cast_back): x^ = float(q) * s, in fp32. */
 void oracle_cast_back(const uint8_t *q, const float *scales, int64_t T,
                       int64_t H, int64_t G, float *out)
