@@ -67,6 +67,41 @@ def load_traffic(name):
     return data.get("kernels", {}).get(name)
 
 
+def partitioned_legs(ep, torch, dev, w, idx, wts, x, y, lay, out_c, per_op):
+    """The non-expanded partition layout, its dispatch and combine, and the
+    two-level combine on the expanded layout (algorithmic bytes per op:
+    rows moved plus the per-row metadata each kernel reads or writes)."""
+    T, H, E, K, P = w.num_tokens, w.hidden, w.num_experts, w.num_topk, w.num_partitions
+    A, C = w.expert_alignment, w.capacity
+    pl = ep.ep_get_layout(idx, E, A, P, C, partition_layout=True)
+    Rp = pl.num_partition_rows()
+    N = int((w.topk_idx >= 0).sum())
+    res = {"Rp": Rp}
+    res["layout_partitioned"] = per_op(
+        lambda: ep.ep_get_layout(idx, E, A, P, C, layout=pl, partition_layout=True),
+        T * K * 8 + T * K * 4 + T * P + T * P * 4 + R_of(pl) * 4, T)
+    recv = torch.empty((Rp, H), dtype=torch.bfloat16, device=dev)
+    ri = torch.empty((Rp, K), dtype=torch.int64, device=dev)
+    rw = torch.empty((Rp, K), dtype=torch.float32, device=dev)
+    meta = T * P * 4 + T * K * 12
+    res["dispatch_partitioned"] = per_op(
+        lambda: ep.ep_dispatch_partitioned(x, pl, idx, wts, num_recv_rows=Rp,
+                                           out=(recv, None, ri, rw)),
+        T * H * 2 + Rp * H * 2 + Rp * K * 12 + meta, T)
+    res["combine_partitioned"] = per_op(
+        lambda: ep.ep_combine_partitioned(recv, pl, out=out_c), Rp * H * 2 + T * H * 2 + T * P * 4, T)
+    res["combine_reduced"] = per_op(
+        lambda: ep.ep_combine_reduced(y, lay, idx, wts, out=out_c),
+        N * H * 2 + T * H * 2 + T * K * 16, T)
+    assert pl.check() == 0
+    del recv, ri, rw
+    return res
+
+
+def R_of(lay):
+    return int(lay.expert_offset[-1].item())
+
+
 def other_workloads(ep, torch, dev, steps):
     """Per-operation timings for the fp8, decode, skewed and tiny workloads
     (K back-to-back launches between two events; algorithmic bytes per op)."""
@@ -133,6 +168,8 @@ def other_workloads(ep, torch, dev, steps):
             del recv
         res["combine"] = per_op(lambda: ep.ep_combine(y, lay, wts, out=out_c), cb, T)
         assert lay.check() == 0
+        if w.num_partitions > 1:
+            res.update(partitioned_legs(ep, torch, dev, w, idx, wts, x, y, lay, out_c, per_op))
         out[name] = res
         del y, x, lay
         torch.cuda.empty_cache()

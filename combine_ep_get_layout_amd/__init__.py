@@ -187,48 +187,52 @@ def _is_fp8(t: torch.Tensor) -> bool:
     return t.dtype in (torch.float8_e4m3fn, torch.uint8)
 
 
+# Scale formats of the fp8 rows: fp32 amax/448, fp32 rounded up to a power of
+# two, or that power of two as one UE8M0 byte (biased exponent).
+_FP8_DTYPES = {"fp32": _abi.EP_DTYPE_FP8_E4M3, "pow2": _abi.EP_DTYPE_FP8_E4M3_POW2,
+               "ue8m0": _abi.EP_DTYPE_FP8_E4M3_UE8M0}
+
+
+def _fp8_dtype(scale_fmt: str) -> int:
+    if scale_fmt not in _FP8_DTYPES:
+        raise ValueError(f"scale_fmt must be one of {sorted(_FP8_DTYPES)}")
+    return _FP8_DTYPES[scale_fmt]
+
+
+def _scale_dtype(scale_fmt: str):
+    return torch.uint8 if scale_fmt == "ue8m0" else torch.float32
+
+
 def ep_dispatch(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]], layout: Layout,
                 topk_weights: Optional[torch.Tensor] = None, recv_fp8: bool = False,
                 scale_group: int = 128, zero_padding: bool = False,
                 num_recv_rows: Optional[int] = None,
-                out: Optional[Sequence[Optional[torch.Tensor]]] = None):
+                out: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                scale_fmt: str = "fp32"):
     """Permute token rows into the receive buffer.
 
-    x: bf16 [T, H], or (fp8 codes [T, H], fp32 scales [T, H/G]).  With bf16 x
-    and recv_fp8=True the rows are cast to e4m3 on the fly.  Returns
+    x: bf16 [T, H], or (fp8 codes [T, H], scales [T, H/G]: float32, or uint8
+    UE8M0 bytes).  With bf16 x and recv_fp8=True the rows are cast to e4m3 on
+    the fly with scales in `scale_fmt` ("fp32", "pow2" or "ue8m0").  Returns
     (recv_x, recv_scales or None, recv_topk_weights or None); recv buffers
     have num_recv_rows rows (default: the layout's max_recv_rows)."""
     lib = load_library()
-    x_scales = None
-    if isinstance(x, (tuple, list)):
-        x, x_scales = x
-    _need_cuda(x, "x")
+    x, x_scales, scale_group, x_dtype, recv_dtype, scale_fmt = _x_and_dtypes(
+        x, recv_fp8, scale_group, scale_fmt)
     T, H = x.shape
     if T != layout.num_tokens:
         raise ValueError("x rows != layout tokens")
-    fp8_in = _is_fp8(x)
-    if fp8_in:
-        if x_scales is None:
-            raise ValueError("fp8 x needs its scales")
-        _need_cuda(x_scales, "x_scales")
-        scale_group = H // x_scales.shape[1]
-        x_dtype, recv_dtype = _abi.EP_DTYPE_FP8_E4M3, _abi.EP_DTYPE_FP8_E4M3
-    else:
-        if x.dtype != torch.bfloat16:
-            raise ValueError("x must be bf16 or fp8")
-        x_dtype = _abi.EP_DTYPE_BF16
-        recv_dtype = _abi.EP_DTYPE_FP8_E4M3 if recv_fp8 else _abi.EP_DTYPE_BF16
     rows = layout.max_recv_rows if num_recv_rows is None else int(num_recv_rows)
     dev = x.device
     recv_x = recv_s = recv_w = None
     if out is not None:
         recv_x, recv_s, recv_w = (list(out) + [None, None, None])[:3]
-    fp8_out = recv_dtype == _abi.EP_DTYPE_FP8_E4M3
+    fp8_out = recv_dtype != _abi.EP_DTYPE_BF16
     if recv_x is None:
         recv_x = torch.empty((rows, H), dtype=torch.float8_e4m3fn if fp8_out else torch.bfloat16,
                              device=dev)
     if fp8_out and recv_s is None:
-        recv_s = torch.empty((rows, H // scale_group), dtype=torch.float32, device=dev)
+        recv_s = torch.empty((rows, H // scale_group), dtype=_scale_dtype(scale_fmt), device=dev)
     if topk_weights is not None:
         _need_cuda(topk_weights, "topk_weights")
         if topk_weights.dtype != torch.float32:
@@ -289,25 +293,30 @@ def ep_combine(y: torch.Tensor, layout: Layout, topk_weights: Optional[torch.Ten
 
 
 def ep_cast_fp8(x: torch.Tensor, group: int = 128,
-                out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+                out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, scale_fmt: str = "fp32"):
     """Per (token, group of `group` channels) cast of bf16 rows to e4m3.
-    Returns (codes float8_e4m3fn [T, H], scales float32 [T, H/group])."""
+    Returns (codes float8_e4m3fn [T, H], scales [T, H/group]): float32 for
+    scale_fmt "fp32" (amax/448) and "pow2" (rounded up to a power of two),
+    uint8 biased exponents for "ue8m0"."""
     lib = load_library()
     _need_cuda(x, "x")
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bf16")
+    out_dtype = _fp8_dtype(scale_fmt)
     T, H = x.shape
     if out is None:
         q = torch.empty((T, H), dtype=torch.float8_e4m3fn, device=x.device)
-        s = torch.empty((T, H // group), dtype=torch.float32, device=x.device)
+        s = torch.empty((T, H // group), dtype=_scale_dtype(scale_fmt), device=x.device)
     else:
         q, s = out
-    rc = lib.ep_cast_fp8(_ptr(x), T, H, group, _ptr(q), _ptr(s), _stream(x.device))
+    rc = lib.ep_cast_fp8(_ptr(x), T, H, group, out_dtype, _ptr(q), _ptr(s), _stream(x.device))
     _abi.check("ep_cast_fp8", rc)
     return q, s
 
 
-def _x_and_dtypes(x, recv_fp8, scale_group):
+def _x_and_dtypes(x, recv_fp8, scale_group, scale_fmt="fp32"):
+    """(x, x_scales, G, x_dtype, recv_dtype, scale_fmt) for a dispatch call;
+    fp8 input with uint8 scales is UE8M0."""
     x_scales = None
     if isinstance(x, (tuple, list)):
         x, x_scales = x
@@ -317,26 +326,37 @@ def _x_and_dtypes(x, recv_fp8, scale_group):
         if x_scales is None:
             raise ValueError("fp8 x needs its scales")
         _need_cuda(x_scales, "x_scales")
-        return x, x_scales, H // x_scales.shape[1], _abi.EP_DTYPE_FP8_E4M3, _abi.EP_DTYPE_FP8_E4M3
+        if x_scales.dtype == torch.uint8:
+            scale_fmt = "ue8m0"
+        elif x_scales.dtype != torch.float32:
+            raise ValueError("fp8 scales must be float32 or uint8 (UE8M0)")
+        elif scale_fmt == "ue8m0":
+            scale_fmt = "fp32"
+        d = _fp8_dtype(scale_fmt)
+        return x, x_scales, H // x_scales.shape[1], d, d, scale_fmt
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bf16 or fp8")
-    recv = _abi.EP_DTYPE_FP8_E4M3 if recv_fp8 else _abi.EP_DTYPE_BF16
-    return x, None, scale_group, _abi.EP_DTYPE_BF16, recv
+    recv = _fp8_dtype(scale_fmt) if recv_fp8 else _abi.EP_DTYPE_BF16
+    return x, None, scale_group, _abi.EP_DTYPE_BF16, recv, scale_fmt
 
 
 def ep_dispatch_partitioned(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]],
                             layout: Layout, topk_idx: torch.Tensor,
                             topk_weights: Optional[torch.Tensor] = None, recv_fp8: bool = False,
-                            scale_group: int = 128, num_recv_rows: Optional[int] = None):
+                            scale_group: int = 128, num_recv_rows: Optional[int] = None,
+                            out: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                            scale_fmt: str = "fp32"):
     """Non-expanded dispatch: token t's row goes once to every partition q
     that owns one of its experts, at layout.token_slot[t, q].  Returns
     (recv_x, recv_scales or None, recv_topk_idx int64 [rows, K] with the
     partition-local expert id or -1, recv_topk_weights float32 [rows, K] or
-    None).  rows defaults to T*P, the worst case."""
+    None).  rows defaults to T*P, the worst case; `out` may supply the four
+    buffers (None entries are allocated)."""
     lib = load_library()
     if layout.token_slot is None:
         raise ValueError("layout was built without partition_layout=True")
-    x, x_scales, scale_group, x_dtype, recv_dtype = _x_and_dtypes(x, recv_fp8, scale_group)
+    x, x_scales, scale_group, x_dtype, recv_dtype, scale_fmt = _x_and_dtypes(
+        x, recv_fp8, scale_group, scale_fmt)
     T, H = x.shape
     K = layout.num_topk
     if T != layout.num_tokens:
@@ -344,16 +364,25 @@ def ep_dispatch_partitioned(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Ten
     _need_cuda(topk_idx, "topk_idx")
     rows = T * layout.num_partitions if num_recv_rows is None else int(num_recv_rows)
     dev = x.device
-    fp8_out = recv_dtype == _abi.EP_DTYPE_FP8_E4M3
-    recv_x = torch.empty((rows, H), dtype=torch.float8_e4m3fn if fp8_out else torch.bfloat16,
-                         device=dev)
-    recv_s = torch.empty((rows, H // scale_group), dtype=torch.float32, device=dev) \
-        if fp8_out else None
-    recv_i = torch.empty((rows, K), dtype=torch.int64, device=dev)
-    recv_w = None
+    fp8_out = recv_dtype != _abi.EP_DTYPE_BF16
+    recv_x = recv_s = recv_i = recv_w = None
+    if out is not None:
+        recv_x, recv_s, recv_i, recv_w = (list(out) + [None] * 4)[:4]
+    if recv_x is None:
+        recv_x = torch.empty((rows, H), dtype=torch.float8_e4m3fn if fp8_out else torch.bfloat16,
+                             device=dev)
+    if fp8_out and recv_s is None:
+        recv_s = torch.empty((rows, H // scale_group), dtype=_scale_dtype(scale_fmt), device=dev)
+    if recv_i is None:
+        recv_i = torch.empty((rows, K), dtype=torch.int64, device=dev)
     if topk_weights is not None:
         _need_cuda(topk_weights, "topk_weights")
-        recv_w = torch.empty((rows, K), dtype=torch.float32, device=dev)
+        if recv_w is None:
+            recv_w = torch.empty((rows, K), dtype=torch.float32, device=dev)
+    else:
+        recv_w = None
+    if recv_x.shape[0] < rows or recv_i.shape[0] < rows:
+        raise ValueError("receive buffers have fewer rows than num_recv_rows")
     params = layout.params
     ptrs = layout.ptrs()
     rc = lib.ep_dispatch_partitioned(_ptr(x), x_dtype, _ptr(x_scales), recv_dtype, H, scale_group,

@@ -19,6 +19,8 @@ EP_DEV_RECV_OVERFLOW = 4
 
 EP_DTYPE_BF16 = 0
 EP_DTYPE_FP8_E4M3 = 1
+EP_DTYPE_FP8_E4M3_POW2 = 2
+EP_DTYPE_FP8_E4M3_UE8M0 = 3
 
 EP_MAX_EXPERTS = 4096
 EP_MAX_PARTITIONS = 1024
@@ -90,7 +92,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ep_combine_reduced.argtypes = [vp, i32, i64, vp, vp, vp, vp, P(LayoutParams),
                                        P(LayoutPtrs), vp, vp]
     lib.ep_combine_reduced.restype = ctypes.c_int
-    lib.ep_cast_fp8.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.ep_cast_fp8.argtypes = [vp, i32, i32, i32, ctypes.c_int, vp, vp, vp]
     lib.ep_cast_fp8.restype = ctypes.c_int
     lib.ep_status_string.argtypes = [ctypes.c_int]
     lib.ep_status_string.restype = ctypes.c_char_p

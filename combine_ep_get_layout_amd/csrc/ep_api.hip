@@ -83,38 +83,57 @@ static bool valid_group(int hidden, int group) {
     return hidden % group == 0;
 }
 
-int ep_dispatch(const void *x, int x_dtype, const float *x_scales, int recv_dtype, int32_t hidden,
+static bool is_fp8(int d) {
+    return d == EP_DTYPE_FP8_E4M3 || d == EP_DTYPE_FP8_E4M3_POW2 || d == EP_DTYPE_FP8_E4M3_UE8M0;
+}
+
+static int scale_fmt_of(int d) {
+    return d == EP_DTYPE_FP8_E4M3_POW2 ? 1 : (d == EP_DTYPE_FP8_E4M3_UE8M0 ? 2 : 0);
+}
+
+// Row mode (0 copy bf16, 1 copy fp8 with its scales, 2 cast bf16 -> fp8) and
+// scale format from the two dtypes, with the checks both dispatches share.
+static int dispatch_io(int x_dtype, const void *x, const void *x_scales, int recv_dtype,
+                       int32_t hidden, int32_t scale_group, int32_t T, const void *recv_x,
+                       const void *recv_scales, int64_t num_recv_rows, int *mode, int *fmt) {
+    if (num_recv_rows < 0 || hidden < 1) return EP_ERR_INVALID_ARG;
+    if (x_dtype == EP_DTYPE_BF16 && recv_dtype == EP_DTYPE_BF16) *mode = 0;
+    else if (is_fp8(x_dtype) && x_dtype == recv_dtype) *mode = 1;
+    else if (x_dtype == EP_DTYPE_BF16 && is_fp8(recv_dtype)) *mode = 2;
+    else return EP_ERR_INVALID_ARG;
+    *fmt = scale_fmt_of(recv_dtype);
+    if (*mode == 0 && hidden % 8 != 0) return EP_ERR_INVALID_ARG;
+    if (*mode != 0) {
+        if (hidden % 16 != 0) return EP_ERR_INVALID_ARG;
+        if (!valid_group(hidden, scale_group)) return EP_ERR_UNSUPPORTED;
+        if (*mode == 2 && scale_group == hidden && hidden > 16 * 64 * 8) return EP_ERR_UNSUPPORTED;
+        if (!recv_scales && num_recv_rows > 0) return EP_ERR_INVALID_ARG;
+        if (*mode == 1 && !x_scales && T > 0) return EP_ERR_INVALID_ARG;
+    }
+    if (T > 0 && (!x || !aligned16(x))) return EP_ERR_INVALID_ARG;
+    if (num_recv_rows > 0 && (!recv_x || !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
+int ep_dispatch(const void *x, int x_dtype, const void *x_scales, int recv_dtype, int32_t hidden,
                 int32_t scale_group, const float *topk_weights, const ep_layout_params *p,
-                const ep_layout *layout, void *recv_x, float *recv_scales,
+                const ep_layout *layout, void *recv_x, void *recv_scales,
                 float *recv_topk_weights, int64_t num_recv_rows, int zero_padding, void *stream) {
     int rc = check_params(p);
     if (rc != EP_OK) return rc;
     if (!layout || !layout->num_tokens_per_expert || !layout->expert_offset || !layout->status)
         return EP_ERR_INVALID_ARG;
     if (p->num_tokens > 0 && !layout->dst_slot) return EP_ERR_INVALID_ARG;
-    if (num_recv_rows < 0 || hidden < 1) return EP_ERR_INVALID_ARG;
-    int mode;
-    if (x_dtype == EP_DTYPE_BF16 && recv_dtype == EP_DTYPE_BF16) mode = 0;
-    else if (x_dtype == EP_DTYPE_FP8_E4M3 && recv_dtype == EP_DTYPE_FP8_E4M3) mode = 1;
-    else if (x_dtype == EP_DTYPE_BF16 && recv_dtype == EP_DTYPE_FP8_E4M3) mode = 2;
-    else return EP_ERR_INVALID_ARG;
-    if (mode == 0 && hidden % 8 != 0) return EP_ERR_INVALID_ARG;
-    if (mode != 0) {
-        if (hidden % 16 != 0) return EP_ERR_INVALID_ARG;
-        if (!valid_group(hidden, scale_group)) return EP_ERR_UNSUPPORTED;
-        if (mode == 2 && scale_group == hidden && hidden > 16 * 64 * 8) return EP_ERR_UNSUPPORTED;
-        if (!recv_scales && num_recv_rows > 0) return EP_ERR_INVALID_ARG;
-        if (mode == 1 && !x_scales && p->num_tokens > 0) return EP_ERR_INVALID_ARG;
-    }
-    if (p->num_tokens > 0 && (!x || !aligned16(x))) return EP_ERR_INVALID_ARG;
-    if (num_recv_rows > 0 && (!recv_x || !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
+    int mode = 0, fmt = 0;
+    rc = dispatch_io(x_dtype, x, x_scales, recv_dtype, hidden, scale_group, p->num_tokens, recv_x,
+                     recv_scales, num_recv_rows, &mode, &fmt);
+    if (rc != EP_OK) return rc;
     ep::DispatchArgs a = {};
     a.x = x;
     a.x_scales = x_scales;
+    a.scale_fmt = fmt;
     a.topk_weights = topk_weights;
     a.dst = layout->dst_slot;
-    a.src_of_slot = layout->src_of_slot;
-    a.src_rows = p->max_recv_rows;
     a.counts = layout->num_tokens_per_expert;
     a.offsets = layout->expert_offset;
     a.status = layout->status;
@@ -166,10 +185,10 @@ int ep_combine(const void *y, int32_t hidden, int64_t num_y_rows, const float *t
     return to_status(ep::launch_combine(c, (hipStream_t)stream));
 }
 
-int ep_dispatch_partitioned(const void *x, int x_dtype, const float *x_scales, int recv_dtype,
+int ep_dispatch_partitioned(const void *x, int x_dtype, const void *x_scales, int recv_dtype,
                             int32_t hidden, int32_t scale_group, const int64_t *topk_idx,
                             const float *topk_weights, const ep_layout_params *p,
-                            const ep_layout *layout, void *recv_x, float *recv_scales,
+                            const ep_layout *layout, void *recv_x, void *recv_scales,
                             int64_t *recv_topk_idx, float *recv_topk_weights,
                             int64_t num_recv_rows, void *stream) {
     int rc = check_params(p);
@@ -179,25 +198,14 @@ int ep_dispatch_partitioned(const void *x, int x_dtype, const float *x_scales, i
     if (p->num_tokens > 0 && !layout->token_slot) return EP_ERR_INVALID_ARG;
     if (p->num_tokens > 0 && (recv_topk_idx || recv_topk_weights) && !topk_idx)
         return EP_ERR_INVALID_ARG;
-    if (num_recv_rows < 0 || hidden < 1) return EP_ERR_INVALID_ARG;
-    int mode;
-    if (x_dtype == EP_DTYPE_BF16 && recv_dtype == EP_DTYPE_BF16) mode = 0;
-    else if (x_dtype == EP_DTYPE_FP8_E4M3 && recv_dtype == EP_DTYPE_FP8_E4M3) mode = 1;
-    else if (x_dtype == EP_DTYPE_BF16 && recv_dtype == EP_DTYPE_FP8_E4M3) mode = 2;
-    else return EP_ERR_INVALID_ARG;
-    if (mode == 0 && hidden % 8 != 0) return EP_ERR_INVALID_ARG;
-    if (mode != 0) {
-        if (hidden % 16 != 0) return EP_ERR_INVALID_ARG;
-        if (!valid_group(hidden, scale_group)) return EP_ERR_UNSUPPORTED;
-        if (mode == 2 && scale_group == hidden && hidden > 16 * 64 * 8) return EP_ERR_UNSUPPORTED;
-        if (!recv_scales && num_recv_rows > 0) return EP_ERR_INVALID_ARG;
-        if (mode == 1 && !x_scales && p->num_tokens > 0) return EP_ERR_INVALID_ARG;
-    }
-    if (p->num_tokens > 0 && (!x || !aligned16(x))) return EP_ERR_INVALID_ARG;
-    if (num_recv_rows > 0 && (!recv_x || !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
+    int mode = 0, fmt = 0;
+    rc = dispatch_io(x_dtype, x, x_scales, recv_dtype, hidden, scale_group, p->num_tokens, recv_x,
+                     recv_scales, num_recv_rows, &mode, &fmt);
+    if (rc != EP_OK) return rc;
     ep::DispatchArgs a = {};
     a.x = x;
     a.x_scales = x_scales;
+    a.scale_fmt = fmt;
     a.topk_weights = topk_weights;
     a.status = layout->status;
     a.recv = recv_x;
@@ -281,15 +289,16 @@ int ep_combine_reduced(const void *y, int32_t hidden, int64_t num_y_rows, const 
     return to_status(ep::launch_combine(c, (hipStream_t)stream));
 }
 
-int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group, uint8_t *x_fp8,
-                float *scales, void *stream) {
+int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group, int out_dtype,
+                uint8_t *x_fp8, void *scales, void *stream) {
     if (num_tokens < 0 || hidden < 16 || hidden % 16 != 0) return EP_ERR_INVALID_ARG;
+    if (!is_fp8(out_dtype)) return EP_ERR_INVALID_ARG;
     if (!valid_group(hidden, group)) return EP_ERR_UNSUPPORTED;
     if (group == hidden && hidden > 16 * 64 * 8) return EP_ERR_UNSUPPORTED;
     if (num_tokens == 0) return EP_OK;
     if (!x || !x_fp8 || !scales || !aligned16(x) || !aligned16(x_fp8)) return EP_ERR_INVALID_ARG;
-    return to_status(ep::launch_cast_fp8(x, num_tokens, hidden, group, x_fp8, scales,
-                                         (hipStream_t)stream));
+    return to_status(ep::launch_cast_fp8(x, num_tokens, hidden, group, scale_fmt_of(out_dtype),
+                                         x_fp8, scales, (hipStream_t)stream));
 }
 
 const char *ep_status_string(int code) {

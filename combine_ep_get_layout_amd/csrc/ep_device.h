@@ -103,6 +103,17 @@ __device__ __forceinline__ float group_max(float v, int width) {
     return v;
 }
 
+// Smallest power of two >= s, for positive normal s: a value with mantissa
+// bits set moves to the next exponent with a clear mantissa.
+__device__ __forceinline__ float pow2_ceil(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (u & 0x7FFFFFu) u = (u & 0x7F800000u) + 0x00800000u;
+    return __uint_as_float(u);
+}
+
+// UE8M0 encoding of a power of two: its biased 8-bit exponent.
+__device__ __forceinline__ uint32_t ue8m0_of(float p) { return (__float_as_uint(p) >> 23) & 0xFFu; }
+
 __device__ __forceinline__ float scale_of(float amax) {
     const float ap = amax > 1e-4f ? amax : 1e-4f;
     return ap / 448.0f;

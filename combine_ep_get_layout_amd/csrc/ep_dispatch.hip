@@ -27,9 +27,6 @@
 #ifndef EP_CAST_VPL
 #define EP_CAST_VPL 4
 #endif
-#ifndef EP_DISPATCH_ORDER
-#define EP_DISPATCH_ORDER 0   // 0: per token row, 1: per (token, k) pair, 2: per receive slot
-#endif
 #ifndef EP_DISPATCH_TPW
 #define EP_DISPATCH_TPW 2        // tokens per wave in the copy modes (2: measured best)
 #endif
@@ -45,16 +42,14 @@ enum { kModeCopy16 = 0, kModeCopyFp8 = 1, kModeCast = 2 };
 
 struct DispatchK {
     const uint8_t *x;
-    const float *x_scales;
+    const uint8_t *x_scales;  // [T, ng] scales of fp8 x: fp32, or UE8M0 bytes
     const float *w;
     const int32_t *dst;       // NULL: identity (cast only), slot = t, K = 1
-    const int32_t *src_of_slot;
-    int64_t src_rows;
     const int32_t *counts;
     const int32_t *offsets;
     int32_t *status;
     uint8_t *recv;
-    float *recv_scales;
+    uint8_t *recv_scales;     // [rows, ng] scales of fp8 rows: fp32, or UE8M0 bytes
     float *recv_w;
     int64_t recv_rows;
     int T, K, E, C;
@@ -67,6 +62,7 @@ struct DispatchK {
     int in_row_bytes;
     int out_row_bytes;
     int ng;                   // scales per row (fp8 modes)
+    int scale_fmt;            // 0: fp32 amax/448; 1: fp32 power of two; 2: UE8M0 byte
     int group_lanes;          // cast: lanes per scale group; 0 = one scale per row
     int wpr;                  // waves per row
     int n_tok_blocks;
@@ -82,6 +78,34 @@ template <typename T>
 __device__ __forceinline__ void row_store(T *p, T v) {
     if (EP_DISPATCH_NT_STORE) __builtin_nontemporal_store(v, p);
     else *p = v;
+}
+
+// Scale element size and stores (fp32, or one UE8M0 byte per group).
+__device__ __forceinline__ int scale_bytes(const DispatchK &a) { return a.scale_fmt == 2 ? 1 : 4; }
+
+__device__ __forceinline__ void store_scale(const DispatchK &a, int64_t slot, int j, float s) {
+    if (a.scale_fmt == 2) a.recv_scales[slot * a.ng + j] = (uint8_t)ue8m0_of(s);
+    else ((float *)a.recv_scales)[slot * a.ng + j] = s;
+}
+
+// fp8 copy: the token's scale row to the receive row, by lanes.
+__device__ __forceinline__ void copy_scales(const DispatchK &a, int t, int64_t slot, int lane) {
+    if (a.scale_fmt == 2) {
+        const uint8_t *ss = a.x_scales + (int64_t)t * a.ng;
+        uint8_t *sd = a.recv_scales + slot * a.ng;
+        for (int j = lane; j < a.ng; j += 64) sd[j] = ss[j];
+    } else {
+        const float *ss = (const float *)a.x_scales + (int64_t)t * a.ng;
+        float *sd = (float *)a.recv_scales + slot * a.ng;
+        for (int j = lane; j < a.ng; j += 64) sd[j] = ss[j];
+    }
+}
+
+// Scale of one group from its amax, in the call's format (fp32 values; the
+// UE8M0 byte is taken from the power of two when stored).
+__device__ __forceinline__ float group_scale(const DispatchK &a, float amax) {
+    const float s = scale_of(amax);
+    return a.scale_fmt == 0 ? s : pow2_ceil(s);
 }
 
 // Per-destination bookkeeping of one lane: the expanded layout records the
@@ -126,7 +150,8 @@ __device__ __forceinline__ void pad_rows(const DispatchK &a, int pb) {
         ep_u32x4 *row = (ep_u32x4 *)(a.recv + r * (int64_t)a.out_row_bytes);
         for (int v = threadIdx.x; v < nv_out; v += kBlock) row_store(row + v, z);
         if (a.recv_scales)
-            for (int j = threadIdx.x; j < a.ng; j += kBlock) a.recv_scales[r * a.ng + j] = 0.0f;
+            for (int j = threadIdx.x; j < a.ng * scale_bytes(a); j += kBlock)
+                a.recv_scales[r * a.ng * scale_bytes(a) + j] = 0;
         if (a.recv_w && threadIdx.x == 0) a.recv_w[r] = 0.0f;
     }
 }
@@ -175,12 +200,12 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
             float s[VPL];
             if (a.group_lanes > 0) {
 #pragma unroll
-                for (int i = 0; i < VPL; ++i) s[i] = scale_of(group_max(amax8(v[i]), a.group_lanes));
+                for (int i = 0; i < VPL; ++i) s[i] = group_scale(a, group_max(amax8(v[i]), a.group_lanes));
             } else {
                 float m = 0.0f;
 #pragma unroll
                 for (int i = 0; i < VPL; ++i) m = fmaxf(m, amax8(v[i]));
-                const float sr = scale_of(group_max(m, 64));
+                const float sr = group_scale(a, group_max(m, 64));
 #pragma unroll
                 for (int i = 0; i < VPL; ++i) s[i] = sr;
             }
@@ -196,15 +221,15 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
                     const int vi = v0 + i * 64 + lane;
                     if (vi < a.nvec) row_store(dstrow + vi, q[i]);
                 }
-                float *srow = a.recv_scales + (int64_t)slot * a.ng;
                 if (a.group_lanes > 0) {
 #pragma unroll
                     for (int i = 0; i < VPL; ++i) {
                         const int vi = v0 + i * 64 + lane;
-                        if (vi < a.nvec && (vi % a.group_lanes) == 0) srow[vi / a.group_lanes] = s[i];
+                        if (vi < a.nvec && (vi % a.group_lanes) == 0)
+                            store_scale(a, slot, vi / a.group_lanes, s[i]);
                     }
                 } else if (lane == 0) {
-                    srow[0] = s[0];
+                    store_scale(a, slot, 0, s[0]);
                 }
             }
         } else {
@@ -217,11 +242,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
                     const int vi = v0 + i * 64 + lane;
                     if (vi < a.nvec) row_store(dstrow + vi, v[i]);
                 }
-                if (MODE == kModeCopyFp8 && ci == 0) {
-                    const float *ss = a.x_scales + (int64_t)t * a.ng;
-                    float *sd = a.recv_scales + (int64_t)slot * a.ng;
-                    for (int j = lane; j < a.ng; j += 64) sd[j] = ss[j];
-                }
+                if (MODE == kModeCopyFp8 && ci == 0) copy_scales(a, t, slot, lane);
             }
         }
     }
@@ -286,121 +307,19 @@ __global__ void __launch_bounds__(kBlock) dispatch_multi_kernel(DispatchK a) {
                     const int vi = v0 + i * 64 + lane;
                     if (vi < a.nvec) row_store(dstrow + vi, v[j & 1][i]);
                 }
-                if (MODE == kModeCopyFp8 && ci == 0) {
-                    const float *ss = a.x_scales + (int64_t)t * a.ng;
-                    float *sd = a.recv_scales + (int64_t)slot * a.ng;
-                    for (int jj = lane; jj < a.ng; jj += 64) sd[jj] = ss[jj];
-                }
+                if (MODE == kModeCopyFp8 && ci == 0) copy_scales(a, t, slot, lane);
             }
         }
     }
 }
 
-// Copy modes, one wave per (pair, chunk): the wave reads its chunk of the
-// token row (the K waves of one token hit L2/MALL after the first) and writes
-// one destination.  More, shorter waves keep more stores in flight.
-template <int VPL, int MODE>
-__global__ void __launch_bounds__(kBlock) dispatch_pair_kernel(DispatchK a) {
-    if ((int)blockIdx.x >= a.n_tok_blocks) {
-        pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
-        return;
-    }
-    const int lane = __lane_id();
-    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
-    const int64_t pair = gw / a.wpr;
-    const int ci = (int)(gw - pair * a.wpr);
-    if (pair >= (int64_t)a.T * a.K) return;
-    const int t = (int)(pair / a.K);
-    int slot = a.dst[pair];
-    if ((int64_t)slot >= a.recv_rows) {
-        if (lane == 0 && ci == 0) atomicOr(a.status, kDevRecvOverflow);
-        slot = -1;
-    }
-    slot = wave_uniform(slot);
-    if (ci == 0 && a.recv_w && slot >= 0 && lane == 0) a.recv_w[slot] = a.w ? a.w[pair] : 1.0f;
-    if (slot < 0) return;
-    const int v0 = ci * VPL * 64;
-    ep_u32x4 v[VPL];
-    const ep_u32x4 *src = (const ep_u32x4 *)(a.x + (int64_t)t * a.in_row_bytes);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int vi = v0 + i * 64 + lane;
-        if (vi < a.nvec) v[i] = src[vi];
-    }
-    ep_u32x4 *dstrow = (ep_u32x4 *)(a.recv + (int64_t)slot * a.out_row_bytes);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int vi = v0 + i * 64 + lane;
-        if (vi < a.nvec) row_store(dstrow + vi, v[i]);
-    }
-    if (MODE == kModeCopyFp8 && ci == 0) {
-        const float *ss = a.x_scales + (int64_t)t * a.ng;
-        float *sd = a.recv_scales + (int64_t)slot * a.ng;
-        for (int j = lane; j < a.ng; j += 64) sd[j] = ss[j];
-    }
-}
-
-// Copy modes, one wave per (receive slot, chunk), in slot order: the stores
-// of neighbouring waves land on neighbouring rows, and each token row is
-// re-read K times from L2 / the memory-side cache instead of HBM.  Padding
-// slots are zeroed (and their weights cleared) inline.
-template <int VPL, int MODE>
-__global__ void __launch_bounds__(kBlock) dispatch_slot_kernel(DispatchK a) {
-    const int lane = __lane_id();
-    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
-    const int64_t slot = gw / a.wpr;
-    const int ci = (int)(gw - slot * a.wpr);
-    const int64_t R = a.offsets[a.E];
-    if (slot == 0 && ci == 0 && lane == 0 && R > a.recv_rows) atomicOr(a.status, kDevRecvOverflow);
-    if (slot >= R || slot >= a.recv_rows || slot >= a.src_rows) return;
-    const int src = wave_uniform(a.src_of_slot[slot]);
-    const int v0 = ci * VPL * 64;
-    ep_u32x4 *dstrow = (ep_u32x4 *)(a.recv + slot * a.out_row_bytes);
-    if (src < 0) {
-        if (ci == 0 && lane == 0 && a.recv_w) a.recv_w[slot] = 0.0f;
-        if (!a.zero_padding) return;
-        const ep_u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int vi = v0 + i * 64 + lane;
-            if (vi < a.nvec) row_store(dstrow + vi, z);
-        }
-        if (MODE == kModeCopyFp8 && ci == 0)
-            for (int j = lane; j < a.ng; j += 64) a.recv_scales[slot * a.ng + j] = 0.0f;
-        return;
-    }
-    const int t = src / a.K;
-    if (ci == 0 && lane == 0 && a.recv_w) a.recv_w[slot] = a.w ? a.w[src] : 1.0f;
-    ep_u32x4 v[VPL];
-    const ep_u32x4 *srow = (const ep_u32x4 *)(a.x + (int64_t)t * a.in_row_bytes);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int vi = v0 + i * 64 + lane;
-        if (vi < a.nvec) v[i] = srow[vi];
-    }
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int vi = v0 + i * 64 + lane;
-        if (vi < a.nvec) row_store(dstrow + vi, v[i]);
-    }
-    if (MODE == kModeCopyFp8 && ci == 0) {
-        const float *ss = a.x_scales + (int64_t)t * a.ng;
-        float *sd = a.recv_scales + slot * a.ng;
-        for (int j = lane; j < a.ng; j += 64) sd[j] = ss[j];
-    }
-}
-
 template <int MODE>
-hipError_t launch_mode(const DispatchK &k, int vpl, int grid, int order, hipStream_t stream) {
+hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStream_t stream) {
 #define EP_CASE(V)                                                                              \
     case V:                                                                                     \
-        if (order == 3)                                                                         \
+        if (multi)                                                                              \
             hipLaunchKernelGGL((dispatch_multi_kernel<V, MODE, (MODE == kModeCast ? 1 : EP_DISPATCH_TPW)>), \
                                dim3(grid), dim3(kBlock), 0, stream, k);                        \
-        else if (order == 1)                                                                    \
-            hipLaunchKernelGGL((dispatch_pair_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
-        else if (order == 2)                                                                    \
-            hipLaunchKernelGGL((dispatch_slot_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
         else                                                                                    \
             hipLaunchKernelGGL((dispatch_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
         break;
@@ -434,22 +353,18 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     }
     k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
     if (k.wpr < 1) k.wpr = 1;
-    int order = (mode != kModeCast && k.dst != nullptr && k.m == 0) ? EP_DISPATCH_ORDER : 0;
-    if (order == 0 && mode != kModeCast && k.dst != nullptr && EP_DISPATCH_TPW > 1) order = 3;
-    int64_t waves = (int64_t)k.T * (order == 1 ? k.K : 1) * k.wpr;
-    if (order == 3) waves = (((int64_t)k.T + EP_DISPATCH_TPW - 1) / EP_DISPATCH_TPW) * k.wpr;
-    if (order == 2) {
-        waves = (k.recv_rows < k.src_rows ? k.recv_rows : k.src_rows) * k.wpr;
-        k.pad_slices = 0;
-    }
+    // copy modes with a layout: TPW tokens per wave
+    const bool multi = mode != kModeCast && k.dst != nullptr && EP_DISPATCH_TPW > 1;
+    int64_t waves = (int64_t)k.T * k.wpr;
+    if (multi) waves = (((int64_t)k.T + EP_DISPATCH_TPW - 1) / EP_DISPATCH_TPW) * k.wpr;
     k.n_tok_blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
     const int64_t grid = (int64_t)k.n_tok_blocks + (int64_t)k.E * k.pad_slices;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     switch (mode) {
-        case kModeCopy16: return launch_mode<kModeCopy16>(k, vpl, (int)grid, order, stream);
-        case kModeCopyFp8: return launch_mode<kModeCopyFp8>(k, vpl, (int)grid, order, stream);
-        default: return launch_mode<kModeCast>(k, vpl, (int)grid, 0, stream);
+        case kModeCopy16: return launch_mode<kModeCopy16>(k, vpl, (int)grid, multi, stream);
+        case kModeCopyFp8: return launch_mode<kModeCopyFp8>(k, vpl, (int)grid, multi, stream);
+        default: return launch_mode<kModeCast>(k, vpl, (int)grid, false, stream);
     }
 }
 
@@ -458,16 +373,15 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     DispatchK k = {};
     k.x = (const uint8_t *)a.x;
-    k.x_scales = a.x_scales;
+    k.x_scales = (const uint8_t *)a.x_scales;
     k.w = a.topk_weights;
     k.dst = a.dst;
-    k.src_of_slot = a.src_of_slot;
-    k.src_rows = a.src_rows;
     k.counts = a.counts;
     k.offsets = a.offsets;
     k.status = a.status;
     k.recv = (uint8_t *)a.recv;
-    k.recv_scales = a.recv_scales;
+    k.recv_scales = (uint8_t *)a.recv_scales;
+    k.scale_fmt = a.scale_fmt;
     k.recv_w = a.recv_w;
     k.recv_rows = a.recv_rows;
     k.T = a.T;
@@ -501,14 +415,15 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     return run(k, a.mode, EP_DISPATCH_VPL, stream);
 }
 
-hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, uint8_t *q, float *scales,
-                           hipStream_t stream) {
+hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, int scale_fmt, uint8_t *q,
+                           void *scales, hipStream_t stream) {
     DispatchK k = {};
     k.x = (const uint8_t *)x;
     k.dst = nullptr;
     k.status = nullptr;
     k.recv = q;
-    k.recv_scales = scales;
+    k.recv_scales = (uint8_t *)scales;
+    k.scale_fmt = scale_fmt;
     k.recv_rows = T;
     k.T = T;
     k.K = 1;

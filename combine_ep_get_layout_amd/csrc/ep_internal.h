@@ -32,22 +32,21 @@ hipError_t launch_layout(const LayoutPlan &plan, const int64_t *topk_idx, const 
 
 struct DispatchArgs {
     const void *x;
-    const float *x_scales;
+    const void *x_scales;          // fp32 or UE8M0 bytes [T, hidden/group]
     const float *topk_weights;
     const int32_t *dst;            // [T*K]
-    const int32_t *src_of_slot;    // [src_rows]
-    int64_t src_rows;              // the layout's max_recv_rows
     const int32_t *counts;         // [E]
     const int32_t *offsets;        // [E+1]
     int32_t *status;
     void *recv;
-    float *recv_scales;
+    void *recv_scales;
     float *recv_w;
     int64_t recv_rows;
     int T, K, E, A, C;
     int hidden;
     int group;                     // fp8 scale group (0 when bf16 -> bf16)
     int mode;                      // 0 copy bf16, 1 copy fp8 (+scales), 2 cast bf16 -> fp8
+    int scale_fmt;                 // 0 fp32 amax/448, 1 fp32 power of two, 2 UE8M0 byte
     int zero_padding;
     // partitioned (non-expanded) dispatch
     int partitioned;
@@ -79,7 +78,8 @@ struct CombineArgs {
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 
-hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, uint8_t *q, float *scales,
+hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, int scale_fmt, uint8_t *q,
+                           void *scales,
                            hipStream_t stream);
 
 }  // namespace ep

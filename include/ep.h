@@ -52,7 +52,16 @@ enum {
     EP_DEV_RECV_OVERFLOW = 4   /* a slot >= the rows the caller allocated       */
 };
 
-enum { EP_DTYPE_BF16 = 0, EP_DTYPE_FP8_E4M3 = 1 };
+/* Row types.  The fp8 types carry one scale per (row, group of G channels):
+ *   EP_DTYPE_FP8_E4M3        fp32 scale s = max(amax, 1e-4f) / 448 ([API] 4.2)
+ *   EP_DTYPE_FP8_E4M3_POW2   fp32 scale rounded up to a power of two
+ *                            ([API] 3.3 round_scale)
+ *   EP_DTYPE_FP8_E4M3_UE8M0  the same power of two stored as one UE8M0 byte,
+ *                            its biased exponent b, value 2^(b-127)
+ *                            ([API] 3.3 use_ue8m0)
+ * Codes are e4m3_rne(x / s) in every case (exact division for powers of two). */
+enum { EP_DTYPE_BF16 = 0, EP_DTYPE_FP8_E4M3 = 1, EP_DTYPE_FP8_E4M3_POW2 = 2,
+       EP_DTYPE_FP8_E4M3_UE8M0 = 3 };
 
 /* Limits of this build. */
 enum { EP_MAX_EXPERTS = 4096, EP_MAX_PARTITIONS = 1024, EP_MAX_TOPK = 256,
@@ -141,14 +150,16 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,
 
 /* ep_dispatch - permute token rows into the receive buffer.
  * ([API] 2.1: x is bf16 [T, hidden] or the pair (fp8 codes, scales); recv_x
- *  has the input's type; do_zero_padding; 4.2 per-token cast to e4m3.)
+ *  has the input's type; do_zero_padding; 4.2 per-token cast to e4m3;
+ *  3.3 round_scale / use_ue8m0 scale formats.)
  *
  *   x            device [T, hidden]: bf16 (x_dtype EP_DTYPE_BF16) or e4m3 codes
- *                (EP_DTYPE_FP8_E4M3); 16-byte aligned.
- *   x_scales     device float [T, hidden/scale_group] when x is fp8, else NULL.
- *   recv_dtype   == x_dtype, or EP_DTYPE_FP8_E4M3 with bf16 x: the rows are
- *                cast on the fly, exactly as ep_cast_fp8 followed by an fp8
- *                dispatch would do.
+ *                (one of the EP_DTYPE_FP8_* types); 16-byte aligned.
+ *   x_scales     device [T, hidden/scale_group] when x is fp8, else NULL:
+ *                float, or uint8 for EP_DTYPE_FP8_E4M3_UE8M0.
+ *   recv_dtype   == x_dtype, or an fp8 type with bf16 x: the rows are cast
+ *                on the fly, exactly as ep_cast_fp8 to that type followed by
+ *                an fp8 dispatch would do.
  *   hidden       channels per row; multiple of 8 (bf16) or 16 (fp8 rows).
  *   scale_group  G, channels per fp32 scale when fp8 is involved: a power of
  *                two in [16, 512] dividing hidden, or hidden itself (one scale
@@ -156,7 +167,8 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,
  *   topk_weights device float [T, K] or NULL.
  *   params, layout  as produced by ep_get_layout for the same routing.
  *   recv_x       device [num_recv_rows, hidden] of recv_dtype; 16-byte aligned.
- *   recv_scales  device float [num_recv_rows, hidden/G] when recv is fp8.
+ *   recv_scales  device [num_recv_rows, hidden/G] when recv is fp8: float,
+ *                or uint8 for EP_DTYPE_FP8_E4M3_UE8M0.
  *   recv_topk_weights device float [num_recv_rows] or NULL: weight of the pair
  *                in each row (1 when topk_weights is NULL), 0 for padding rows.
  *   num_recv_rows rows allocated for recv_x / recv_scales / recv_topk_weights;
@@ -166,10 +178,10 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,
  * recv_x[dst_slot[t,k]] = x[t] byte for byte (fp8: codes and scale row).
  * Errors: EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED (a scale_group outside the
  * set above). */
-int ep_dispatch(const void *x, int x_dtype, const float *x_scales, int recv_dtype,
+int ep_dispatch(const void *x, int x_dtype, const void *x_scales, int recv_dtype,
                 int32_t hidden, int32_t scale_group, const float *topk_weights,
                 const ep_layout_params *params, const ep_layout *layout,
-                void *recv_x, float *recv_scales, float *recv_topk_weights,
+                void *recv_x, void *recv_scales, float *recv_topk_weights,
                 int64_t num_recv_rows, int zero_padding, void *stream);
 
 /* ep_combine - gather expert outputs back to their tokens and reduce.
@@ -211,10 +223,10 @@ int ep_combine(const void *y, int32_t hidden, int64_t num_y_rows,
  * Receive rows are [partition_offset[q], partition_offset[q+1]) for partition
  * q, tokens ascending; there is no padding.  Errors as ep_dispatch;
  * EP_ERR_UNSUPPORTED when P > EP_MAX_SLOT_PARTITIONS. */
-int ep_dispatch_partitioned(const void *x, int x_dtype, const float *x_scales, int recv_dtype,
+int ep_dispatch_partitioned(const void *x, int x_dtype, const void *x_scales, int recv_dtype,
                             int32_t hidden, int32_t scale_group, const int64_t *topk_idx,
                             const float *topk_weights, const ep_layout_params *params,
-                            const ep_layout *layout, void *recv_x, float *recv_scales,
+                            const ep_layout *layout, void *recv_x, void *recv_scales,
                             int64_t *recv_topk_idx, float *recv_topk_weights,
                             int64_t num_recv_rows, void *stream);
 
@@ -241,17 +253,21 @@ int ep_combine_reduced(const void *y, int32_t hidden, int64_t num_y_rows, const 
 
 /* ep_cast_fp8 - per (token, group) cast of bf16 rows to OCP e4m3
  * ([API] 4.2 per_token_cast_to_fp8, with one scale per group of G channels;
- *  G = hidden is the page's one-scale-per-token form).
+ *  G = hidden is the page's one-scale-per-token form; 3.3 round_scale and
+ *  use_ue8m0 through out_dtype).
  *
- *   x       device bf16 [T, hidden], 16-byte aligned, hidden % 16 == 0.
- *   group   G: a power of two in [16, 512] dividing hidden, or hidden.
- *   x_fp8   device uint8 [T, hidden], 16-byte aligned (e4m3fn codes).
- *   scales  device float [T, hidden/G].
- * amax = max |x| over the group; s = max(amax, 1e-4f) / 448 (fp32, nearest);
- * code = e4m3_rne(x / s) (fp32 nearest division, ties to even, sign kept on
- * underflow).  Decode: x ~= float(code) * s. */
+ *   x         device bf16 [T, hidden], 16-byte aligned, hidden % 16 == 0.
+ *   group     G: a power of two in [16, 512] dividing hidden, or hidden.
+ *   out_dtype EP_DTYPE_FP8_E4M3, EP_DTYPE_FP8_E4M3_POW2 or
+ *             EP_DTYPE_FP8_E4M3_UE8M0 (else EP_ERR_INVALID_ARG).
+ *   x_fp8     device uint8 [T, hidden], 16-byte aligned (e4m3fn codes).
+ *   scales    device [T, hidden/G]: float, or uint8 for UE8M0.
+ * amax = max |x| over the group; s = max(amax, 1e-4f) / 448 (fp32, nearest),
+ * rounded up to a power of two for POW2 / UE8M0; code = e4m3_rne(x / s)
+ * (fp32 nearest division, ties to even, sign kept on underflow).
+ * Decode: x ~= float(code) * s. */
 int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group,
-                uint8_t *x_fp8, float *scales, void *stream);
+                int out_dtype, uint8_t *x_fp8, void *scales, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *ep_status_string(int code);

@@ -101,6 +101,11 @@ def test_dispatch_rejects_bad_arguments():
     assert call(rd=f8, H=192, G=96, rs=16) == _abi.EP_ERR_UNSUPPORTED  # group not a power of 2
     assert call(rd=f8, H=128, G=1024, rs=16) == _abi.EP_ERR_UNSUPPORTED
     assert call(xd=f8, rd=f8, H=128, rs=16) == _abi.EP_ERR_INVALID_ARG  # fp8 x without scales
+    ue, p2 = _abi.EP_DTYPE_FP8_E4M3_UE8M0, _abi.EP_DTYPE_FP8_E4M3_POW2
+    assert call(xd=ue, rd=f8, H=128, rs=16) == _abi.EP_ERR_INVALID_ARG  # copy changes scale format
+    assert call(xd=p2, rd=ue, H=128, rs=16) == _abi.EP_ERR_INVALID_ARG
+    assert call(xd=f8, rd=bf) == _abi.EP_ERR_INVALID_ARG
+    assert call(rd=7, H=128, rs=16) == _abi.EP_ERR_INVALID_ARG           # unknown dtype
     assert call(rows=-1) == _abi.EP_ERR_INVALID_ARG
 
 
@@ -116,11 +121,14 @@ def test_combine_and_cast_reject_bad_arguments():
     assert lib.ep_combine(ctypes.c_void_p(16), 64, 8, None, None, None, ctypes.byref(p),
                           ctypes.byref(lay), None, ctypes.c_void_p(16), ctypes.c_void_p(16),
                           None) == _abi.EP_ERR_INVALID_ARG       # combined weights need recv weights
-    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 4, 100, 128, ctypes.c_void_p(16),
+    f8 = _abi.EP_DTYPE_FP8_E4M3
+    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 4, 100, 128, f8, ctypes.c_void_p(16),
                            ctypes.c_void_p(16), None) == _abi.EP_ERR_INVALID_ARG
-    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 4, 384, 96, ctypes.c_void_p(16),
+    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 4, 384, 96, f8, ctypes.c_void_p(16),
                            ctypes.c_void_p(16), None) == _abi.EP_ERR_UNSUPPORTED
-    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 0, 128, 128, None, None, None) == _abi.EP_OK
+    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 4, 128, 128, _abi.EP_DTYPE_BF16,
+                           ctypes.c_void_p(16), ctypes.c_void_p(16), None) == _abi.EP_ERR_INVALID_ARG
+    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 0, 128, 128, f8, None, None, None) == _abi.EP_OK
 
 
 def test_partition_layout_limits():
