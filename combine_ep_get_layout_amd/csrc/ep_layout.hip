@@ -40,7 +40,10 @@ namespace {
 
 constexpr int kCountBlock = 256;   // count workgroup of the two-kernel tiling: 4 waves
 constexpr int kSlotsBlock = 1024;  // slots workgroup, and the fused tiling: 16 waves
-constexpr int kReduceBatch = 8;    // loads in flight per thread in column_sums
+#ifndef EP_LAYOUT_RBATCH
+#define EP_LAYOUT_RBATCH 8
+#endif
+constexpr int kReduceBatch = EP_LAYOUT_RBATCH;   // loads in flight per thread in column_sums
 constexpr int kMaxFusedExperts = 512;
 #ifndef EP_LAYOUT_FUSED
 #define EP_LAYOUT_FUSED 0      // cooperative single launch (measured slower to launch)
