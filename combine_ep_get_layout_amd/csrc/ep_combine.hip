@@ -26,9 +26,6 @@
 #ifndef EP_COMBINE_U
 #define EP_COMBINE_U 8      // rows in flight per wave (0: by VPL)
 #endif
-#ifndef EP_COMBINE_PERSIST
-#define EP_COMBINE_PERSIST 0   // >0: persistent grid of this many waves per CU
-#endif
 
 namespace ep {
 
@@ -78,11 +75,15 @@ __device__ __forceinline__ void fma_bf16x8(float *acc, float w, ep_u32x4 v) {
     acc[7] = __builtin_fmaf(w, bf16_hi(v.w), acc[7]);
 }
 
-// One output row chunk (token t, chunk ci) of the plain combine.
 template <int VPL>
-__device__ __forceinline__ void combine_unit(const CombineK &a, int t, int ci, int lane) {
+__global__ void __launch_bounds__(kBlock) combine_kernel(CombineK a) {
     constexpr int U = EP_COMBINE_U > 0 ? EP_COMBINE_U
                                        : (VPL >= 16 ? 1 : (VPL >= 8 ? 2 : (VPL >= 4 ? 4 : 8)));
+    const int lane = __lane_id();
+    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int t = gw / a.wpr;
+    const int ci = gw - t * a.wpr;
+    if (t >= a.T) return;
     const int v0 = ci * VPL * 64;
 
     float acc[VPL][8];
@@ -153,20 +154,6 @@ __device__ __forceinline__ void combine_unit(const CombineK &a, int t, int ci, i
         o.z = bf16_rne(acc[i][4]) | (bf16_rne(acc[i][5]) << 16);
         o.w = bf16_rne(acc[i][6]) | (bf16_rne(acc[i][7]) << 16);
         store_nt(dst + vi, o);
-    }
-}
-
-// One wave per chunk; with EP_COMBINE_PERSIST the grid holds only resident
-// waves and each takes every (waves)-th chunk, so no wave is relaunched.
-template <int VPL>
-__global__ void __launch_bounds__(kBlock) combine_kernel(CombineK a) {
-    const int lane = __lane_id();
-    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
-    const int units = a.T * a.wpr;
-    const int stride = EP_COMBINE_PERSIST ? (int)gridDim.x * kWavesPerBlock : units;
-    for (int u = gw; u < units; u += stride) {
-        const int t = u / a.wpr;
-        combine_unit<VPL>(a, t, u - t * a.wpr, lane);
     }
 }
 
@@ -328,20 +315,9 @@ hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
     k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
     if (k.wpr < 1) k.wpr = 1;
     const int64_t waves = (int64_t)k.T * k.wpr;
-    int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (EP_COMBINE_PERSIST > 0 && !k.idx) {
-        static int cus = 0;
-        if (cus == 0) {
-            int dev = 0;
-            if (hipGetDevice(&dev) != hipSuccess ||
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-                cus = 256;
-        }
-        const int64_t cap = (int64_t)cus * EP_COMBINE_PERSIST / kWavesPerBlock;
-        if (grid > cap) grid = cap;
-    }
 #define EP_CASE(V)                                                                              \
     case V:                                                                                     \
         if (k.idx)                                                                              \
