@@ -85,20 +85,85 @@ __device__ __forceinline__ float amax8(ep_u32x4 v) {
     return m;
 }
 
+#ifndef EP_CAST_DIV
+#define EP_CAST_DIV 1   // 1: reciprocal + two residual corrections; 0: plain '/' per element
+#endif
+
+// x / s rounded to nearest even, given y = RN(1/s) (one correctly rounded
+// division per scale group).  Markstein's refinement (P. Markstein, IBM J.
+// Res. Dev. 34(1), 1990): with y = RN(1/s) and q within one ulp of x/s, the
+// residual r = x - s*q is exact in one FMA and RN(q + r*y) = RN(x/s).  q =
+// x*y can be just over one ulp off, so one correction makes it faithful and
+// a second gives the rounded quotient.  Exactness needs the residual to be a
+// normal fp32 number: with s >= 1e-4/448 that holds for every |x/s| >= 2^-12,
+// and every smaller quotient has e4m3 code +-0 whatever its low bits.  The
+// sign is x's (s > 0), which also keeps -0.
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+#if EP_CAST_DIV
+    float q = x * y;
+    float r = __builtin_fmaf(-q, s, x);
+    q = __builtin_fmaf(r, y, q);
+    r = __builtin_fmaf(-q, s, x);
+    q = __builtin_fmaf(r, y, q);
+    return __builtin_copysignf(q, x);
+#else
+    (void)y;
+    return x / s;
+#endif
+}
+
+#ifndef EP_CAST_HWCVT
+#define EP_CAST_HWCVT 1   // 1: gfx950's packed fp32 -> e4m3 conversion; 0: e4m3_rne
+#endif
+
+// Four quotients -> four e4m3 codes, little-endian in one dword.  The
+// hardware conversion rounds to nearest even like e4m3_rne; the quotients
+// here never exceed 448 * (1 + 2^-23), so its overflow handling is not met.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+#if EP_CAST_HWCVT
+    uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+#else
+    return e4m3_rne(a) | (e4m3_rne(b) << 8) | (e4m3_rne(c) << 16) | (e4m3_rne(d) << 24);
+#endif
+}
+
 // 8 bf16 values / s -> 8 e4m3 codes packed little-endian in two dwords.
 __device__ __forceinline__ ep_u32x2 encode8(ep_u32x4 v, float s) {
-    uint32_t c0 = e4m3_rne(bf16_lo(v.x) / s) | (e4m3_rne(bf16_hi(v.x) / s) << 8) |
-                  (e4m3_rne(bf16_lo(v.y) / s) << 16) | (e4m3_rne(bf16_hi(v.y) / s) << 24);
-    uint32_t c1 = e4m3_rne(bf16_lo(v.z) / s) | (e4m3_rne(bf16_hi(v.z) / s) << 8) |
-                  (e4m3_rne(bf16_lo(v.w) / s) << 16) | (e4m3_rne(bf16_hi(v.w) / s) << 24);
+    const float y = 1.0f / s;
     ep_u32x2 r;
-    r.x = c0;
-    r.y = c1;
+    r.x = pack4_e4m3(div_rn(bf16_lo(v.x), s, y), div_rn(bf16_hi(v.x), s, y),
+                     div_rn(bf16_lo(v.y), s, y), div_rn(bf16_hi(v.y), s, y));
+    r.y = pack4_e4m3(div_rn(bf16_lo(v.z), s, y), div_rn(bf16_hi(v.z), s, y),
+                     div_rn(bf16_lo(v.w), s, y), div_rn(bf16_hi(v.w), s, y));
     return r;
 }
 
+#ifndef EP_GROUP_MAX_DPP
+#define EP_GROUP_MAX_DPP 1
+#endif
+
+// v from the lane given by a DPP control code (all lanes active).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 // max over aligned groups of `width` lanes (width a power of two <= 64).
+// Up to 16 lanes (one DPP row) the exchanges are DPP moves at ALU rate:
+// lane ^ 1 and lane ^ 2 by quad permutes, then the mirror inside each half
+// row and inside the row, which pair every lane with one of the other
+// half; wider groups go through ds_bpermute.
 __device__ __forceinline__ float group_max(float v, int width) {
+#if EP_GROUP_MAX_DPP
+    if (width <= 16) {
+        if (width >= 2) v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+        if (width >= 4) v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+        if (width >= 8) v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
+        if (width >= 16) v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+        return v;
+    }
+#endif
     for (int o = 1; o < width; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
 }

@@ -30,6 +30,9 @@
 #ifndef EP_DISPATCH_TPW
 #define EP_DISPATCH_TPW 2        // tokens per wave in the copy modes (2: measured best)
 #endif
+#ifndef EP_CAST_TPW
+#define EP_CAST_TPW 1            // tokens per wave in the cast modes
+#endif
 #ifndef EP_DISPATCH_NT_STORE
 #define EP_DISPATCH_NT_STORE 0   // plain stores measured faster for the receive rows
 #endif
@@ -106,6 +109,47 @@ __device__ __forceinline__ void copy_scales(const DispatchK &a, int t, int64_t s
 __device__ __forceinline__ float group_scale(const DispatchK &a, float amax) {
     const float s = scale_of(amax);
     return a.scale_fmt == 0 ? s : pow2_ceil(s);
+}
+
+// Cast of one wave's chunk: per-group (or, with group_lanes == 0, per-row)
+// scales, then 8 codes per lane per vector.
+template <int VPL>
+__device__ __forceinline__ void cast_chunk(const DispatchK &a, const ep_u32x4 (&v)[VPL],
+                                           float (&s)[VPL], ep_u32x2 (&q)[VPL]) {
+    if (a.group_lanes > 0) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) s[i] = group_scale(a, group_max(amax8(v[i]), a.group_lanes));
+    } else {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) m = fmaxf(m, amax8(v[i]));
+        const float sr = group_scale(a, group_max(m, 64));
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) s[i] = sr;
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) q[i] = encode8(v[i], s[i]);
+}
+
+// Codes and scales of one cast chunk into receive row `slot`.
+template <int VPL>
+__device__ __forceinline__ void store_cast(const DispatchK &a, int64_t slot, int v0, int lane,
+                                           const float (&s)[VPL], const ep_u32x2 (&q)[VPL]) {
+    ep_u32x2 *dstrow = (ep_u32x2 *)(a.recv + slot * a.out_row_bytes);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int vi = v0 + i * 64 + lane;
+        if (vi < a.nvec) row_store(dstrow + vi, q[i]);
+    }
+    if (a.group_lanes > 0) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const int vi = v0 + i * 64 + lane;
+            if (vi < a.nvec && (vi % a.group_lanes) == 0) store_scale(a, slot, vi / a.group_lanes, s[i]);
+        }
+    } else if (lane == 0) {
+        store_scale(a, slot, 0, s[0]);
+    }
 }
 
 // Per-destination bookkeeping of one lane: the expanded layout records the
@@ -196,41 +240,12 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
         const int kn = min(64, K - kb);
 
         if (MODE == kModeCast) {
-            // Per-group scales, then codes; 8 codes (8 bytes) per lane per vector.
             float s[VPL];
-            if (a.group_lanes > 0) {
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) s[i] = group_scale(a, group_max(amax8(v[i]), a.group_lanes));
-            } else {
-                float m = 0.0f;
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) m = fmaxf(m, amax8(v[i]));
-                const float sr = group_scale(a, group_max(m, 64));
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) s[i] = sr;
-            }
             ep_u32x2 q[VPL];
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) q[i] = encode8(v[i], s[i]);
+            cast_chunk<VPL>(a, v, s, q);
             for (int k = 0; k < kn; ++k) {
                 const int slot = lane_read(my_slot, k);
-                if (slot < 0) continue;
-                ep_u32x2 *dstrow = (ep_u32x2 *)(a.recv + (int64_t)slot * a.out_row_bytes);
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    const int vi = v0 + i * 64 + lane;
-                    if (vi < a.nvec) row_store(dstrow + vi, q[i]);
-                }
-                if (a.group_lanes > 0) {
-#pragma unroll
-                    for (int i = 0; i < VPL; ++i) {
-                        const int vi = v0 + i * 64 + lane;
-                        if (vi < a.nvec && (vi % a.group_lanes) == 0)
-                            store_scale(a, slot, vi / a.group_lanes, s[i]);
-                    }
-                } else if (lane == 0) {
-                    store_scale(a, slot, 0, s[0]);
-                }
+                if (slot >= 0) store_cast<VPL>(a, slot, v0, lane, s, q);
             }
         } else {
             for (int k = 0; k < kn; ++k) {
@@ -285,15 +300,18 @@ __global__ void __launch_bounds__(kBlock) dispatch_multi_kernel(DispatchK a) {
                 v[(j + 1) & 1][i] = vi < a.nvec ? load_nt(src + vi) : ep_u32x4{0u, 0u, 0u, 0u};
             }
         }
+        float s[VPL];
+        ep_u32x2 q[VPL];
+        if (MODE == kModeCast) cast_chunk<VPL>(a, v[j & 1], s, q);
         for (int kb = 0; kb < a.nd; kb += 64) {
             int my_slot = -1;
             float my_w = 1.0f;
             if (kb + lane < a.nd) {
-                my_slot = a.dst[(int64_t)t * a.nd + kb + lane];
+                my_slot = a.dst ? a.dst[(int64_t)t * a.nd + kb + lane] : t;
                 if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
             }
             if ((int64_t)my_slot >= a.recv_rows) {
-                atomicOr(a.status, kDevRecvOverflow);
+                if (a.status) atomicOr(a.status, kDevRecvOverflow);
                 my_slot = -1;
             }
             if (ci == 0) record_dest(a, t, kb + lane, my_slot, my_w);
@@ -301,6 +319,10 @@ __global__ void __launch_bounds__(kBlock) dispatch_multi_kernel(DispatchK a) {
             for (int k = 0; k < kn; ++k) {
                 const int slot = lane_read(my_slot, k);
                 if (slot < 0) continue;
+                if (MODE == kModeCast) {
+                    store_cast<VPL>(a, slot, v0, lane, s, q);
+                    continue;
+                }
                 ep_u32x4 *dstrow = (ep_u32x4 *)(a.recv + (int64_t)slot * a.out_row_bytes);
 #pragma unroll
                 for (int i = 0; i < VPL; ++i) {
@@ -318,7 +340,7 @@ hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStr
 #define EP_CASE(V)                                                                              \
     case V:                                                                                     \
         if (multi)                                                                              \
-            hipLaunchKernelGGL((dispatch_multi_kernel<V, MODE, (MODE == kModeCast ? 1 : EP_DISPATCH_TPW)>), \
+            hipLaunchKernelGGL((dispatch_multi_kernel<V, MODE, (MODE == kModeCast ? EP_CAST_TPW : EP_DISPATCH_TPW)>), \
                                dim3(grid), dim3(kBlock), 0, stream, k);                        \
         else                                                                                    \
             hipLaunchKernelGGL((dispatch_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
@@ -353,10 +375,10 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     }
     k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
     if (k.wpr < 1) k.wpr = 1;
-    // copy modes with a layout: TPW tokens per wave
-    const bool multi = mode != kModeCast && k.dst != nullptr && EP_DISPATCH_TPW > 1;
-    int64_t waves = (int64_t)k.T * k.wpr;
-    if (multi) waves = (((int64_t)k.T + EP_DISPATCH_TPW - 1) / EP_DISPATCH_TPW) * k.wpr;
+    // several tokens per wave: copy modes with a layout, and the cast modes
+    const int tpw = mode == kModeCast ? EP_CAST_TPW : (k.dst != nullptr ? EP_DISPATCH_TPW : 1);
+    const bool multi = tpw > 1;
+    int64_t waves = (((int64_t)k.T + tpw - 1) / tpw) * k.wpr;
     k.n_tok_blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
     const int64_t grid = (int64_t)k.n_tok_blocks + (int64_t)k.E * k.pad_slices;
     if (grid == 0) return hipSuccess;
@@ -364,7 +386,7 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     switch (mode) {
         case kModeCopy16: return launch_mode<kModeCopy16>(k, vpl, (int)grid, multi, stream);
         case kModeCopyFp8: return launch_mode<kModeCopyFp8>(k, vpl, (int)grid, multi, stream);
-        default: return launch_mode<kModeCast>(k, vpl, (int)grid, false, stream);
+        default: return launch_mode<kModeCast>(k, vpl, (int)grid, multi, stream);
     }
 }
 

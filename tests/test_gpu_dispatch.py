@@ -137,12 +137,15 @@ def test_cast_fp8_groups(gpu, G):
 
 def test_cast_fp8_every_bf16_pattern(gpu):
     """All finite bf16 patterns, each in groups whose amax is set by one of
-    several leading values, so every pattern is cast under many scales."""
+    several leading values, so every pattern is cast under many scales.  The
+    leads 448 and 0.875 give the exact scales 1 and 2^-9: there the quotients
+    are the bf16 values themselves (times 2^9), which include every e4m3 code,
+    every rounding midpoint (ties) and their bf16 neighbours."""
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     finite = bits[(bits & 0x7F80) != 0x7F80]
     mags = np.abs(oracle.bf16_to_float(finite))
     rows = []
-    for lead in (0x7F7F, 0x4380, 0x3F80, 0x3400, 0x0080):
+    for lead in (0x7F7F, 0x4380, 0x43E0, 0x3F80, 0x3F60, 0x3400, 0x0080):
         lead_v = abs(float(oracle.bf16_to_float(np.array([lead], np.uint16))[0]))
         vals = finite[mags <= lead_v]
         pad = (-len(vals)) % 127
