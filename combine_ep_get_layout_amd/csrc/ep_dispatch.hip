@@ -33,6 +33,9 @@
 #ifndef EP_CAST_TPW
 #define EP_CAST_TPW 1            // tokens per wave in the cast modes
 #endif
+#ifndef EP_PAD_ROWS_PER_SLICE
+#define EP_PAD_ROWS_PER_SLICE 4  // padding rows per workgroup when zeroing
+#endif
 #ifndef EP_DISPATCH_NT_STORE
 #define EP_DISPATCH_NT_STORE 0   // plain stores measured faster for the receive rows
 #endif
@@ -433,7 +436,8 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     k.zero_padding = a.zero_padding;
     int maxpad = a.C > 0 ? a.C : a.A - 1;
     if ((!a.zero_padding && !a.recv_w) || a.partitioned) maxpad = 0;
-    if (maxpad > 0) k.pad_slices = a.zero_padding ? (maxpad + 3) / 4 : 1;
+    if (maxpad > 0)
+        k.pad_slices = a.zero_padding ? (maxpad + EP_PAD_ROWS_PER_SLICE - 1) / EP_PAD_ROWS_PER_SLICE : 1;
     return run(k, a.mode, EP_DISPATCH_VPL, stream);
 }
 

@@ -459,14 +459,19 @@ __device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_flags,
         if ((int64_t)slot < a.max_rows) a.src_of_slot[slot] = (int32_t)p;
     }
 
-    // Padding slots of the experts this workgroup owns (e = tile mod tiles).
-    for (int e = tile; e < E; e += nt) {
-        const int c = s_tot[e];
-        const int used = C > 0 ? min(c, C) : c;
-        const int64_t beg = (int64_t)s_off[e] + used;
-        int64_t end = C > 0 ? (int64_t)s_off[e] + C : (int64_t)s_off[e + 1];
-        if (end > a.max_rows) end = a.max_rows;
-        for (int64_t s = beg + tid; s < end; s += blockDim.x) a.src_of_slot[s] = -1;
+    // Padding slots of the experts this workgroup owns (e = tile mod tiles),
+    // one expert per wave at a time: an expert's padding is at most
+    // max(A - 1, C) rows, so whole-block passes would leave most lanes idle.
+    {
+        const int lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+        for (int e = tile + w * nt; e < E; e += nt * nw) {
+            const int c = s_tot[e];
+            const int used = C > 0 ? min(c, C) : c;
+            const int64_t beg = (int64_t)s_off[e] + used;
+            int64_t end = C > 0 ? (int64_t)s_off[e] + C : (int64_t)s_off[e + 1];
+            if (end > a.max_rows) end = a.max_rows;
+            for (int64_t s = beg + lane; s < end; s += 64) a.src_of_slot[s] = -1;
+        }
     }
 }
 
