@@ -9,15 +9,17 @@
 // with padding rows zeroed on request and recv weights 0 on padding.
 //
 // Kernel shape (gfx950, wave64).  A wave owns one chunk of VPL x 64 16-byte
-// vectors of one token row: it loads the chunk once into registers (x is
-// read exactly once) and stores it to each of the token's K destination rows
-// with 16-byte non-temporal stores, so the write stream (K times the read
-// stream) does not evict the routing tables from L2.  Rows are moved as
-// integer vectors, never as floats.  In the fused-cast mode the chunk is
-// converted in registers: per-group amax by a butterfly over the group's
-// lanes, fp32 scale, correctly rounded fp32 division, e4m3 round-to-nearest-
-// even, 8 codes per lane per vector.  Padding rows are handled by extra
-// workgroups of the same launch (one slice of one expert's padding each).
+// vectors of a token row (VPL = 14: the whole 7168-channel bf16 row): it
+// loads the chunk once into registers with non-temporal loads (x is read
+// exactly once) and stores it to each of the token's K destination rows with
+// 16-byte stores.  Rows are moved as integer vectors, never as floats.  The
+// copy modes run on a grid of resident waves, each streaming its share of
+// the tokens with the next token's chunk in flight while the current one is
+// stored.  In the cast modes the chunk is converted in registers: per-group
+// amax by DPP exchanges, fp32 scale, the correctly rounded quotient from one
+// reciprocal per group, e4m3 round-to-nearest-even, 8 codes per lane per
+// vector.  Padding rows are handled by extra workgroups of the same launch
+// (one slice of one expert's padding each).
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -28,10 +30,7 @@
 #define EP_CAST_VPL 4
 #endif
 #ifndef EP_DISPATCH_TPW
-#define EP_DISPATCH_TPW 2        // tokens per wave in the copy modes (2: measured best)
-#endif
-#ifndef EP_CAST_TPW
-#define EP_CAST_TPW 1            // tokens per wave in the cast modes
+#define EP_DISPATCH_TPW 2        // consecutive tokens per group in the copy modes (2: measured best)
 #endif
 #ifndef EP_PAD_ROWS_PER_SLICE
 #define EP_PAD_ROWS_PER_SLICE 4  // padding rows per workgroup when zeroing
@@ -72,6 +71,7 @@ struct DispatchK {
     int group_lanes;          // cast: lanes per scale group; 0 = one scale per row
     int wpr;                  // waves per row
     int n_tok_blocks;
+    int n_groups;             // streaming kernel: token-group slots (waves / wpr)
     int pad_slices;           // padding workgroups per expert (0 = none)
     int zero_padding;
 };
@@ -266,11 +266,58 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
     }
 }
 
-// Copy modes, TPW consecutive tokens per wave (same row chunk): the next
-// token's row is requested before the current one is stored, so reads of x
-// overlap the K-fold stores instead of all arriving in one burst up front.
+#ifndef EP_DISPATCH_PERSIST
+#define EP_DISPATCH_PERSIST 12   // copy modes: waves per CU of the resident grid (the kernel's
+                                 // registers allow three per SIMD); 0: one group per wave
+#endif
+
+// All destinations of token t for one row chunk (copy modes).
+template <int VPL, int MODE>
+__device__ __forceinline__ void store_token(const DispatchK &a, int t, int ci, int v0, int lane,
+                                            const ep_u32x4 (&v)[VPL]) {
+    for (int kb = 0; kb < a.nd; kb += 64) {
+        int my_slot = -1;
+        float my_w = 1.0f;
+        if (kb + lane < a.nd) {
+            my_slot = a.dst[(int64_t)t * a.nd + kb + lane];
+            if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
+        }
+        if ((int64_t)my_slot >= a.recv_rows) {
+            atomicOr(a.status, kDevRecvOverflow);
+            my_slot = -1;
+        }
+        if (ci == 0) record_dest(a, t, kb + lane, my_slot, my_w);
+        const int kn = min(64, a.nd - kb);
+        for (int k = 0; k < kn; ++k) {
+            const int slot = lane_read(my_slot, k);
+            if (slot < 0) continue;
+            ep_u32x4 *dstrow = (ep_u32x4 *)(a.recv + (int64_t)slot * a.out_row_bytes);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int vi = v0 + i * 64 + lane;
+                if (vi < a.nvec) row_store(dstrow + vi, v[i]);
+            }
+            if (MODE == kModeCopyFp8 && ci == 0) copy_scales(a, t, slot, lane);
+        }
+    }
+}
+
+template <int VPL>
+__device__ __forceinline__ void load_chunk(const DispatchK &a, int t, int v0, int lane, ep_u32x4 (&v)[VPL]) {
+    const ep_u32x4 *src = (const ep_u32x4 *)(a.x + (int64_t)t * a.in_row_bytes);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int vi = v0 + i * 64 + lane;
+        v[i] = vi < a.nvec ? load_nt(src + vi) : ep_u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Copy modes on a grid of resident waves: wave (g, ci) streams the tokens of
+// groups g, g + n_groups, g + 2 n_groups, ... (TPW consecutive tokens each),
+// always holding the next token's chunk in flight while it stores the
+// current one, so reads and writes stay interleaved for the whole launch.
 template <int VPL, int MODE, int TPW>
-__global__ void __launch_bounds__(kBlock) dispatch_multi_kernel(DispatchK a) {
+__global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
     if ((int)blockIdx.x >= a.n_tok_blocks) {
         pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
         return;
@@ -279,62 +326,26 @@ __global__ void __launch_bounds__(kBlock) dispatch_multi_kernel(DispatchK a) {
     const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
     const int g = gw / a.wpr;
     const int ci = gw - g * a.wpr;
-    const int t0 = g * TPW;
-    if (t0 >= a.T) return;
+    if (g >= a.n_groups) return;
     const int v0 = ci * VPL * 64;
-    ep_u32x4 v[2][VPL];
-    {
-        const ep_u32x4 *src = (const ep_u32x4 *)(a.x + (int64_t)t0 * a.in_row_bytes);
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int vi = v0 + i * 64 + lane;
-            v[0][i] = vi < a.nvec ? load_nt(src + vi) : ep_u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-        const int t = t0 + j;
-        if (t >= a.T) break;
-        if (j + 1 < TPW && t + 1 < a.T) {
-            const ep_u32x4 *src = (const ep_u32x4 *)(a.x + (int64_t)(t + 1) * a.in_row_bytes);
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int vi = v0 + i * 64 + lane;
-                v[(j + 1) & 1][i] = vi < a.nvec ? load_nt(src + vi) : ep_u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-        float s[VPL];
-        ep_u32x2 q[VPL];
-        if (MODE == kModeCast) cast_chunk<VPL>(a, v[j & 1], s, q);
-        for (int kb = 0; kb < a.nd; kb += 64) {
-            int my_slot = -1;
-            float my_w = 1.0f;
-            if (kb + lane < a.nd) {
-                my_slot = a.dst ? a.dst[(int64_t)t * a.nd + kb + lane] : t;
-                if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
-            }
-            if ((int64_t)my_slot >= a.recv_rows) {
-                if (a.status) atomicOr(a.status, kDevRecvOverflow);
-                my_slot = -1;
-            }
-            if (ci == 0) record_dest(a, t, kb + lane, my_slot, my_w);
-            const int kn = min(64, a.nd - kb);
-            for (int k = 0; k < kn; ++k) {
-                const int slot = lane_read(my_slot, k);
-                if (slot < 0) continue;
-                if (MODE == kModeCast) {
-                    store_cast<VPL>(a, slot, v0, lane, s, q);
-                    continue;
-                }
-                ep_u32x4 *dstrow = (ep_u32x4 *)(a.recv + (int64_t)slot * a.out_row_bytes);
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    const int vi = v0 + i * 64 + lane;
-                    if (vi < a.nvec) row_store(dstrow + vi, v[j & 1][i]);
-                }
-                if (MODE == kModeCopyFp8 && ci == 0) copy_scales(a, t, slot, lane);
-            }
-        }
+    const int64_t stride = (int64_t)a.n_groups * TPW;
+    // j-th token of this wave
+    auto tok = [&](int j) -> int64_t { return (int64_t)g * TPW + (j / TPW) * stride + (j % TPW); };
+    int64_t t = tok(0);
+    if (t >= a.T) return;
+    ep_u32x4 v0b[VPL], v1b[VPL];
+    load_chunk<VPL>(a, (int)t, v0, lane, v0b);
+    for (int j = 0;; j += 2) {
+        int64_t tn = tok(j + 1);
+        if (tn < a.T) load_chunk<VPL>(a, (int)tn, v0, lane, v1b);
+        store_token<VPL, MODE>(a, (int)t, ci, v0, lane, v0b);
+        if (tn >= a.T) break;
+        t = tn;
+        tn = tok(j + 2);
+        if (tn < a.T) load_chunk<VPL>(a, (int)tn, v0, lane, v0b);
+        store_token<VPL, MODE>(a, (int)t, ci, v0, lane, v1b);
+        if (tn >= a.T) break;
+        t = tn;
     }
 }
 
@@ -342,9 +353,9 @@ template <int MODE>
 hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStream_t stream) {
 #define EP_CASE(V)                                                                              \
     case V:                                                                                     \
-        if (multi)                                                                              \
-            hipLaunchKernelGGL((dispatch_multi_kernel<V, MODE, (MODE == kModeCast ? EP_CAST_TPW : EP_DISPATCH_TPW)>), \
-                               dim3(grid), dim3(kBlock), 0, stream, k);                        \
+        if (MODE != kModeCast && multi)                                                         \
+            hipLaunchKernelGGL((dispatch_stream_kernel<V, MODE, EP_DISPATCH_TPW>), dim3(grid),  \
+                               dim3(kBlock), 0, stream, k);                                     \
         else                                                                                    \
             hipLaunchKernelGGL((dispatch_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
         break;
@@ -378,10 +389,19 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     }
     k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
     if (k.wpr < 1) k.wpr = 1;
-    // several tokens per wave: copy modes with a layout, and the cast modes
-    const int tpw = mode == kModeCast ? EP_CAST_TPW : (k.dst != nullptr ? EP_DISPATCH_TPW : 1);
-    const bool multi = tpw > 1;
+    // copy modes with a layout: the streaming kernel, TPW tokens per group
+    const int tpw = mode != kModeCast && k.dst != nullptr ? EP_DISPATCH_TPW : 1;
+    const bool multi = mode != kModeCast && k.dst != nullptr;
     int64_t waves = (((int64_t)k.T + tpw - 1) / tpw) * k.wpr;
+    k.n_groups = (int)(((int64_t)k.T + tpw - 1) / tpw);
+    if (EP_DISPATCH_PERSIST > 0 && multi) {
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess)
+            (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        const int64_t cap = (int64_t)cus * EP_DISPATCH_PERSIST / k.wpr;   // group slots
+        if (k.n_groups > cap) k.n_groups = (int)cap;
+        waves = (int64_t)k.n_groups * k.wpr;
+    }
     k.n_tok_blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
     const int64_t grid = (int64_t)k.n_tok_blocks + (int64_t)k.E * k.pad_slices;
     if (grid == 0) return hipSuccess;
