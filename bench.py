@@ -176,6 +176,33 @@ def other_workloads(ep, torch, dev, steps):
     return out
 
 
+def cold_per_op(torch, dev, iters, ops):
+    """Each operation timed alone, `iters` times, after a 768 MiB write that
+    evicts L2 and the memory-side cache; the flush is outside the event pair.
+    Returns median / p10 / p90 in microseconds."""
+    flush = torch.empty(768 << 20, dtype=torch.uint8, device=dev)
+    out = {}
+    for name, fn in ops.items():
+        fn()
+        pairs = []
+        for _ in range(iters):
+            flush.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+        out[name] = {"median_us": round(float(np.median(us)), 2),
+                     "p10_us": round(float(np.percentile(us, 10)), 2),
+                     "p90_us": round(float(np.percentile(us, 90)), 2)}
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle, as it stands, on a token prefix of the same workload."""
     import oracle
@@ -214,6 +241,8 @@ def main():
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the per-operation timings after a cache flush")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before timing, run one plain device copy of MIB MiB (a known-size "
                          "reference for HBM byte counters under rocprofv3 --pmc)")
@@ -295,6 +324,16 @@ def main():
     dis_ms = per_op(lambda: ep.ep_dispatch(x, lay, wts, out=(recv, None, recv_w)))
     com_ms = per_op(lambda: ep.ep_combine(y, lay, wts, out=out))
     assert lay.check() == 0
+    cold = None
+    if not args.no_cold:
+        cold = cold_per_op(torch, dev, args.steps, {
+            "layout": lambda: ep.ep_get_layout(idx, E, A, w.num_partitions, w.capacity, layout=lay),
+            "dispatch_reused_layout": lambda: ep.ep_dispatch(x, lay, wts, out=(recv, None, recv_w)),
+            "dispatch_fresh_layout": lambda: (
+                ep.ep_get_layout(idx, E, A, w.num_partitions, w.capacity, layout=lay),
+                ep.ep_dispatch(x, lay, wts, out=(recv, None, recv_w))),
+            "combine": lambda: ep.ep_combine(y, lay, wts, out=out),
+        })
 
     lb, rb, cb = algorithmic_bytes(T, H, K, N, R)
     total = lb + rb + cb
@@ -324,6 +363,14 @@ def main():
                         for kk, vv in v.items()} for k, v in kern.items()},
         "wall_s_timed": round(wall, 4),
     }
+    if cold is not None:
+        lb_, rb_, cb_ = algorithmic_bytes(T, H, K, N, R)
+        nbytes = {"layout": lb_, "dispatch_reused_layout": rb_, "dispatch_fresh_layout": lb_ + rb_,
+                  "combine": cb_}
+        for k, v in cold.items():
+            v["GBps_median"] = round(nbytes[k] / (v["median_us"] * 1e-6) / 1e9, 1)
+            v["hbm_frac_median"] = round(v["GBps_median"] / HBM_PEAK_GBS, 4)
+        res["cold_cache"] = cold
     if not args.no_other_workloads:
         del recv, y
         torch.cuda.empty_cache()
