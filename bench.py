@@ -248,7 +248,7 @@ def main():
                          "reference for HBM byte counters under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU's share only; --gpus {args.gpus} is not "
+        print(f"bench.py: the benchmark measures one GPU's share only; --gpus {args.gpus} is not "
               "supported (no collectives, no sharding).", file=sys.stderr)
         sys.exit(2)
 

@@ -305,7 +305,7 @@ const char *ep_status_string(int code) {
     switch (code) {
         case EP_OK: return "ok";
         case EP_ERR_INVALID_ARG: return "invalid argument";
-        case EP_ERR_UNSUPPORTED: return "unsupported by this build";
+        case EP_ERR_UNSUPPORTED: return "outside the library's limits";
         case EP_ERR_WORKSPACE: return "workspace missing or too small";
         case EP_ERR_LAUNCH: return "kernel launch failed";
         default: return "unknown status";

@@ -40,7 +40,7 @@ extern "C" {
 typedef enum {
     EP_OK = 0,
     EP_ERR_INVALID_ARG = -1,  /* bad size, null required pointer, misalignment */
-    EP_ERR_UNSUPPORTED = -2,  /* valid but outside this build's limits        */
+    EP_ERR_UNSUPPORTED = -2,  /* valid but outside the library's limits      */
     EP_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required   */
     EP_ERR_LAUNCH = -4        /* the HIP runtime refused a launch             */
 } ep_status;
@@ -63,7 +63,7 @@ enum {
 enum { EP_DTYPE_BF16 = 0, EP_DTYPE_FP8_E4M3 = 1, EP_DTYPE_FP8_E4M3_POW2 = 2,
        EP_DTYPE_FP8_E4M3_UE8M0 = 3 };
 
-/* Limits of this build. */
+/* Limits of the library. */
 enum { EP_MAX_EXPERTS = 4096, EP_MAX_PARTITIONS = 1024, EP_MAX_TOPK = 256,
        EP_MAX_SLOT_PARTITIONS = 64 };
 
