@@ -46,9 +46,13 @@ def algorithmic_bytes(T, H, K, N, R, elem=2):
 
 
 def kernel_source_hash():
+    """Hash of the device sources (every csrc file but the host-only C-ABI
+    layer): profiles/traffic.json is used only while it matches."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "combine_ep_get_layout_amd", "csrc")
     for f in sorted(os.listdir(d)):
+        if f == "ep_api.hip":
+            continue
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
