@@ -205,3 +205,41 @@ def test_combine_reduced_with_capacity_drops(gpu):
     out = gpu.ep_combine_reduced(bf16_to_dev(y), lay, to_dev(w.topk_idx), to_dev(w.topk_weights))
     np.testing.assert_array_equal(
         bf16_bits(out), oracle.combine_reduced_f32(y, w.topk_idx, exp.dst, E, P, w.topk_weights))
+
+
+def test_partition_major_order_and_reduced_combine(gpu):
+    """The partition-major receive order (partition, t, k) is the expanded
+    layout of topk_idx // (E/P) over P "experts", one per partition; the
+    reduced combine over it (routing given as those partition ids) equals, bit
+    for bit, the reduced combine over the expert-major layout holding the same
+    rows (its partial sums fold each partition's pairs in k order either way)."""
+    announce("partition-major order")
+    T, K, E, P, H = 1500, 8, 256, 32, 1024
+    w = ep_inputs.make_workload("skewed", seed=6, T=T, K=K, E=E, with_x=False)
+    m = E // P
+    idx_q = np.where(w.topk_idx >= 0, w.topk_idx // m, -1)
+    lay_e = gpu.ep_get_layout(to_dev(w.topk_idx), E, 1, num_partitions=P)
+    lay_q = gpu.ep_get_layout(to_dev(idx_q), P, 1, num_partitions=P)
+    ref_q = oracle.get_layout(idx_q, P, 1)
+    dst_q = lay_q.dst_slot.cpu().numpy()
+    np.testing.assert_array_equal(dst_q, ref_q.dst)
+    # slots in (partition, t, k) order
+    pairs = [(idx_q[t, k], t, k) for t in range(T) for k in range(K) if idx_q[t, k] >= 0]
+    order = sorted(pairs)
+    np.testing.assert_array_equal([dst_q[t, k] for _, t, k in order], np.arange(len(order)))
+    # the same expert outputs in both receive orders
+    rng = ep_inputs.make_rng(7)
+    vals = ep_inputs.bf16_normal(rng, (T * K, H))           # one row per (t, k)
+    dst_e = lay_e.dst_slot.cpu().numpy()
+    y_e = np.zeros((lay_e.num_recv_rows(), H), np.uint16)
+    y_q = np.zeros((lay_q.num_recv_rows(), H), np.uint16)
+    for t in range(T):
+        for k in range(K):
+            if dst_e[t, k] >= 0:
+                y_e[dst_e[t, k]] = vals[t * K + k]
+                y_q[dst_q[t, k]] = vals[t * K + k]
+    out_e = gpu.ep_combine_reduced(bf16_to_dev(y_e), lay_e, to_dev(w.topk_idx), to_dev(w.topk_weights))
+    out_q = gpu.ep_combine_reduced(bf16_to_dev(y_q), lay_q, to_dev(idx_q), to_dev(w.topk_weights))
+    np.testing.assert_array_equal(bf16_bits(out_e), bf16_bits(out_q))
+    np.testing.assert_array_equal(
+        bf16_bits(out_q), oracle.combine_reduced_f32(y_q, w.topk_idx, dst_q, E, P, w.topk_weights))
