@@ -21,10 +21,10 @@
 #include "ep_internal.h"
 
 #ifndef EP_COMBINE_VPL
-#define EP_COMBINE_VPL 2    // 16-byte vectors per lane per row chunk
+#define EP_COMBINE_VPL 1    // 16-byte vectors per lane per row chunk (1: measured best)
 #endif
 #ifndef EP_COMBINE_U
-#define EP_COMBINE_U 8      // rows in flight per wave (0: by VPL)
+#define EP_COMBINE_U 4      // rows in flight per wave (0: by VPL; 4: measured best)
 #endif
 
 namespace ep {
