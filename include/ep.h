@@ -10,8 +10,9 @@
  *   [API]  "DeepEP test target API reference" (DeepEP v2 test page):
  *          2.1 dispatch() and its parameter table, 2.2 combine(),
  *          3.1 V1 Buffer.dispatch() layout tensors, 3.2 V1 combine (no
- *          weights), 4.1 refs (ordered accumulation), 4.2 math (align,
- *          per-token cast to float8_e4m3fn).
+ *          weights), 3.3 low-latency dispatch scale options, 4.1 refs
+ *          (ordered accumulation), 4.2 math (align, per-token cast to
+ *          float8_e4m3fn).
  *   [RUST] "spark_model/layers/ep_dispatch.rs": partition of (token, expert,
  *          weight) pairs by expert ownership; length checks.
  *
@@ -135,13 +136,15 @@ int64_t ep_worst_case_recv_rows(const ep_layout_params *params);
  * used slots and -1 for padding slots (slots >= max_recv_rows are not
  * written); partition membership and per-partition token counts; and, for
  * the optional pointers that are set, the partition layout (offsets,
- * token_slot, tokens per group of G partitions).  The optional pointers
- * need P <= EP_MAX_SLOT_PARTITIONS (else EP_ERR_UNSUPPORTED).
+ * token_slot, tokens per group of G partitions).  token_slot needs
+ * P <= EP_MAX_SLOT_PARTITIONS (else EP_ERR_UNSUPPORTED); the offsets and the
+ * group counts work for any P.
  * layout->status is overwritten with EP_DEV_BAD_EXPERT / EP_DEV_CAPACITY /
  * EP_DEV_RECV_OVERFLOW (R > max_recv_rows).  T = 0 is valid.
  * Errors: EP_ERR_INVALID_ARG (null pointer, T < 0, K < 1, E < 1, A < 1,
- * P < 1, E % P != 0, C < 0, C % A != 0, fixed mode with E*C > max_recv_rows,
- * int32 overflow of T*K or of the worst-case rows), EP_ERR_UNSUPPORTED
+ * P < 1, E % P != 0, partitions_per_group < 0 or not dividing P, C < 0,
+ * C % A != 0, fixed mode with E*C > max_recv_rows, int32 overflow of T*K or
+ * of the worst-case rows), EP_ERR_UNSUPPORTED
  * (E > EP_MAX_EXPERTS, P > EP_MAX_PARTITIONS, K > EP_MAX_TOPK),
  * EP_ERR_WORKSPACE. */
 int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,
@@ -177,7 +180,8 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,
  *                0: their bytes are left as they were.
  * recv_x[dst_slot[t,k]] = x[t] byte for byte (fp8: codes and scale row).
  * Errors: EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED (a scale_group outside the
- * set above). */
+ * set above, or one scale per row, G = hidden, above 8192 channels in a cast:
+ * the row must fit one wave). */
 int ep_dispatch(const void *x, int x_dtype, const void *x_scales, int recv_dtype,
                 int32_t hidden, int32_t scale_group, const float *topk_weights,
                 const ep_layout_params *params, const ep_layout *layout,
