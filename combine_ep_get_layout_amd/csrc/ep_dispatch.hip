@@ -63,6 +63,7 @@ struct DispatchK {
     int64_t *recv_idx;        // partitioned: [rows, K] local expert ids, or NULL
     float *recv_wk;           // partitioned: [rows, K] weights, or NULL
     int m;                    // partitioned: experts per partition (0: expanded)
+    int meta_vec;             // partitioned: metadata rows 16-byte aligned (K % 4 == 0)
     int nvec;                 // 16-byte vectors per input row
     int in_row_bytes;
     int out_row_bytes;
@@ -155,23 +156,77 @@ __device__ __forceinline__ void store_cast(const DispatchK &a, int64_t slot, int
     }
 }
 
-// Per-destination bookkeeping of one lane: the expanded layout records the
-// pair's weight in its row; the partitioned layout records, for the row of
-// (t, q), every pair's partition-local expert id (-1 when elsewhere) and
-// weight (0 when elsewhere).
+// Partitioned metadata of row (t, q) (slot; -1: this lane has no row) for
+// pairs [kb, kb + kn) of the token, whose expert ids and weights are held
+// one pair per lane (e: -1 for none or invalid; wv): every pair's
+// partition-local id when it belongs to q, else -1, and its weight, else 0.
+// Broadcast by readlane; each destination lane writes its row four pairs at
+// a time with 16-byte stores when the rows are aligned for them (meta_vec).
+__device__ __forceinline__ void write_meta(const DispatchK &a, int q, int slot, int kb, int kn,
+                                           int e, float wv) {
+    const int64_t row = (int64_t)slot * a.K + kb;
+    for (int k = 0; k < kn; k += 4) {
+        int loc[4];
+        float wt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ej = k + j < kn ? lane_read(e, k + j) : -1;
+            const float wj = k + j < kn ? lane_read_f(wv, k + j) : 0.0f;
+            const bool mine = ej >= 0 && ej / a.m == q;
+            loc[j] = mine ? ej - q * a.m : -1;
+            wt[j] = mine ? wj : 0.0f;
+        }
+        if (slot < 0) continue;
+        if (a.meta_vec && k + 4 <= kn) {
+            if (a.recv_idx) {
+                ep_u32x4 *p = (ep_u32x4 *)(a.recv_idx + row + k);
+                p[0] = ep_u32x4{(uint32_t)loc[0], (uint32_t)(loc[0] >> 31), (uint32_t)loc[1],
+                                (uint32_t)(loc[1] >> 31)};
+                p[1] = ep_u32x4{(uint32_t)loc[2], (uint32_t)(loc[2] >> 31), (uint32_t)loc[3],
+                                (uint32_t)(loc[3] >> 31)};
+            }
+            if (a.recv_wk)
+                *(ep_u32x4 *)(a.recv_wk + row + k) =
+                    ep_u32x4{__float_as_uint(wt[0]), __float_as_uint(wt[1]), __float_as_uint(wt[2]),
+                             __float_as_uint(wt[3])};
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (k + j >= kn) break;
+                if (a.recv_idx) a.recv_idx[row + k + j] = loc[j];
+                if (a.recv_wk) a.recv_wk[row + k + j] = wt[j];
+            }
+        }
+    }
+}
+
+// Token t's expert id and weight for pair kb + lane (partitioned mode).
+__device__ __forceinline__ void load_pair(const DispatchK &a, int t, int kb, int lane, int &e, float &wv) {
+    e = -1;
+    wv = 0.0f;
+    if (kb + lane < a.K) {
+        const int64_t v = a.idx[(int64_t)t * a.K + kb + lane];
+        e = (v >= 0 && v < a.E) ? (int)v : -1;
+        wv = a.w ? a.w[(int64_t)t * a.K + kb + lane] : 1.0f;
+    }
+}
+
+// Per-destination bookkeeping, called by every lane of the wave with its
+// destination q (slot -1 when the lane has none): the expanded layout
+// records the pair's weight in its row, the partitioned layout (PART, its
+// own kernel instances, so the expanded ones carry none of this code and
+// keep their register count) the row's metadata, reading the routing here.
+template <bool PART>
 __device__ __forceinline__ void record_dest(const DispatchK &a, int t, int q, int slot, float w) {
-    if (slot < 0) return;
-    if (a.m == 0) {
-        if (a.recv_w) a.recv_w[slot] = w;
+    if (!PART) {
+        if (slot >= 0 && a.recv_w) a.recv_w[slot] = w;
         return;
     }
-    for (int k = 0; k < a.K; ++k) {
-        const int64_t e = a.idx[(int64_t)t * a.K + k];
-        const bool local = e >= 0 && e < a.E && e / a.m == q;
-        if (a.recv_idx) a.recv_idx[(int64_t)slot * a.K + k] = local ? e - (int64_t)q * a.m : -1;
-        if (a.recv_wk)
-            a.recv_wk[(int64_t)slot * a.K + k] =
-                local ? (a.w ? a.w[(int64_t)t * a.K + k] : 1.0f) : 0.0f;
+    for (int kb = 0; kb < a.K; kb += 64) {
+        int e;
+        float wv;
+        load_pair(a, t, kb, __lane_id(), e, wv);
+        write_meta(a, q, slot, kb, min(64, a.K - kb), e, wv);
     }
 }
 
@@ -203,7 +258,7 @@ __device__ __forceinline__ void pad_rows(const DispatchK &a, int pb) {
     }
 }
 
-template <int VPL, int MODE>
+template <int VPL, int MODE, bool PART>
 __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
     if ((int)blockIdx.x >= a.n_tok_blocks) {
         pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
@@ -239,7 +294,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
             if (a.status) atomicOr(a.status, kDevRecvOverflow);
             my_slot = -1;
         }
-        if (ci == 0) record_dest(a, t, kb + lane, my_slot, my_w);
+        if (ci == 0) record_dest<PART>(a, t, kb + lane, my_slot, my_w);
         const int kn = min(64, K - kb);
 
         if (MODE == kModeCast) {
@@ -266,13 +321,16 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
     }
 }
 
+#ifndef EP_DISPATCH_PERSIST_PART
+#define EP_DISPATCH_PERSIST_PART 8   // the same for the partitioned instances (two per SIMD)
+#endif
 #ifndef EP_DISPATCH_PERSIST
 #define EP_DISPATCH_PERSIST 12   // copy modes: waves per CU of the resident grid (the kernel's
                                  // registers allow three per SIMD); 0: one group per wave
 #endif
 
 // All destinations of token t for one row chunk (copy modes).
-template <int VPL, int MODE>
+template <int VPL, int MODE, bool PART>
 __device__ __forceinline__ void store_token(const DispatchK &a, int t, int ci, int v0, int lane,
                                             const ep_u32x4 (&v)[VPL]) {
     for (int kb = 0; kb < a.nd; kb += 64) {
@@ -286,7 +344,7 @@ __device__ __forceinline__ void store_token(const DispatchK &a, int t, int ci, i
             atomicOr(a.status, kDevRecvOverflow);
             my_slot = -1;
         }
-        if (ci == 0) record_dest(a, t, kb + lane, my_slot, my_w);
+        if (ci == 0) record_dest<PART>(a, t, kb + lane, my_slot, my_w);
         const int kn = min(64, a.nd - kb);
         for (int k = 0; k < kn; ++k) {
             const int slot = lane_read(my_slot, k);
@@ -316,7 +374,7 @@ __device__ __forceinline__ void load_chunk(const DispatchK &a, int t, int v0, in
 // groups g, g + n_groups, g + 2 n_groups, ... (TPW consecutive tokens each),
 // always holding the next token's chunk in flight while it stores the
 // current one, so reads and writes stay interleaved for the whole launch.
-template <int VPL, int MODE, int TPW>
+template <int VPL, int MODE, int TPW, bool PART>
 __global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
     if ((int)blockIdx.x >= a.n_tok_blocks) {
         pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
@@ -338,26 +396,27 @@ __global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
     for (int j = 0;; j += 2) {
         int64_t tn = tok(j + 1);
         if (tn < a.T) load_chunk<VPL>(a, (int)tn, v0, lane, v1b);
-        store_token<VPL, MODE>(a, (int)t, ci, v0, lane, v0b);
+        store_token<VPL, MODE, PART>(a, (int)t, ci, v0, lane, v0b);
         if (tn >= a.T) break;
         t = tn;
         tn = tok(j + 2);
         if (tn < a.T) load_chunk<VPL>(a, (int)tn, v0, lane, v0b);
-        store_token<VPL, MODE>(a, (int)t, ci, v0, lane, v1b);
+        store_token<VPL, MODE, PART>(a, (int)t, ci, v0, lane, v1b);
         if (tn >= a.T) break;
         t = tn;
     }
 }
 
-template <int MODE>
+template <int MODE, bool PART>
 hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStream_t stream) {
 #define EP_CASE(V)                                                                              \
     case V:                                                                                     \
         if (MODE != kModeCast && multi)                                                         \
-            hipLaunchKernelGGL((dispatch_stream_kernel<V, MODE, EP_DISPATCH_TPW>), dim3(grid),  \
-                               dim3(kBlock), 0, stream, k);                                     \
+            hipLaunchKernelGGL((dispatch_stream_kernel<V, MODE, EP_DISPATCH_TPW, PART>),        \
+                               dim3(grid), dim3(kBlock), 0, stream, k);                         \
         else                                                                                    \
-            hipLaunchKernelGGL((dispatch_kernel<V, MODE>), dim3(grid), dim3(kBlock), 0, stream, k); \
+            hipLaunchKernelGGL((dispatch_kernel<V, MODE, PART>), dim3(grid), dim3(kBlock), 0,   \
+                               stream, k);                                                      \
         break;
     switch (vpl) {
         EP_CASE(1) EP_CASE(2) EP_CASE(4) EP_CASE(7) EP_CASE(8) EP_CASE(14) EP_CASE(16)
@@ -365,6 +424,12 @@ hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStr
     }
 #undef EP_CASE
     return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStream_t stream) {
+    return k.m > 0 ? launch_mode<MODE, true>(k, vpl, grid, multi, stream)
+                   : launch_mode<MODE, false>(k, vpl, grid, multi, stream);
 }
 
 // Vectors per lane: the largest allowed count <= limit that divides the
@@ -398,7 +463,8 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess)
             (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        const int64_t cap = (int64_t)cus * EP_DISPATCH_PERSIST / k.wpr;   // group slots
+        const int per_cu = k.m > 0 ? EP_DISPATCH_PERSIST_PART : EP_DISPATCH_PERSIST;
+        const int64_t cap = (int64_t)cus * per_cu / k.wpr;                // group slots
         if (k.n_groups > cap) k.n_groups = (int)cap;
         waves = (int64_t)k.n_groups * k.wpr;
     }
@@ -438,6 +504,7 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     k.idx = a.topk_idx;
     k.recv_idx = a.recv_idx;
     k.recv_wk = a.recv_wk;
+    k.meta_vec = a.K % 4 == 0 && ((uintptr_t)a.recv_idx & 15) == 0 && ((uintptr_t)a.recv_wk & 15) == 0;
     if (a.partitioned) k.dst = a.token_slot;
     if (a.mode == kModeCopy16) {
         k.in_row_bytes = k.out_row_bytes = a.hidden * 2;
