@@ -30,6 +30,7 @@ def _setup(gpu, w, A=None, C=None, P=None):
     (129, 8, 16, 3, 4, True),        # one vector per row
     (65, 16384, 64, 2, 2, True),     # row wider than one wave chunk
     (50, 2056, 128, 8, 1, False),
+    (90, 1024, 1024, 100, 1, True),  # K > 64: destinations in two 64-lane passes
 ])
 def test_dispatch_bf16(gpu, T, H, E, K, A, zero):
     announce("dispatch bf16", T, H, E, K, A, zero)

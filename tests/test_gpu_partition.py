@@ -89,6 +89,8 @@ def test_partition_layout_with_capacity(gpu):
 @pytest.mark.parametrize("name,T,K,E,P,H", [
     ("skewed", 1000, 8, 256, 32, 7168), ("prefill", 333, 6, 64, 64, 1024),
     ("prefill", 129, 4, 32, 4, 2048), ("tiny", 3, 2, 4, 2, 128),
+    ("prefill", 70, 100, 512, 16, 256),     # K > 64: metadata in two passes
+    ("prefill", 70, 30, 512, 16, 256),      # K % 4 != 0: metadata by single stores
 ])
 @pytest.mark.parametrize("weighted", [True, False])
 def test_dispatch_partitioned_parity(gpu, mode, name, T, K, E, P, H, weighted):
