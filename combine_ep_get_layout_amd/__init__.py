@@ -65,8 +65,8 @@ class Layout:
     Tensors: num_tokens_per_expert [E], expert_offset [E+1] (R at [E]),
     num_tokens_per_partition [P], is_token_in_partition [T, P] uint8,
     dst_slot [T, K], src_of_slot [max_recv_rows], status [1]; with the
-    partition layout also partition_offset [P+1], token_slot [T, P] and
-    num_tokens_per_group [P/G] (else None)."""
+    partition layout also partition_offset [P+1], num_tokens_per_group [P/G]
+    and, for P <= 64, token_slot [T, P] (else None)."""
 
     def __init__(self, params: LayoutParams, device, partition_layout: bool = False):
         T, K, E, P = params.num_tokens, params.num_topk, params.num_experts, params.num_partitions
@@ -84,8 +84,9 @@ class Layout:
         if partition_layout:
             G = params.partitions_per_group or P
             self.partition_offset = torch.empty(P + 1, **i32)
-            self.token_slot = torch.empty((T, P), **i32)
             self.num_tokens_per_group = torch.empty(P // G, **i32)
+            if P <= _abi.EP_MAX_SLOT_PARTITIONS:      # token_slot only up to 64 partitions
+                self.token_slot = torch.empty((T, P), **i32)
         nbytes = load_library().ep_get_layout_workspace_bytes(ctypes.byref(params))
         self.workspace = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -167,7 +168,7 @@ def ep_get_layout(topk_idx: torch.Tensor, num_experts: int, expert_alignment: in
            layout.params.partitions_per_group or num_partitions)
           != (T, K, num_experts, num_partitions, int(max_recv_rows),
               partitions_per_group or num_partitions)
-          or (layout.token_slot is not None) != partition_layout):
+          or (layout.partition_offset is not None) != partition_layout):
         raise ValueError("layout buffers do not match these shapes")
     else:
         layout.params = params
@@ -354,7 +355,7 @@ def ep_dispatch_partitioned(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Ten
     buffers (None entries are allocated)."""
     lib = load_library()
     if layout.token_slot is None:
-        raise ValueError("layout was built without partition_layout=True")
+        raise ValueError("the partitioned dispatch needs token_slot: partition_layout=True, P <= 64")
     x, x_scales, scale_group, x_dtype, recv_dtype, scale_fmt = _x_and_dtypes(
         x, recv_fp8, scale_group, scale_fmt)
     T, H = x.shape
@@ -414,7 +415,7 @@ def ep_combine_partitioned(y: torch.Tensor, layout: Layout,
     order, bias first, bf16 round to nearest even)."""
     lib = load_library()
     if layout.token_slot is None:
-        raise ValueError("layout was built without partition_layout=True")
+        raise ValueError("the partitioned combine needs token_slot: partition_layout=True, P <= 64")
     _need_cuda(y, "y")
     if y.dtype != torch.bfloat16:
         raise ValueError("y must be bf16")

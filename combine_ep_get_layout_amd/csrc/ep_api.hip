@@ -12,7 +12,11 @@ namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int to_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_LAUNCH; }
+int to_status(hipError_t e) {
+    if (e == hipSuccess) return EP_OK;
+    // a shape whose kernels would need more LDS than a workgroup can have
+    return e == hipErrorInvalidConfiguration ? EP_ERR_UNSUPPORTED : EP_ERR_LAUNCH;
+}
 
 // Shape checks shared by every call that takes layout params.
 int check_params(const ep_layout_params *p) {

@@ -39,6 +39,7 @@ namespace ep {
 namespace {
 
 constexpr int kCountBlock = 256;   // count workgroup of the two-kernel tiling: 4 waves
+constexpr size_t kMaxLdsBytes = 160 * 1024;   // LDS one workgroup may allocate on gfx950
 constexpr int kSlotsBlock = 1024;  // slots workgroup, and the fused tiling: 16 waves
 #ifndef EP_LAYOUT_RBATCH
 #define EP_LAYOUT_RBATCH 8
@@ -339,8 +340,9 @@ __device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_flags,
     int32_t *s_base = s_tot + W;             // [W]  totals over the tiles before this one
     int32_t *s_off = s_base + W;             // [E+1]
     int32_t *s_poff = s_off + E + 1;         // [P+1] partition offsets
-    int32_t *s_wq = s_poff + P + 1;          // [waves][P] per-wave partition token counts
-    int32_t *s_red = s_wq + (blockDim.x >> 6) * P;   // [kRedInts]
+    int32_t *s_wq = s_poff + P + 1;          // [waves][P] per-wave partition token counts,
+                                             // only with token_slot (P <= 64)
+    int32_t *s_red = s_wq + (blockDim.x >> 6) * (a.token_slot_out ? P : 0);   // [kRedInts]
     const int tid = threadIdx.x;
     const int tile = blockIdx.x;
     const int nt = a.num_tiles > 0 ? a.num_tiles : 1;
@@ -623,7 +625,8 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     const size_t lds_count =
         ((size_t)(L.block / 64) * L.E + ca.tile_pairs_max + L.P + L.NG) * 4;
     const size_t lds_slots = ((size_t)2 * L.row_stride + L.E + 1 + L.P + 1 +
-                              (size_t)(kSlotsBlock / 64) * L.P + kRedInts) * 4;
+                              (size_t)(kSlotsBlock / 64) * (lay->token_slot ? L.P : 0) + kRedInts) * 4;
+    if (lds_count > kMaxLdsBytes || lds_slots > kMaxLdsBytes) return hipErrorInvalidConfiguration;
 
     if (L.fused && L.num_tiles > 0) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;

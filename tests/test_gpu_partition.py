@@ -245,3 +245,21 @@ def test_partition_major_order_and_reduced_combine(gpu):
     np.testing.assert_array_equal(bf16_bits(out_e), bf16_bits(out_q))
     np.testing.assert_array_equal(
         bf16_bits(out_q), oracle.combine_reduced_f32(y_q, w.topk_idx, dst_q, E, P, w.topk_weights))
+
+
+def test_partition_offsets_many_partitions(gpu):
+    """Past 64 partitions the layout still gives the partition offsets and the
+    group counts (no token_slot): E = 4096 experts, P = 1024, G = 1 and 8."""
+    announce("partition offsets P=1024")
+    w = ep_inputs.make_workload("prefill", seed=8, T=300, K=8, E=4096, A=1, with_x=False)
+    for G in (1, 8):
+        lay = gpu.ep_get_layout(to_dev(w.topk_idx), 4096, 1, num_partitions=1024,
+                                partition_layout=True, partitions_per_group=G)
+        assert lay.token_slot is None
+        ref = oracle.partition_layout(w.topk_idx, 4096, 1024, G)
+        np.testing.assert_array_equal(lay.partition_offset.cpu().numpy(), ref.part_offset)
+        np.testing.assert_array_equal(lay.num_tokens_per_group.cpu().numpy(), ref.tok_per_group)
+        np.testing.assert_array_equal(lay.num_tokens_per_partition.cpu().numpy(), ref.tok_per_part)
+        np.testing.assert_array_equal(lay.is_token_in_partition.cpu().numpy(), ref.in_part)
+        exp = oracle.get_layout(w.topk_idx, 4096, 1, 1024)
+        np.testing.assert_array_equal(lay.dst_slot.cpu().numpy(), exp.dst)
