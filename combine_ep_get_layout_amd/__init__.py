@@ -66,7 +66,8 @@ class Layout:
     num_tokens_per_partition [P], is_token_in_partition [T, P] uint8,
     dst_slot [T, K], src_of_slot [max_recv_rows], status [1]; with the
     partition layout also partition_offset [P+1], num_tokens_per_group [P/G]
-    and, for P <= 64, token_slot [T, P] (else None)."""
+    and, for P <= 64, token_slot [T, P] and partition_src [T*P] (the token of
+    each partition row) (else None)."""
 
     def __init__(self, params: LayoutParams, device, partition_layout: bool = False):
         T, K, E, P = params.num_tokens, params.num_topk, params.num_experts, params.num_partitions
@@ -81,12 +82,14 @@ class Layout:
         self.src_of_slot = torch.empty(max(params.max_recv_rows, 1), **i32)
         self.status = torch.zeros(1, **i32)
         self.partition_offset = self.token_slot = self.num_tokens_per_group = None
+        self.partition_src = None
         if partition_layout:
             G = params.partitions_per_group or P
             self.partition_offset = torch.empty(P + 1, **i32)
             self.num_tokens_per_group = torch.empty(P // G, **i32)
             if P <= _abi.EP_MAX_SLOT_PARTITIONS:      # token_slot only up to 64 partitions
                 self.token_slot = torch.empty((T, P), **i32)
+                self.partition_src = torch.empty(max(T * P, 1), **i32)
         nbytes = load_library().ep_get_layout_workspace_bytes(ctypes.byref(params))
         self.workspace = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -112,7 +115,8 @@ class Layout:
 
     def ptrs(self) -> LayoutPtrs:
         opt = [None if t is None else t.data_ptr()
-               for t in (self.partition_offset, self.token_slot, self.num_tokens_per_group)]
+               for t in (self.partition_offset, self.token_slot, self.num_tokens_per_group,
+                         self.partition_src)]
         return LayoutPtrs(self.num_tokens_per_expert.data_ptr(), self.expert_offset.data_ptr(),
                           self.num_tokens_per_partition.data_ptr(),
                           self.is_token_in_partition.data_ptr(), self.dst_slot.data_ptr(),

@@ -46,7 +46,7 @@ class LayoutPtrs(ctypes.Structure):
                 ("is_token_in_partition", ctypes.c_void_p), ("dst_slot", ctypes.c_void_p),
                 ("src_of_slot", ctypes.c_void_p), ("status", ctypes.c_void_p),
                 ("partition_offset", ctypes.c_void_p), ("token_slot", ctypes.c_void_p),
-                ("num_tokens_per_group", ctypes.c_void_p)]
+                ("num_tokens_per_group", ctypes.c_void_p), ("partition_src", ctypes.c_void_p)]
 
 
 _lib = None

@@ -73,6 +73,7 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *p, const ep_l
         return EP_ERR_INVALID_ARG;
     if (p->max_recv_rows > 0 && !layout->src_of_slot) return EP_ERR_INVALID_ARG;
     if (layout->token_slot && p->num_partitions > EP_MAX_SLOT_PARTITIONS) return EP_ERR_UNSUPPORTED;
+    if (layout->partition_src && !layout->token_slot && p->num_tokens > 0) return EP_ERR_INVALID_ARG;
     ep::LayoutPlan plan;
     if (!ep::make_layout_plan(p, &plan)) return EP_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace))
@@ -229,6 +230,8 @@ int ep_dispatch_partitioned(const void *x, int x_dtype, const void *x_scales, in
     a.topk_idx = topk_idx;
     a.recv_idx = recv_topk_idx;
     a.recv_wk = recv_topk_weights;
+    a.part_src = layout->partition_src;
+    a.part_offset = layout->partition_offset;
     return to_status(ep::launch_dispatch(a, (hipStream_t)stream));
 }
 

@@ -64,6 +64,10 @@ struct DispatchK {
     float *recv_wk;           // partitioned: [rows, K] weights, or NULL
     int m;                    // partitioned: experts per partition (0: expanded)
     int meta_vec;             // partitioned: metadata rows 16-byte aligned (K % 4 == 0)
+    int meta_rows;            // partitioned: metadata by row workgroups after the token ones
+    const int32_t *part_src;      // partitioned: token of each receive row
+    const int32_t *part_offset;   // partitioned: [P+1] first row of each partition
+    int P;
     int nvec;                 // 16-byte vectors per input row
     int in_row_bytes;
     int out_row_bytes;
@@ -211,6 +215,61 @@ __device__ __forceinline__ void load_pair(const DispatchK &a, int t, int kb, int
     }
 }
 
+// Partitioned metadata in receive order: thread r of these workgroups writes
+// row r (< Rp) for its token part_src[r] and partition q (the last one whose
+// first row is <= r), so consecutive threads write consecutive rows.
+__device__ __forceinline__ void meta_rows(const DispatchK &a, int mb) {
+    const int64_t r = (int64_t)mb * kBlock + threadIdx.x;
+    const int rp = a.part_offset[a.P];
+    if (r >= rp || r >= a.recv_rows) return;
+    const int t = a.part_src[r];
+    int lo = 0, hi = a.P - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.part_offset[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    const int q = lo, K = a.K;
+    const int64_t *ids = a.idx + (int64_t)t * K;
+    const float *ws = a.w ? a.w + (int64_t)t * K : nullptr;
+    for (int k = 0; k < K; k += 4) {
+        int loc[4];
+        float wt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            loc[j] = -1;
+            wt[j] = 0.0f;
+            if (k + j < K) {
+                const int64_t e = ids[k + j];
+                if (e >= 0 && e < a.E && e / a.m == q) {
+                    loc[j] = (int)(e - (int64_t)q * a.m);
+                    wt[j] = ws ? ws[k + j] : 1.0f;
+                }
+            }
+        }
+        if (a.meta_vec && k + 4 <= K) {
+            if (a.recv_idx) {
+                ep_u32x4 *p = (ep_u32x4 *)(a.recv_idx + r * K + k);
+                p[0] = ep_u32x4{(uint32_t)loc[0], (uint32_t)(loc[0] >> 31), (uint32_t)loc[1],
+                                (uint32_t)(loc[1] >> 31)};
+                p[1] = ep_u32x4{(uint32_t)loc[2], (uint32_t)(loc[2] >> 31), (uint32_t)loc[3],
+                                (uint32_t)(loc[3] >> 31)};
+            }
+            if (a.recv_wk)
+                *(ep_u32x4 *)(a.recv_wk + r * K + k) =
+                    ep_u32x4{__float_as_uint(wt[0]), __float_as_uint(wt[1]), __float_as_uint(wt[2]),
+                             __float_as_uint(wt[3])};
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (k + j >= K) break;
+                if (a.recv_idx) a.recv_idx[r * K + k + j] = loc[j];
+                if (a.recv_wk) a.recv_wk[r * K + k + j] = wt[j];
+            }
+        }
+    }
+}
+
 // Per-destination bookkeeping, called by every lane of the wave with its
 // destination q (slot -1 when the lane has none): the expanded layout
 // records the pair's weight in its row, the partitioned layout (PART, its
@@ -222,6 +281,7 @@ __device__ __forceinline__ void record_dest(const DispatchK &a, int t, int q, in
         if (slot >= 0 && a.recv_w) a.recv_w[slot] = w;
         return;
     }
+    if (a.meta_rows) return;   // written in receive order by the row workgroups
     for (int kb = 0; kb < a.K; kb += 64) {
         int e;
         float wv;
@@ -261,7 +321,8 @@ __device__ __forceinline__ void pad_rows(const DispatchK &a, int pb) {
 template <int VPL, int MODE, bool PART>
 __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
     if ((int)blockIdx.x >= a.n_tok_blocks) {
-        pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        if (PART && a.meta_rows) meta_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        else pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
         return;
     }
     const int lane = __lane_id();
@@ -377,7 +438,8 @@ __device__ __forceinline__ void load_chunk(const DispatchK &a, int t, int v0, in
 template <int VPL, int MODE, int TPW, bool PART>
 __global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
     if ((int)blockIdx.x >= a.n_tok_blocks) {
-        pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        if (PART && a.meta_rows) meta_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        else pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
         return;
     }
     const int lane = __lane_id();
@@ -469,7 +531,12 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
         waves = (int64_t)k.n_groups * k.wpr;
     }
     k.n_tok_blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
-    const int64_t grid = (int64_t)k.n_tok_blocks + (int64_t)k.E * k.pad_slices;
+    int64_t grid = (int64_t)k.n_tok_blocks + (int64_t)k.E * k.pad_slices;
+    if (k.meta_rows) {   // the partitioned layout has no padding: these follow the token blocks
+        int64_t rows = (int64_t)k.T * k.P;
+        if (rows > k.recv_rows) rows = k.recv_rows;
+        grid = (int64_t)k.n_tok_blocks + (rows + kBlock - 1) / kBlock;
+    }
     if (grid == 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     switch (mode) {
@@ -505,6 +572,10 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     k.recv_idx = a.recv_idx;
     k.recv_wk = a.recv_wk;
     k.meta_vec = a.K % 4 == 0 && ((uintptr_t)a.recv_idx & 15) == 0 && ((uintptr_t)a.recv_wk & 15) == 0;
+    k.P = a.P;
+    k.part_src = a.part_src;
+    k.part_offset = a.part_offset;
+    k.meta_rows = a.partitioned && a.part_src && a.part_offset && (a.recv_idx || a.recv_wk);
     if (a.partitioned) k.dst = a.token_slot;
     if (a.mode == kModeCopy16) {
         k.in_row_bytes = k.out_row_bytes = a.hidden * 2;

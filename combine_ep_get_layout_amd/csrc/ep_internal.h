@@ -55,6 +55,8 @@ struct DispatchArgs {
     const int64_t *topk_idx;       // [T*K]
     int64_t *recv_idx;             // [rows*K] or NULL
     float *recv_wk;                // [rows*K] or NULL
+    const int32_t *part_src;       // [T*P] token of each receive row, or NULL
+    const int32_t *part_offset;    // [P+1]
 };
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream);

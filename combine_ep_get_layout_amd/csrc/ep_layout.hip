@@ -81,6 +81,7 @@ struct SlotsArgs {
     const uint64_t *tok_mask;
     int32_t *part_offset_out;   // [P+1] or NULL
     int32_t *token_slot_out;    // [T*P] or NULL
+    int32_t *part_src_out;      // [T*P] token of each partition row, or NULL (needs token_slot)
     int32_t *group_out;         // [NG] or NULL
     int32_t *count_out;
     int32_t *offset_out;
@@ -435,8 +436,10 @@ __device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_flags,
             const int bit = (int)((tmask >> q) & 1ull);
             const uint64_t b = __ballot(bit);
             const int rank = __popcll(b & lanes_below());
-            if (tid < ntok)
-                row[q] = bit ? s_poff[q] + s_base[E + q] + s_wq[w * P + q] + rank : -1;
+            const int slot = s_poff[q] + s_base[E + q] + s_wq[w * P + q] + rank;
+            if (tid < ntok) row[q] = bit ? slot : -1;
+            // the inverse map: a wave's tokens of one partition take consecutive rows
+            if (tid < ntok && bit && a.part_src_out) a.part_src_out[slot] = t0 + tid;
         }
     }
 
@@ -613,6 +616,7 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     sa.tok_mask = ca.tok_mask;
     sa.part_offset_out = lay->partition_offset;
     sa.token_slot_out = lay->token_slot;
+    sa.part_src_out = lay->token_slot ? lay->partition_src : nullptr;
     sa.group_out = lay->num_tokens_per_group;
     sa.count_out = lay->num_tokens_per_expert;
     sa.offset_out = lay->expert_offset;

@@ -104,6 +104,8 @@ typedef struct ep_layout {
     int32_t *token_slot;                /* [T*P] row of (t, q) or -1; needs P <= 64  */
     int32_t *num_tokens_per_group;      /* [P/G] tokens reaching any partition of    */
                                         /*       the group (num_tokens_per_rdma_rank) */
+    int32_t *partition_src;             /* [T*P] token of partition row r (r < Rp):  */
+                                        /*       the inverse of token_slot; needs it */
 } ep_layout;
 
 /* Bytes of device workspace ep_get_layout needs for these params (host call,
@@ -224,6 +226,9 @@ int ep_combine(const void *y, int32_t hidden, int64_t num_y_rows,
  *                       (the expert id local to the partition), else -1.
  *   recv_topk_weights   device float [num_recv_rows, K] or NULL: w[t,k] (1 when
  *                       topk_weights is NULL) for local pairs, else 0.
+ * With layout->partition_src set, these two are written row by row in
+ * receive order (coalesced); without it, by the token's wave at scattered
+ * rows (the same values). 
  * Receive rows are [partition_offset[q], partition_offset[q+1]) for partition
  * q, tokens ascending; there is no padding.  Errors as ep_dispatch;
  * EP_ERR_UNSUPPORTED when P > EP_MAX_SLOT_PARTITIONS. */

@@ -269,7 +269,7 @@ def bf16_to_float(bits):
 def partition_layout(topk_idx, num_experts, num_partitions, partitions_per_group=None):
     """Non-expanded (per-rank) receive layout.  Returns a Layout dict with
     in_part [T,P], tok_per_part [P], part_offset [P+1], token_slot [T,P],
-    tok_per_group [P/G], Rp."""
+    tok_per_group [P/G], part_src [Rp] (the token of each row), Rp."""
     lib = _load()
     idx = _c(topk_idx, np.int64)
     T, K = idx.shape
@@ -280,15 +280,16 @@ def partition_layout(topk_idx, num_experts, num_partitions, partitions_per_group
     off = np.zeros(P + 1, np.int32)
     slot = np.zeros(max(T * P, 1), np.int32)
     tpg = np.zeros(max(P // G, 1), np.int32)
+    src = np.full(max(T * P, 1), -1, np.int32)
     Rp = ctypes.c_int64(0)
     rc = lib.oracle_partition_layout(_p(idx), _i64(T), _i64(K), _i64(E), _i64(P), _i64(G),
-                                     _p(in_part), _p(tpp), _p(off), _p(slot), _p(tpg),
+                                     _p(in_part), _p(tpp), _p(off), _p(slot), _p(tpg), _p(src),
                                      ctypes.byref(Rp))
     if rc != 0:
         raise ValueError("oracle_partition_layout: invalid arguments")
     return Layout(in_part=in_part[:T * P].reshape(T, P), tok_per_part=tpp, part_offset=off,
                   token_slot=slot[:T * P].reshape(T, P), tok_per_group=tpg[:P // G],
-                  Rp=int(Rp.value), P=P, E=E)
+                  part_src=src[:int(Rp.value)], Rp=int(Rp.value), P=P, E=E)
 
 
 def dispatch_partitioned(x_rows, topk_idx, play, topk_weights=None, x_scales=None,

@@ -462,7 +462,7 @@ void oracle_div_f32_n(const float *a, const float *b, int64_t n, float *out)
 int oracle_partition_layout(const int64_t *idx, int64_t T, int64_t K, int64_t E, int64_t P,
                             int64_t G, uint8_t *in_part, int32_t *tok_per_part,
                             int32_t *part_offset, int32_t *token_slot,
-                            int32_t *tok_per_group, int64_t *Rp_out)
+                            int32_t *tok_per_group, int32_t *part_src, int64_t *Rp_out)
 {
     if (T < 0 || K < 1 || E < 1 || P < 1 || E % P != 0 || G < 1 || P % G != 0) return OR_EINVAL;
     int64_t m = E / P;
@@ -487,8 +487,11 @@ int oracle_partition_layout(const int64_t *idx, int64_t T, int64_t K, int64_t E,
     int32_t *cursor = (int32_t *)calloc((size_t)P, sizeof(int32_t));
     if (!cursor) return OR_EINVAL;
     for (int64_t t = 0; t < T; ++t)
-        for (int64_t q = 0; q < P; ++q)
+        for (int64_t q = 0; q < P; ++q) {
             token_slot[t * P + q] = in_part[t * P + q] ? part_offset[q] + cursor[q]++ : -1;
+            /* the inverse: the token each partition row holds */
+            if (part_src && token_slot[t * P + q] >= 0) part_src[token_slot[t * P + q]] = (int32_t)t;
+        }
     free(cursor);
     *Rp_out = part_offset[P];
     return OR_OK;

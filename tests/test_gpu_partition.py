@@ -56,6 +56,7 @@ def test_partition_layout_parity(gpu, name, T, K, E, P, G):
     np.testing.assert_array_equal(lay.token_slot.cpu().numpy(), ref.token_slot)
     np.testing.assert_array_equal(lay.num_tokens_per_group.cpu().numpy(), ref.tok_per_group)
     assert lay.num_partition_rows() == ref.Rp
+    np.testing.assert_array_equal(lay.partition_src.cpu().numpy()[:ref.Rp], ref.part_src)
     # the expanded layout beside it is unchanged
     exp = oracle.get_layout(w.topk_idx, E, 1, P)
     np.testing.assert_array_equal(lay.dst_slot.cpu().numpy(), exp.dst)
@@ -93,11 +94,14 @@ def test_partition_layout_with_capacity(gpu):
     ("prefill", 70, 30, 512, 16, 256),      # K % 4 != 0: metadata by single stores
 ])
 @pytest.mark.parametrize("weighted", [True, False])
-def test_dispatch_partitioned_parity(gpu, mode, name, T, K, E, P, H, weighted):
-    announce("dispatch_partitioned", mode, name, T, K, E, P, H, weighted)
+@pytest.mark.parametrize("row_order", [True, False])
+def test_dispatch_partitioned_parity(gpu, mode, name, T, K, E, P, H, weighted, row_order):
+    announce("dispatch_partitioned", mode, name, T, K, E, P, H, weighted, row_order)
     w = ep_inputs.make_workload(name, seed=1, T=T, K=K, E=E, H=H,
                                 **({} if name == "tiny" else {"A": 1}))
     lay, ref = _layouts(gpu, w.topk_idx, E, P, 0)
+    if not row_order:
+        lay.partition_src = None    # metadata written by the token waves instead
     wt = w.topk_weights if weighted else None
     wt_d = to_dev(wt) if weighted else None
     idx_d = to_dev(w.topk_idx)

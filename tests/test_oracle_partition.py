@@ -31,6 +31,7 @@ def test_partition_layout_brute_force(T, K, E, P, G):
         np.testing.assert_array_equal(o.token_slot, np.array(b["token_slot"]).reshape(T, P))
         np.testing.assert_array_equal(o.tok_per_part, b["tok_per_part"])
         np.testing.assert_array_equal(o.tok_per_group, b["tok_per_group"])
+        np.testing.assert_array_equal(o.part_src, [t for q in range(P) for t in b["members"][q]])
 
 
 def test_partition_layout_rust_page_examples():
