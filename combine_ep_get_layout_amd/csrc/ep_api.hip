@@ -11,6 +11,7 @@
 namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 int to_status(hipError_t e) {
     if (e == hipSuccess) return EP_OK;
@@ -114,6 +115,9 @@ static int dispatch_io(int x_dtype, const void *x, const void *x_scales, int rec
         if (*mode == 2 && scale_group == hidden && hidden > 16 * 64 * 8) return EP_ERR_UNSUPPORTED;
         if (!recv_scales && num_recv_rows > 0) return EP_ERR_INVALID_ARG;
         if (*mode == 1 && !x_scales && T > 0) return EP_ERR_INVALID_ARG;
+        // fp32 scales are written (and, for a copy, read) as whole floats
+        if (*fmt != 2 && !aligned4(recv_scales)) return EP_ERR_INVALID_ARG;
+        if (*mode == 1 && *fmt != 2 && !aligned4(x_scales)) return EP_ERR_INVALID_ARG;
     }
     if (T > 0 && (!x || !aligned16(x))) return EP_ERR_INVALID_ARG;
     if (num_recv_rows > 0 && (!recv_x || !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
@@ -304,6 +308,7 @@ int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group
     if (group == hidden && hidden > 16 * 64 * 8) return EP_ERR_UNSUPPORTED;
     if (num_tokens == 0) return EP_OK;
     if (!x || !x_fp8 || !scales || !aligned16(x) || !aligned16(x_fp8)) return EP_ERR_INVALID_ARG;
+    if (out_dtype != EP_DTYPE_FP8_E4M3_UE8M0 && !aligned4(scales)) return EP_ERR_INVALID_ARG;
     return to_status(ep::launch_cast_fp8(x, num_tokens, hidden, group, scale_fmt_of(out_dtype),
                                          x_fp8, scales, (hipStream_t)stream));
 }

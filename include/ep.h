@@ -161,7 +161,7 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,
  *   x            device [T, hidden]: bf16 (x_dtype EP_DTYPE_BF16) or e4m3 codes
  *                (one of the EP_DTYPE_FP8_* types); 16-byte aligned.
  *   x_scales     device [T, hidden/scale_group] when x is fp8, else NULL:
- *                float, or uint8 for EP_DTYPE_FP8_E4M3_UE8M0.
+ *                float (4-byte aligned), or uint8 for EP_DTYPE_FP8_E4M3_UE8M0.
  *   recv_dtype   == x_dtype, or an fp8 type with bf16 x: the rows are cast
  *                on the fly, exactly as ep_cast_fp8 to that type followed by
  *                an fp8 dispatch would do.
@@ -172,8 +172,8 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,
  *   topk_weights device float [T, K] or NULL.
  *   params, layout  as produced by ep_get_layout for the same routing.
  *   recv_x       device [num_recv_rows, hidden] of recv_dtype; 16-byte aligned.
- *   recv_scales  device [num_recv_rows, hidden/G] when recv is fp8: float,
- *                or uint8 for EP_DTYPE_FP8_E4M3_UE8M0.
+ *   recv_scales  device [num_recv_rows, hidden/G] when recv is fp8: float
+ *                (4-byte aligned), or uint8 for EP_DTYPE_FP8_E4M3_UE8M0.
  *   recv_topk_weights device float [num_recv_rows] or NULL: weight of the pair
  *                in each row (1 when topk_weights is NULL), 0 for padding rows.
  *   num_recv_rows rows allocated for recv_x / recv_scales / recv_topk_weights;
@@ -270,7 +270,7 @@ int ep_combine_reduced(const void *y, int32_t hidden, int64_t num_y_rows, const 
  *   out_dtype EP_DTYPE_FP8_E4M3, EP_DTYPE_FP8_E4M3_POW2 or
  *             EP_DTYPE_FP8_E4M3_UE8M0 (else EP_ERR_INVALID_ARG).
  *   x_fp8     device uint8 [T, hidden], 16-byte aligned (e4m3fn codes).
- *   scales    device [T, hidden/G]: float, or uint8 for UE8M0.
+ *   scales    device [T, hidden/G]: float (4-byte aligned), or uint8 for UE8M0.
  * amax = max |x| over the group; s = max(amax, 1e-4f) / 448 (fp32, nearest),
  * rounded up to a power of two for POW2 / UE8M0; code = e4m3_rne(x / s)
  * (fp32 nearest division, ties to even, sign kept on underflow).

@@ -107,6 +107,9 @@ def test_dispatch_rejects_bad_arguments():
     assert call(xd=f8, rd=bf) == _abi.EP_ERR_INVALID_ARG
     assert call(rd=7, H=128, rs=16) == _abi.EP_ERR_INVALID_ARG           # unknown dtype
     assert call(rows=-1) == _abi.EP_ERR_INVALID_ARG
+    # float scale rows must be 4-byte aligned
+    assert call(rd=f8, H=128, rs=18) == _abi.EP_ERR_INVALID_ARG
+    assert call(xd=f8, rd=f8, H=128, xs=ctypes.c_void_p(18), rs=16) == _abi.EP_ERR_INVALID_ARG
 
 
 def test_combine_and_cast_reject_bad_arguments():
@@ -129,6 +132,8 @@ def test_combine_and_cast_reject_bad_arguments():
     assert lib.ep_cast_fp8(ctypes.c_void_p(16), 4, 128, 128, _abi.EP_DTYPE_BF16,
                            ctypes.c_void_p(16), ctypes.c_void_p(16), None) == _abi.EP_ERR_INVALID_ARG
     assert lib.ep_cast_fp8(ctypes.c_void_p(16), 0, 128, 128, f8, None, None, None) == _abi.EP_OK
+    assert lib.ep_cast_fp8(ctypes.c_void_p(16), 4, 128, 128, f8, ctypes.c_void_p(16),
+                           ctypes.c_void_p(18), None) == _abi.EP_ERR_INVALID_ARG   # float scales
 
 
 def test_partition_layout_limits():
