@@ -86,3 +86,51 @@ def test_full_decode_zero_padding(gpu):
     y = ep_inputs.make_y(w.rng, ref.R, w.hidden)
     out, _ = gpu.ep_combine(bf16_to_dev(y), lay, to_dev(w.topk_weights))
     np.testing.assert_array_equal(bf16_bits(out), oracle.combine_f32(y, ref.dst, w.topk_weights))
+
+
+def test_full_skewed_partitioned_legs(gpu):
+    """The skewed workload's partition layout (compared in full), its
+    dispatch (rows on sampled tokens, per-row routing metadata in full) and
+    combine, and the two-level combine on the expanded layout, in the calls
+    the benchmark times."""
+    w = ep_inputs.make_workload("skewed")
+    T, H, E, K, P, A = (w.num_tokens, w.hidden, w.num_experts, w.num_topk, w.num_partitions,
+                        w.expert_alignment)
+    idx = to_dev(w.topk_idx)
+    wts = to_dev(w.topk_weights)
+    announce("full skewed partition layout")
+    pl = gpu.ep_get_layout(idx, E, A, P, w.capacity, partition_layout=True)
+    ref = oracle.partition_layout(w.topk_idx, E, P)
+    np.testing.assert_array_equal(pl.token_slot.cpu().numpy(), ref.token_slot)
+    np.testing.assert_array_equal(pl.partition_offset.cpu().numpy(), ref.part_offset)
+    np.testing.assert_array_equal(pl.partition_src[:ref.Rp].cpu().numpy(), ref.part_src)
+    assert pl.num_partition_rows() == ref.Rp
+    announce("full skewed dispatch_partitioned")
+    recv, _, ri, rw = gpu.ep_dispatch_partitioned(bf16_to_dev(w.x), pl, idx, wts,
+                                                  num_recv_rows=ref.Rp)
+    toks = _sample(T)
+    for t in toks:
+        slots = ref.token_slot[t][ref.token_slot[t] >= 0]
+        got = bf16_bits(recv[torch.from_numpy(slots.astype(np.int64)).to(recv.device)])
+        np.testing.assert_array_equal(got, np.broadcast_to(w.x[t], got.shape))
+    # metadata from the oracle with one-channel rows (the row bytes are checked above)
+    _, _, ri_ref, rw_ref = oracle.dispatch_partitioned(np.zeros((T, 1), np.uint16), w.topk_idx,
+                                                       ref, w.topk_weights)
+    np.testing.assert_array_equal(ri.cpu().numpy(), ri_ref)
+    np.testing.assert_array_equal(rw.cpu().numpy(), rw_ref)
+    del recv, ri, rw
+    announce("full skewed combine_partitioned")
+    y = _tiled_y(w.rng, ref.Rp, H)
+    out = gpu.ep_combine_partitioned(bf16_to_dev(y), pl)
+    np.testing.assert_array_equal(bf16_bits(out)[toks],
+                                  oracle.combine_partitioned_f32(y, ref.token_slot, tokens=toks))
+    del y, out
+    announce("full skewed combine_reduced")
+    lay = gpu.ep_get_layout(idx, E, A, P)
+    exp = oracle.get_layout(w.topk_idx, E, A, P)
+    y = _tiled_y(w.rng, exp.R, H)
+    out = gpu.ep_combine_reduced(bf16_to_dev(y), lay, idx, wts)
+    np.testing.assert_array_equal(
+        bf16_bits(out)[toks],
+        oracle.combine_reduced_f32(y, w.topk_idx, exp.dst, E, P, w.topk_weights, tokens=toks))
+    assert pl.check() == 0 and lay.check() == 0
