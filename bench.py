@@ -106,10 +106,16 @@ def R_of(lay):
     return int(lay.expert_offset[-1].item())
 
 
-def other_workloads(ep, torch, dev, steps):
+def other_workloads(ep, torch, dev, steps, cold_iters=0):
     """Per-operation timings for the fp8, decode, skewed and tiny workloads
-    (K back-to-back launches between two events; algorithmic bytes per op)."""
+    (K back-to-back launches between two events; algorithmic bytes per op).
+    With cold_iters > 0 each operation is also timed alone that many times
+    after a 768 MiB write that evicts L2 and the memory-side cache (median in
+    cold_us): back to back, an operation whose buffers fit that 256 MB cache
+    finds them there."""
     import ep_inputs
+
+    flush = torch.empty(768 << 20, dtype=torch.uint8, device=dev) if cold_iters > 0 else None
 
     def per_op(fn, nbytes, T):
         fn()
@@ -126,6 +132,22 @@ def other_workloads(ep, torch, dev, steps):
         if nbytes:
             r["GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
             r["hbm_frac"] = round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        if flush is not None:
+            pairs = []
+            for _ in range(cold_iters):
+                flush.fill_(1)
+                c0 = torch.cuda.Event(enable_timing=True)
+                c1 = torch.cuda.Event(enable_timing=True)
+                c0.record()
+                fn()
+                c1.record()
+                pairs.append((c0, c1))
+            torch.cuda.synchronize()
+            cus = float(np.median([a.elapsed_time(b) * 1e3 for a, b in pairs]))
+            r["cold_us"] = round(cus, 2)
+            if nbytes:
+                r["cold_GBps"] = round(nbytes / (cus * 1e-6) / 1e9, 1)
+                r["cold_hbm_frac"] = round(nbytes / (cus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         return r
 
     out = {}
@@ -378,7 +400,8 @@ def main():
     if not args.no_other_workloads:
         del recv, y
         torch.cuda.empty_cache()
-        res["other_workloads"] = other_workloads(ep, torch, dev, args.steps)
+        res["other_workloads"] = other_workloads(ep, torch, dev, args.steps,
+                                                 0 if args.no_cold else min(args.steps, 20))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)
