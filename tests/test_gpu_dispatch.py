@@ -74,6 +74,56 @@ def test_dispatch_fixed_capacity_decode_full(gpu):
     np.testing.assert_array_equal(rw.cpu().numpy(), exp_w)
 
 
+@pytest.mark.parametrize("mode", ["bf16", "fp8", "fused"])
+@pytest.mark.parametrize("short", [False, True])
+def test_dispatch_capacity_mostly_padding(gpu, mode, short):
+    """Fixed capacity with at most one row in eight used (the region is
+    zero-filled first, then the token rows written): every byte of rows,
+    scale rows and weights against the oracle over sentinel-filled buffers,
+    with the full buffer and with one shorter than E*C."""
+    announce("dispatch capacity mostly padding", mode, short)
+    w = ep_inputs.make_workload("decode", T=37, H=1040, E=64, K=4, C=32)
+    lay, ref = _setup(gpu, w)
+    rows = lay.max_recv_rows // 2 if short else lay.max_recv_rows
+    H, G = w.hidden, 16
+    rw = torch.full((rows,), 7.0, dtype=torch.float32, device="cuda:0")
+    if mode == "bf16":
+        recv = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda:0")
+        recv.view(torch.int16).fill_(SENTINEL)
+        recv, _, rw = gpu.ep_dispatch(bf16_to_dev(w.x), lay, to_dev(w.topk_weights),
+                                      num_recv_rows=rows, zero_padding=True, out=(recv, None, rw))
+        exp, _, exp_w = oracle.dispatch(w.x, ref, w.topk_weights, zero_padding=True)
+        np.testing.assert_array_equal(bf16_bits(recv), exp[:rows])
+    else:
+        q_ref, s_ref = oracle.cast_fp8(w.x, G)
+        recv = torch.empty((rows, H), dtype=torch.float8_e4m3fn, device="cuda:0")
+        recv.view(torch.uint8).fill_(0x5A)
+        rs = torch.full((rows, H // G), 3.0, dtype=torch.float32, device="cuda:0")
+        src = (bf16_to_dev(w.x) if mode == "fused"
+               else (fp8_to_dev(q_ref), to_dev(s_ref)))
+        recv, rs, rw = gpu.ep_dispatch(src, lay, to_dev(w.topk_weights), recv_fp8=mode == "fused",
+                                       scale_group=G, num_recv_rows=rows, zero_padding=True,
+                                       out=(recv, rs, rw))
+        exp, exp_s, exp_w = oracle.dispatch(q_ref, ref, w.topk_weights, x_scales=s_ref,
+                                            zero_padding=True)
+        np.testing.assert_array_equal(fp8_bits(recv), exp[:rows])
+        np.testing.assert_array_equal(rs.cpu().numpy().view(np.uint32),
+                                      exp_s[:rows].view(np.uint32))
+    np.testing.assert_array_equal(rw.cpu().numpy(), exp_w[:rows])
+    status = int(lay.status.item())
+    assert bool(status & oracle.RECV_OVERFLOW) == (short and (ref.dst >= rows).any())
+
+
+def test_dispatch_capacity_no_tokens(gpu):
+    """T = 0 with a fixed capacity and zero padding: every row is padding."""
+    lay = gpu.ep_get_layout(torch.zeros((0, 8), dtype=torch.int64, device="cuda:0"), 16, 1, 1, 8)
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda:0")
+    recv = torch.empty((lay.max_recv_rows, 64), dtype=torch.bfloat16, device="cuda:0")
+    recv.view(torch.int16).fill_(SENTINEL)
+    recv, _, _ = gpu.ep_dispatch(x, lay, None, zero_padding=True, out=(recv, None, None))
+    assert (bf16_bits(recv) == 0).all()
+
+
 def test_dispatch_capacity_overflow_drops_pairs(gpu):
     w = ep_inputs.make_workload("decode", H=128)
     lay, ref = _setup(gpu, w, C=4)
