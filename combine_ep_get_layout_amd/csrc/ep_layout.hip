@@ -23,12 +23,12 @@
 //          per-expert counts and offsets, the partition totals, the
 //          cumulative stats and the status word.
 //
-// When the tiles fit on the chip at once (the usual case) both phases run in
-// one cooperative launch with a grid barrier between them, so the pair ranks
-// never leave registers.  Otherwise (E above kMaxFusedExperts, a grid too big
-// to be co-resident, or a stream under graph capture) they run as two
-// kernels and the ranks travel through dst_slot, packed as
-// (e << kRankBits) | rank.
+// The phases run as two kernels and the pair ranks travel through dst_slot,
+// packed as (e << kRankBits) | rank.  A very small batch (a few hundred
+// pairs) runs both phases in one 1024-thread workgroup, one launch, with only
+// a workgroup barrier between them and the ranks kept in registers.  A cooperative single launch of every tile with a
+// grid barrier (EP_LAYOUT_FUSED) is kept as an option: it measured slower to
+// launch than the two kernels.
 #include <hip/hip_cooperative_groups.h>
 
 #include "ep_device.h"
@@ -46,8 +46,12 @@ constexpr int kSlotsBlock = 1024;  // slots workgroup, and the fused tiling: 16 
 #endif
 constexpr int kReduceBatch = EP_LAYOUT_RBATCH;   // loads in flight per thread in column_sums
 constexpr int kMaxFusedExperts = 512;
+constexpr int64_t kSinglePairs = 256;   // batches up to this many pairs: one workgroup
 #ifndef EP_LAYOUT_FUSED
 #define EP_LAYOUT_FUSED 0      // cooperative single launch (measured slower to launch)
+#endif
+#ifndef EP_LAYOUT_SINGLE
+#define EP_LAYOUT_SINGLE 1     // batches that fit one workgroup: one launch, no handoff
 #endif
 #ifndef EP_LAYOUT_NT_HANDOFF
 #define EP_LAYOUT_NT_HANDOFF 0  // bit 0: streaming stores of tile rows, bit 1: streaming loads
@@ -516,6 +520,7 @@ __global__ void __launch_bounds__(kSlotsBlock) layout_slots_kernel(SlotsArgs a) 
     slots_phase(a, lds, &s_flags, pv, pidx);
 }
 
+template <bool SINGLE>
 __global__ void __launch_bounds__(kSlotsBlock) layout_fused_kernel(CountArgs ca, SlotsArgs sa) {
     extern __shared__ int32_t lds[];
     __shared__ int32_t s_flag;
@@ -536,7 +541,8 @@ __global__ void __launch_bounds__(kSlotsBlock) layout_fused_kernel(CountArgs ca,
         pv[c] = ok && ex[c] >= 0 ? ((ex[c] << kRankBits) | rank[c]) : -1;
     }
     // Every tile's counts are in memory before any tile reads them.
-    cooperative_groups::this_grid().sync();
+    if (SINGLE) __syncthreads();   // one tile: the workgroup reads back its own row
+    else cooperative_groups::this_grid().sync();
     slots_phase(sa, lds, &s_flag, pv, pidx);
 }
 
@@ -555,13 +561,18 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
     L.max_rows = p->max_recv_rows;
     const int64_t pairs = (int64_t)L.T * L.K;
     L.fused = EP_LAYOUT_FUSED && L.E <= kMaxFusedExperts;
-    L.block = (L.fused || (EP_LAYOUT_WAVES == 16 && L.E <= kMaxFusedExperts)) ? kSlotsBlock
-                                                                          : kCountBlock;
+    // A batch of at most kSinglePairs pairs is one tile: both phases run in
+    // one workgroup, in one launch.  (Measured: 12.3 -> 11.1 µs at 128 pairs;
+    // already slower than the two kernels at 1,024 pairs, 13.1 -> 15.6 µs.)
+    L.single = EP_LAYOUT_SINGLE && pairs > 0 && L.E <= kMaxFusedExperts &&
+               pairs <= kSinglePairs && L.T <= kSlotsBlock;
+    L.block = (L.single || L.fused || (EP_LAYOUT_WAVES == 16 && L.E <= kMaxFusedExperts))
+                  ? kSlotsBlock : kCountBlock;
     const int64_t per_round = L.block;   // pairs when every wave takes one 64-pair chunk
     // Chunks per wave: enough tiles to spread the count over the chip, few
     // enough that each tile reduces the [tiles, E] count matrix in one or two
     // round trips (16-wave tiles: ~32 of them; 4-wave tiles: ~256).
-    const int64_t target_tiles = L.block == kSlotsBlock ? 32 : 256;
+    const int64_t target_tiles = L.single ? 1 : (L.block == kSlotsBlock ? 32 : 256);
     int64_t cpw = (pairs + target_tiles * per_round - 1) / (target_tiles * per_round);
     cpw = cpw < 1 ? 1 : (cpw > kMaxChunksPerWave ? kMaxChunksPerWave : cpw);
     L.chunks_per_wave = (int)cpw;
@@ -570,6 +581,7 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
     if (tt < 1) return false;
     L.tile_tokens = tt;
     L.num_tiles = L.T > 0 ? (L.T + tt - 1) / tt : 0;
+    L.single = L.single && L.num_tiles == 1;
     const size_t nt = (size_t)(L.num_tiles > 0 ? L.num_tiles : 1);
     L.G = p->partitions_per_group > 0 ? p->partitions_per_group : L.P;
     L.NG = L.P / L.G;
@@ -632,13 +644,18 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
                               (size_t)(kSlotsBlock / 64) * (lay->token_slot ? L.P : 0) + kRedInts) * 4;
     if (lds_count > kMaxLdsBytes || lds_slots > kMaxLdsBytes) return hipErrorInvalidConfiguration;
 
+    if (L.single) {
+        const size_t lds = lds_count > lds_slots ? lds_count : lds_slots;
+        hipLaunchKernelGGL(layout_fused_kernel<true>, dim3(1), dim3(kSlotsBlock), lds, stream, ca, sa);
+        return hipGetLastError();
+    }
     if (L.fused && L.num_tiles > 0) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
             const size_t lds = lds_count > lds_slots ? lds_count : lds_slots;
             void *args[] = {&ca, &sa};
             const hipError_t err = hipLaunchCooperativeKernel(
-                (const void *)layout_fused_kernel, dim3(L.num_tiles), dim3(kSlotsBlock), args,
+                (const void *)layout_fused_kernel<false>, dim3(L.num_tiles), dim3(kSlotsBlock), args,
                 (unsigned)lds, stream);
             if (err == hipSuccess) return hipSuccess;
             (void)hipGetLastError();   // not co-resident: two launches instead
