@@ -54,6 +54,34 @@ def _need_cuda(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check(t: Optional[torch.Tensor], name: str, dtypes, cols=None, min_rows=None, rows=None):
+    """A GPU buffer the kernels will read or write: contiguous, of one of
+    `dtypes`, 2-D with `cols` columns (1-D when cols is None) and `rows` rows
+    exactly or at least `min_rows`.  Catches a buffer the kernels would
+    overrun before anything is launched."""
+    if t is None:
+        return
+    _need_cuda(t, name)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if cols is None:
+        n = t.numel()
+        if (rows is not None and n != rows) or (min_rows is not None and n < min_rows):
+            raise ValueError(f"{name} has {n} elements, needs {rows if rows is not None else min_rows}")
+        return
+    if t.dim() != 2 or t.shape[1] != cols:
+        raise ValueError(f"{name} must be [rows, {cols}], not {list(t.shape)}")
+    if (rows is not None and t.shape[0] != rows) or (min_rows is not None and t.shape[0] < min_rows):
+        raise ValueError(f"{name} has {t.shape[0]} rows, needs "
+                         f"{rows if rows is not None else f'at least {min_rows}'}")
+
+
+_F8 = (torch.float8_e4m3fn, torch.uint8)
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+_I64 = (torch.int64,)
+
+
 def worst_case_recv_rows(num_tokens, num_topk, num_experts, expert_alignment=1, capacity=0) -> int:
     p = LayoutParams(num_tokens, num_topk, num_experts, expert_alignment, 1, capacity, 0, 0)
     return int(load_library().ep_worst_case_recv_rows(ctypes.byref(p)))
@@ -239,13 +267,13 @@ def ep_dispatch(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]], layou
     if fp8_out and recv_s is None:
         recv_s = torch.empty((rows, H // scale_group), dtype=_scale_dtype(scale_fmt), device=dev)
     if topk_weights is not None:
-        _need_cuda(topk_weights, "topk_weights")
-        if topk_weights.dtype != torch.float32:
-            raise ValueError("topk_weights must be float32 [T, K]")
+        _check(topk_weights, "topk_weights", _F32, layout.num_topk, rows=T)
         if recv_w is None:
             recv_w = torch.empty(rows, dtype=torch.float32, device=dev)
-    if recv_x.shape[0] < rows:
-        raise ValueError("recv_x has fewer rows than num_recv_rows")
+    _check(recv_x, "recv_x", _F8 if fp8_out else _BF16, H, min_rows=rows)
+    if fp8_out:
+        _check(recv_s, "recv_scales", (_scale_dtype(scale_fmt),), H // scale_group, min_rows=rows)
+    _check(recv_w, "recv_topk_weights", _F32, min_rows=rows)
     params = layout.params
     ptrs = layout.ptrs()
     rc = lib.ep_dispatch(_ptr(x), x_dtype, _ptr(x_scales), recv_dtype, H, scale_group,
@@ -280,13 +308,13 @@ def ep_combine(y: torch.Tensor, layout: Layout, topk_weights: Optional[torch.Ten
             _need_cuda(b, name)
             if b.dtype != torch.bfloat16 or tuple(b.shape) != (T, H):
                 raise ValueError(f"{name} must be bf16 [T, H]")
-    if topk_weights is not None:
-        _need_cuda(topk_weights, "topk_weights")
+    _check(topk_weights, "topk_weights", _F32, K, rows=T)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check(out, "out", _BF16, H, rows=T)
     cw = None
     if recv_topk_weights is not None:
-        _need_cuda(recv_topk_weights, "recv_topk_weights")
+        _check(recv_topk_weights, "recv_topk_weights", _F32, min_rows=rows)
         cw = torch.empty((T, K), dtype=torch.float32, device=y.device)
     params = layout.params
     ptrs = layout.ptrs()
@@ -314,6 +342,8 @@ def ep_cast_fp8(x: torch.Tensor, group: int = 128,
         s = torch.empty((T, H // group), dtype=_scale_dtype(scale_fmt), device=x.device)
     else:
         q, s = out
+    _check(q, "x_fp8", _F8, H, rows=T)
+    _check(s, "scales", (_scale_dtype(scale_fmt),), H // group, rows=T)
     rc = lib.ep_cast_fp8(_ptr(x), T, H, group, out_dtype, _ptr(q), _ptr(s), _stream(x.device))
     _abi.check("ep_cast_fp8", rc)
     return q, s
@@ -338,6 +368,9 @@ def _x_and_dtypes(x, recv_fp8, scale_group, scale_fmt="fp32"):
         elif scale_fmt == "ue8m0":
             scale_fmt = "fp32"
         d = _fp8_dtype(scale_fmt)
+        if x_scales.dim() != 2 or x_scales.shape[0] != x.shape[0] or x_scales.shape[1] < 1 \
+                or H % x_scales.shape[1] != 0:
+            raise ValueError("x_scales must be [T, H / group]")
         return x, x_scales, H // x_scales.shape[1], d, d, scale_fmt
     if x.dtype != torch.bfloat16:
         raise ValueError("x must be bf16 or fp8")
@@ -366,7 +399,7 @@ def ep_dispatch_partitioned(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Ten
     K = layout.num_topk
     if T != layout.num_tokens:
         raise ValueError("x rows != layout tokens")
-    _need_cuda(topk_idx, "topk_idx")
+    _check(topk_idx, "topk_idx", _I64, K, rows=T)
     rows = T * layout.num_partitions if num_recv_rows is None else int(num_recv_rows)
     dev = x.device
     fp8_out = recv_dtype != _abi.EP_DTYPE_BF16
@@ -381,13 +414,16 @@ def ep_dispatch_partitioned(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Ten
     if recv_i is None:
         recv_i = torch.empty((rows, K), dtype=torch.int64, device=dev)
     if topk_weights is not None:
-        _need_cuda(topk_weights, "topk_weights")
+        _check(topk_weights, "topk_weights", _F32, K, rows=T)
         if recv_w is None:
             recv_w = torch.empty((rows, K), dtype=torch.float32, device=dev)
     else:
         recv_w = None
-    if recv_x.shape[0] < rows or recv_i.shape[0] < rows:
-        raise ValueError("receive buffers have fewer rows than num_recv_rows")
+    _check(recv_x, "recv_x", _F8 if fp8_out else _BF16, H, min_rows=rows)
+    if fp8_out:
+        _check(recv_s, "recv_scales", (_scale_dtype(scale_fmt),), H // scale_group, min_rows=rows)
+    _check(recv_i, "recv_topk_idx", _I64, K, min_rows=rows)
+    _check(recv_w, "recv_topk_weights", _F32, K, min_rows=rows)
     params = layout.params
     ptrs = layout.ptrs()
     rc = lib.ep_dispatch_partitioned(_ptr(x), x_dtype, _ptr(x_scales), recv_dtype, H, scale_group,
@@ -428,6 +464,7 @@ def ep_combine_partitioned(y: torch.Tensor, layout: Layout,
     b0, b1 = _biases(bias, T, H)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check(out, "out", _BF16, H, rows=T)
     params = layout.params
     ptrs = layout.ptrs()
     rc = lib.ep_combine_partitioned(_ptr(y), H, rows, _ptr(b0), _ptr(b1), ctypes.byref(params),
@@ -445,16 +482,16 @@ def ep_combine_reduced(y: torch.Tensor, layout: Layout, topk_idx: torch.Tensor,
     summed in fp32 in partition order and rounded to bf16."""
     lib = load_library()
     _need_cuda(y, "y")
-    _need_cuda(topk_idx, "topk_idx")
     if y.dtype != torch.bfloat16:
         raise ValueError("y must be bf16")
     rows, H = y.shape
-    T = layout.num_tokens
+    T, K = layout.num_tokens, layout.num_topk
+    _check(topk_idx, "topk_idx", _I64, K, rows=T)
     b0, b1 = _biases(bias, T, H)
-    if topk_weights is not None:
-        _need_cuda(topk_weights, "topk_weights")
+    _check(topk_weights, "topk_weights", _F32, K, rows=T)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check(out, "out", _BF16, H, rows=T)
     params = layout.params
     ptrs = layout.ptrs()
     rc = lib.ep_combine_reduced(_ptr(y), H, rows, _ptr(topk_idx), _ptr(topk_weights), _ptr(b0),
