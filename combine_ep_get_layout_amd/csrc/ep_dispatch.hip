@@ -393,10 +393,46 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
                                  // registers allow three per SIMD); 0: one group per wave
 #endif
 
-// All destinations of token t for one row chunk (copy modes).
+// fp8 copy: the token's scale row held in registers across its destinations
+// (element j in lane j % 64, slot j / 64; rows of up to 64 * kScaleRegs
+// scales), loaded together with the row so no destination waits on a load.
+// As raw bits: a 32-bit float, or one UE8M0 byte.
+constexpr int kScaleRegs = 4;
+
+__device__ __forceinline__ bool scales_in_regs(const DispatchK &a) {
+    return a.ng <= 64 * kScaleRegs;
+}
+
+__device__ __forceinline__ void load_scales(const DispatchK &a, int t, int lane,
+                                            uint32_t (&sc)[kScaleRegs]) {
+#pragma unroll
+    for (int i = 0; i < kScaleRegs; ++i) {
+        const int j = i * 64 + lane;
+        sc[i] = 0u;
+        if (j < a.ng)
+            sc[i] = a.scale_fmt == 2 ? (uint32_t)a.x_scales[(int64_t)t * a.ng + j]
+                                     : ((const uint32_t *)a.x_scales)[(int64_t)t * a.ng + j];
+    }
+}
+
+__device__ __forceinline__ void store_scales(const DispatchK &a, int64_t slot, int lane,
+                                             const uint32_t (&sc)[kScaleRegs]) {
+#pragma unroll
+    for (int i = 0; i < kScaleRegs; ++i) {
+        const int j = i * 64 + lane;
+        if (j < a.ng) {
+            if (a.scale_fmt == 2) a.recv_scales[slot * a.ng + j] = (uint8_t)sc[i];
+            else ((uint32_t *)a.recv_scales)[slot * a.ng + j] = sc[i];
+        }
+    }
+}
+
+// All destinations of token t for one row chunk (copy modes); sc holds the
+// token's scale row for the fp8 copy when scales_in_regs.
 template <int VPL, int MODE, bool PART>
 __device__ __forceinline__ void store_token(const DispatchK &a, int t, int ci, int v0, int lane,
-                                            const ep_u32x4 (&v)[VPL]) {
+                                            const ep_u32x4 (&v)[VPL],
+                                            const uint32_t (&sc)[kScaleRegs]) {
     for (int kb = 0; kb < a.nd; kb += 64) {
         int my_slot = -1;
         float my_w = 1.0f;
@@ -419,7 +455,10 @@ __device__ __forceinline__ void store_token(const DispatchK &a, int t, int ci, i
                 const int vi = v0 + i * 64 + lane;
                 if (vi < a.nvec) row_store(dstrow + vi, v[i]);
             }
-            if (MODE == kModeCopyFp8 && ci == 0) copy_scales(a, t, slot, lane);
+            if (MODE == kModeCopyFp8 && ci == 0) {
+                if (scales_in_regs(a)) store_scales(a, slot, lane, sc);
+                else copy_scales(a, t, slot, lane);
+            }
         }
     }
 }
@@ -457,16 +496,25 @@ __global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
     int64_t t = tok(0);
     if (t >= a.T) return;
     ep_u32x4 v0b[VPL], v1b[VPL];
+    uint32_t s0b[kScaleRegs] = {}, s1b[kScaleRegs] = {};
+    const bool regs = MODE == kModeCopyFp8 && ci == 0 && scales_in_regs(a);
     load_chunk<VPL>(a, (int)t, v0, lane, v0b);
+    if (regs) load_scales(a, (int)t, lane, s0b);
     for (int j = 0;; j += 2) {
         int64_t tn = tok(j + 1);
-        if (tn < a.T) load_chunk<VPL>(a, (int)tn, v0, lane, v1b);
-        store_token<VPL, MODE, PART>(a, (int)t, ci, v0, lane, v0b);
+        if (tn < a.T) {
+            load_chunk<VPL>(a, (int)tn, v0, lane, v1b);
+            if (regs) load_scales(a, (int)tn, lane, s1b);
+        }
+        store_token<VPL, MODE, PART>(a, (int)t, ci, v0, lane, v0b, s0b);
         if (tn >= a.T) break;
         t = tn;
         tn = tok(j + 2);
-        if (tn < a.T) load_chunk<VPL>(a, (int)tn, v0, lane, v0b);
-        store_token<VPL, MODE, PART>(a, (int)t, ci, v0, lane, v1b);
+        if (tn < a.T) {
+            load_chunk<VPL>(a, (int)tn, v0, lane, v0b);
+            if (regs) load_scales(a, (int)tn, lane, s0b);
+        }
+        store_token<VPL, MODE, PART>(a, (int)t, ci, v0, lane, v1b, s1b);
         if (tn >= a.T) break;
         t = tn;
     }
