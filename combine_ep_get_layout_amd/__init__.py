@@ -47,6 +47,20 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _launch(name: str, device, fn, *tensors_then_args):
+    """Call entry point `fn` with `device` current (the library launches on the
+    calling thread's current device), after checking that every tensor given
+    before the plain arguments lives on it.  Usage:
+    _launch(name, dev, fn, [tensors...], arg0, arg1, ...)."""
+    tensors, args = tensors_then_args[0], tensors_then_args[1:]
+    for t in tensors:
+        if t is not None and t.device != device:
+            raise ValueError(f"{name}: all tensors must be on {device}, found {t.device}")
+    with torch.cuda.device(device):
+        rc = fn(*args)
+    _abi.check(name, rc)
+
+
 def _need_cuda(t: torch.Tensor, name: str):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
@@ -209,10 +223,11 @@ def ep_get_layout(topk_idx: torch.Tensor, num_experts: int, expert_alignment: in
         if cumulative_expert_stats.dtype != torch.int32 or cumulative_expert_stats.numel() != num_experts:
             raise ValueError("cumulative_expert_stats must be int32 [num_experts]")
     ptrs = layout.ptrs()
-    rc = lib.ep_get_layout(_ptr(topk_idx), ctypes.byref(params), ctypes.byref(ptrs),
-                           _ptr(cumulative_expert_stats), _ptr(layout.workspace),
-                           layout.workspace.numel(), _stream(topk_idx.device))
-    _abi.check("ep_get_layout", rc)
+    _launch("ep_get_layout", topk_idx.device, lib.ep_get_layout,
+            [cumulative_expert_stats, layout.workspace, layout.status],
+            _ptr(topk_idx), ctypes.byref(params), ctypes.byref(ptrs),
+            _ptr(cumulative_expert_stats), _ptr(layout.workspace),
+            layout.workspace.numel(), _stream(topk_idx.device))
     return layout
 
 
@@ -276,11 +291,12 @@ def ep_dispatch(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]], layou
     _check(recv_w, "recv_topk_weights", _F32, min_rows=rows)
     params = layout.params
     ptrs = layout.ptrs()
-    rc = lib.ep_dispatch(_ptr(x), x_dtype, _ptr(x_scales), recv_dtype, H, scale_group,
-                         _ptr(topk_weights), ctypes.byref(params), ctypes.byref(ptrs),
-                         _ptr(recv_x), _ptr(recv_s), _ptr(recv_w), rows,
-                         1 if zero_padding else 0, _stream(dev))
-    _abi.check("ep_dispatch", rc)
+    _launch("ep_dispatch", dev, lib.ep_dispatch,
+            [x_scales, topk_weights, recv_x, recv_s, recv_w, layout.status],
+            _ptr(x), x_dtype, _ptr(x_scales), recv_dtype, H, scale_group,
+            _ptr(topk_weights), ctypes.byref(params), ctypes.byref(ptrs),
+            _ptr(recv_x), _ptr(recv_s), _ptr(recv_w), rows,
+            1 if zero_padding else 0, _stream(dev))
     return recv_x, recv_s, recv_w
 
 
@@ -318,10 +334,11 @@ def ep_combine(y: torch.Tensor, layout: Layout, topk_weights: Optional[torch.Ten
         cw = torch.empty((T, K), dtype=torch.float32, device=y.device)
     params = layout.params
     ptrs = layout.ptrs()
-    rc = lib.ep_combine(_ptr(y), H, rows, _ptr(topk_weights), _ptr(b0), _ptr(b1),
-                        ctypes.byref(params), ctypes.byref(ptrs), _ptr(recv_topk_weights),
-                        _ptr(cw), _ptr(out), _stream(y.device))
-    _abi.check("ep_combine", rc)
+    _launch("ep_combine", y.device, lib.ep_combine,
+            [topk_weights, b0, b1, recv_topk_weights, out, layout.status],
+            _ptr(y), H, rows, _ptr(topk_weights), _ptr(b0), _ptr(b1),
+            ctypes.byref(params), ctypes.byref(ptrs), _ptr(recv_topk_weights),
+            _ptr(cw), _ptr(out), _stream(y.device))
     return out, cw
 
 
@@ -344,8 +361,8 @@ def ep_cast_fp8(x: torch.Tensor, group: int = 128,
         q, s = out
     _check(q, "x_fp8", _F8, H, rows=T)
     _check(s, "scales", (_scale_dtype(scale_fmt),), H // group, rows=T)
-    rc = lib.ep_cast_fp8(_ptr(x), T, H, group, out_dtype, _ptr(q), _ptr(s), _stream(x.device))
-    _abi.check("ep_cast_fp8", rc)
+    _launch("ep_cast_fp8", x.device, lib.ep_cast_fp8, [q, s],
+            _ptr(x), T, H, group, out_dtype, _ptr(q), _ptr(s), _stream(x.device))
     return q, s
 
 
@@ -426,11 +443,12 @@ def ep_dispatch_partitioned(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Ten
     _check(recv_w, "recv_topk_weights", _F32, K, min_rows=rows)
     params = layout.params
     ptrs = layout.ptrs()
-    rc = lib.ep_dispatch_partitioned(_ptr(x), x_dtype, _ptr(x_scales), recv_dtype, H, scale_group,
-                                     _ptr(topk_idx), _ptr(topk_weights), ctypes.byref(params),
-                                     ctypes.byref(ptrs), _ptr(recv_x), _ptr(recv_s), _ptr(recv_i),
-                                     _ptr(recv_w), rows, _stream(dev))
-    _abi.check("ep_dispatch_partitioned", rc)
+    _launch("ep_dispatch_partitioned", dev, lib.ep_dispatch_partitioned,
+            [x_scales, topk_idx, topk_weights, recv_x, recv_s, recv_i, recv_w, layout.status],
+            _ptr(x), x_dtype, _ptr(x_scales), recv_dtype, H, scale_group,
+            _ptr(topk_idx), _ptr(topk_weights), ctypes.byref(params),
+            ctypes.byref(ptrs), _ptr(recv_x), _ptr(recv_s), _ptr(recv_i),
+            _ptr(recv_w), rows, _stream(dev))
     return recv_x, recv_s, recv_i, recv_w
 
 
@@ -467,9 +485,10 @@ def ep_combine_partitioned(y: torch.Tensor, layout: Layout,
     _check(out, "out", _BF16, H, rows=T)
     params = layout.params
     ptrs = layout.ptrs()
-    rc = lib.ep_combine_partitioned(_ptr(y), H, rows, _ptr(b0), _ptr(b1), ctypes.byref(params),
-                                    ctypes.byref(ptrs), _ptr(out), _stream(y.device))
-    _abi.check("ep_combine_partitioned", rc)
+    _launch("ep_combine_partitioned", y.device, lib.ep_combine_partitioned,
+            [b0, b1, out, layout.status],
+            _ptr(y), H, rows, _ptr(b0), _ptr(b1), ctypes.byref(params),
+            ctypes.byref(ptrs), _ptr(out), _stream(y.device))
     return out
 
 
@@ -494,8 +513,9 @@ def ep_combine_reduced(y: torch.Tensor, layout: Layout, topk_idx: torch.Tensor,
     _check(out, "out", _BF16, H, rows=T)
     params = layout.params
     ptrs = layout.ptrs()
-    rc = lib.ep_combine_reduced(_ptr(y), H, rows, _ptr(topk_idx), _ptr(topk_weights), _ptr(b0),
-                                _ptr(b1), ctypes.byref(params), ctypes.byref(ptrs), _ptr(out),
-                                _stream(y.device))
-    _abi.check("ep_combine_reduced", rc)
+    _launch("ep_combine_reduced", y.device, lib.ep_combine_reduced,
+            [topk_idx, topk_weights, b0, b1, out, layout.status],
+            _ptr(y), H, rows, _ptr(topk_idx), _ptr(topk_weights), _ptr(b0),
+            _ptr(b1), ctypes.byref(params), ctypes.byref(ptrs), _ptr(out),
+            _stream(y.device))
     return out
