@@ -45,6 +45,10 @@ def test_layout_workloads_full_size(gpu, name):
     (2049, 1, 7, 5, 7, 0.0),       # K = 1, odd E
     (300, 64, 512, 1, 2, 0.5),     # K = 64: a token fills a whole wave chunk
     (40, 200, 1024, 7, 8, 0.2),    # K > 64
+    (9, 256, 4096, 3, 64, 0.1),    # largest K with the largest E
+    (1, 256, 512, 1, 8, 0.0),      # largest K in one workgroup (256 pairs)
+    (32, 8, 512, 1, 4, 0.05),      # 256 pairs, the largest one-workgroup batch
+    (33, 8, 512, 1, 4, 0.05),      # 264 pairs: the two-kernel path again
 ])
 def test_layout_shapes(gpu, T, K, E, A, P, drop):
     rng = ep_inputs.make_rng(T * 7 + K)
