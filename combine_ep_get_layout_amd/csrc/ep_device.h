@@ -128,15 +128,19 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
 #endif
 }
 
-// 8 bf16 values / s -> 8 e4m3 codes packed little-endian in two dwords.
-__device__ __forceinline__ ep_u32x2 encode8(ep_u32x4 v, float s) {
-    const float y = 1.0f / s;
+// 8 bf16 values / s -> 8 e4m3 codes packed little-endian in two dwords,
+// given y = RN(1/s).
+__device__ __forceinline__ ep_u32x2 encode8_y(ep_u32x4 v, float s, float y) {
     ep_u32x2 r;
     r.x = pack4_e4m3(div_rn(bf16_lo(v.x), s, y), div_rn(bf16_hi(v.x), s, y),
                      div_rn(bf16_lo(v.y), s, y), div_rn(bf16_hi(v.y), s, y));
     r.y = pack4_e4m3(div_rn(bf16_lo(v.z), s, y), div_rn(bf16_hi(v.z), s, y),
                      div_rn(bf16_lo(v.w), s, y), div_rn(bf16_hi(v.w), s, y));
     return r;
+}
+
+__device__ __forceinline__ ep_u32x2 encode8(ep_u32x4 v, float s) {
+    return encode8_y(v, s, 1.0f / s);
 }
 
 #ifndef EP_GROUP_MAX_DPP

@@ -29,6 +29,9 @@
 #ifndef EP_CAST_VPL
 #define EP_CAST_VPL 4
 #endif
+#ifndef EP_CAST_PAIRS
+#define EP_CAST_PAIRS 1          // cast without a layout: two adjacent vectors per lane
+#endif
 #ifndef EP_DISPATCH_TPW
 #define EP_DISPATCH_TPW 2        // consecutive tokens per group in the copy modes (2: measured best)
 #endif
@@ -565,6 +568,38 @@ hipError_t launch_zero_fill(const DispatchK &k, int64_t rows, hipStream_t stream
     return hipGetLastError();
 }
 
+// Cast without a layout, groups narrower than the row.  Lane l of a wave
+// holds the adjacent vectors 2l and 2l+1 of its 128-vector chunk: 16
+// channels of one group, so a lane derives one scale and one reciprocal for
+// its 16 values (not one per vector), and its 16 codes leave in one 16-byte
+// store (the wave writes 1 KB contiguous).  nvec is even (H % 16 == 0) and a
+// multiple of the vectors per group, so a group is wholly inside the row or
+// wholly past its end.
+__global__ void __launch_bounds__(kBlock) cast_pairs_kernel(DispatchK a) {
+    const int lane = __lane_id();
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int t = (int)(gw / a.wpr);
+    const int c = (int)(gw - (int64_t)t * a.wpr);
+    if (t >= a.T) return;
+    const int vi = c * 128 + 2 * lane;
+    const bool on = vi < a.nvec;
+    const ep_u32x4 *src = (const ep_u32x4 *)(a.x + (int64_t)t * a.in_row_bytes);
+    ep_u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+    if (on) {
+        v0 = load_nt(src + vi);
+        v1 = load_nt(src + vi + 1);
+    }
+    const int gl = a.group_lanes >> 1;    // lanes per group here: G / 16
+    const float s = group_scale(a, group_max(fmaxf(amax8(v0), amax8(v1)), gl));
+    const float y = 1.0f / s;
+    const ep_u32x2 e0 = encode8_y(v0, s, y), e1 = encode8_y(v1, s, y);
+    if (on) {
+        row_store((ep_u32x4 *)(a.recv + (int64_t)t * a.out_row_bytes) + (vi >> 1),
+                  ep_u32x4{e0.x, e0.y, e1.x, e1.y});
+        if ((vi % a.group_lanes) == 0) store_scale(a, t, vi / a.group_lanes, s);
+    }
+}
+
 template <int MODE, bool PART>
 hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStream_t stream) {
 #define EP_CASE(V)                                                                              \
@@ -733,6 +768,14 @@ hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, int scal
     k.nvec = hidden / 8;
     k.ng = hidden / group;
     k.group_lanes = group == hidden ? 0 : group / 8;
+    if (EP_CAST_PAIRS && k.group_lanes > 0) {
+        k.wpr = (k.nvec + 127) / 128;
+        const int64_t blocks = ((int64_t)T * k.wpr + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (blocks == 0) return hipSuccess;
+        if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(cast_pairs_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, k);
+        return hipGetLastError();
+    }
     return run(k, kModeCast, EP_DISPATCH_VPL, stream);
 }
 
