@@ -600,8 +600,63 @@ __global__ void __launch_bounds__(kBlock) cast_pairs_kernel(DispatchK a) {
     }
 }
 
+// Fused cast + dispatch with the lane layout of cast_pairs_kernel: each
+// lane's 16 codes go to every destination row with one 16-byte store, and
+// its scale (first lane of each group) with them.  Padding or metadata
+// workgroups follow the token ones, as in dispatch_kernel.
+template <bool PART>
+__global__ void __launch_bounds__(kBlock) dispatch_cast_pairs_kernel(DispatchK a) {
+    if ((int)blockIdx.x >= a.n_tok_blocks) {
+        if (PART && a.meta_rows) meta_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        else pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        return;
+    }
+    const int lane = __lane_id();
+    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int t = gw / a.wpr;
+    const int ci = gw - t * a.wpr;
+    if (t >= a.T) return;
+    const int vi = ci * 128 + 2 * lane;
+    const bool on = vi < a.nvec;
+    const ep_u32x4 *src = (const ep_u32x4 *)(a.x + (int64_t)t * a.in_row_bytes);
+    ep_u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+    if (on) {
+        v0 = load_nt(src + vi);
+        v1 = load_nt(src + vi + 1);
+    }
+    const float s = group_scale(a, group_max(fmaxf(amax8(v0), amax8(v1)), a.group_lanes >> 1));
+    const float y = 1.0f / s;
+    const ep_u32x2 e0 = encode8_y(v0, s, y), e1 = encode8_y(v1, s, y);
+    const ep_u32x4 q = {e0.x, e0.y, e1.x, e1.y};
+    const bool scale_lane = on && (vi % a.group_lanes) == 0;
+    for (int kb = 0; kb < a.nd; kb += 64) {
+        int my_slot = -1;
+        float my_w = 1.0f;
+        if (kb + lane < a.nd) {
+            my_slot = a.dst[(int64_t)t * a.nd + kb + lane];
+            if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
+        }
+        if ((int64_t)my_slot >= a.recv_rows) {
+            atomicOr(a.status, kDevRecvOverflow);
+            my_slot = -1;
+        }
+        if (ci == 0) record_dest<PART>(a, t, kb + lane, my_slot, my_w);
+        const int kn = min(64, a.nd - kb);
+        for (int k = 0; k < kn; ++k) {
+            const int slot = lane_read(my_slot, k);
+            if (slot < 0) continue;
+            if (on) row_store((ep_u32x4 *)(a.recv + (int64_t)slot * a.out_row_bytes) + (vi >> 1), q);
+            if (scale_lane) store_scale(a, slot, vi / a.group_lanes, s);
+        }
+    }
+}
+
 template <int MODE, bool PART>
 hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStream_t stream) {
+    if (EP_CAST_PAIRS && MODE == kModeCast && k.dst != nullptr && k.group_lanes > 0 && vpl == 2) {
+        hipLaunchKernelGGL((dispatch_cast_pairs_kernel<PART>), dim3(grid), dim3(kBlock), 0, stream, k);
+        return hipGetLastError();
+    }
 #define EP_CASE(V)                                                                              \
     case V:                                                                                     \
         if (MODE != kModeCast && multi)                                                         \
@@ -641,6 +696,9 @@ int choose_vpl(int nvec, int limit) {
 
 hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     int vpl = choose_vpl(k.nvec, mode == kModeCast ? EP_CAST_VPL : vpl_limit);
+    // cast with a layout and groups narrower than the row: two adjacent vectors
+    // per lane (dispatch_cast_pairs_kernel), i.e. 128 vectors per wave
+    if (EP_CAST_PAIRS && mode == kModeCast && k.dst != nullptr && k.group_lanes > 0) vpl = 2;
     if (mode == kModeCast && k.group_lanes == 0) {
         // one scale per row: the whole row must sit in one wave
         const int q = (k.nvec + 63) / 64;
