@@ -53,11 +53,16 @@ def _launch(name: str, device, fn, *tensors_then_args):
     before the plain arguments lives on it.  Usage:
     _launch(name, dev, fn, [tensors...], arg0, arg1, ...)."""
     tensors, args = tensors_then_args[0], tensors_then_args[1:]
+    cur = torch.cuda.current_device()
+    idx = cur if device.index is None else device.index
     for t in tensors:
-        if t is not None and t.device != device:
-            raise ValueError(f"{name}: all tensors must be on {device}, found {t.device}")
-    with torch.cuda.device(device):
+        if t is not None and t.get_device() != idx:
+            raise ValueError(f"{name}: all tensors must be on cuda:{idx}, found {t.device}")
+    if idx == cur:
         rc = fn(*args)
+    else:
+        with torch.cuda.device(idx):
+            rc = fn(*args)
     _abi.check(name, rc)
 
 
