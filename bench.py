@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -47,14 +48,19 @@ def algorithmic_bytes(T, H, K, N, R, elem=2):
 
 def kernel_source_hash():
     """Hash of the device sources (every csrc file but the host-only C-ABI
-    layer): profiles/traffic.json is used only while it matches."""
+    layer) with comments and whitespace removed: profiles/traffic.json is used
+    only while it matches, so any change to the code voids it and a change to
+    the comments does not."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "combine_ep_get_layout_amd", "csrc")
     for f in sorted(os.listdir(d)):
         if f == "ep_api.hip":
             continue
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(d, f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(f.encode() + " ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

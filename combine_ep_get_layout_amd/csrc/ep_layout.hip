@@ -25,10 +25,11 @@
 //
 // The phases run as two kernels and the pair ranks travel through dst_slot,
 // packed as (e << kRankBits) | rank.  A very small batch (a few hundred
-// pairs) runs both phases in one 1024-thread workgroup, one launch, with only
-// a workgroup barrier between them and the ranks kept in registers.  A cooperative single launch of every tile with a
-// grid barrier (EP_LAYOUT_FUSED) is kept as an option: it measured slower to
-// launch than the two kernels.
+// pairs) runs both phases in one 1024-thread workgroup, one launch, with
+// only a workgroup barrier between them and the ranks kept in registers.  A
+// cooperative single launch of every tile with a grid barrier
+// (EP_LAYOUT_FUSED) is kept as an option: it measured slower to launch than
+// the two kernels.
 #include <hip/hip_cooperative_groups.h>
 
 #include "ep_device.h"
