@@ -148,6 +148,36 @@ def test_dispatch_recv_rows_bound(gpu):
     assert int(lay.status.item()) & oracle.RECV_OVERFLOW
 
 
+@pytest.mark.parametrize("fmt", ["fp32", "ue8m0"])
+def test_dispatch_fp8_copy_recv_rows_bound(gpu, fmt):
+    """fp8 copy into a receive buffer shorter than R, over sentinel scales:
+    rows and scale rows past it untouched and flagged, every other byte as the
+    oracle's (padding zeroed)."""
+    announce("dispatch fp8 copy recv rows bound", fmt)
+    w = ep_inputs.make_workload("fp8", T=300, H=1024, A=8, drop_p=0.05)
+    lay, ref = _setup(gpu, w)
+    n = ref.R // 2 + 3
+    if fmt == "fp32":
+        q_ref, s_ref = oracle.cast_fp8(w.x, 128)
+        rs = torch.full((n, 8), 3.0, dtype=torch.float32, device="cuda:0")
+        xs = to_dev(s_ref)
+    else:
+        q_ref, _, s_ref = oracle.cast_fp8_pow2(w.x, 128, ue8m0=True)
+        rs = torch.full((n, 8), 7, dtype=torch.uint8, device="cuda:0")
+        xs = torch.from_numpy(np.ascontiguousarray(s_ref)).to("cuda:0")
+    recv = torch.empty((n, 1024), dtype=torch.float8_e4m3fn, device="cuda:0")
+    recv.view(torch.uint8).fill_(0x5A)
+    recv, rs, rw = gpu.ep_dispatch((fp8_to_dev(q_ref), xs), lay, to_dev(w.topk_weights),
+                                   num_recv_rows=n, zero_padding=True, out=(recv, rs, None))
+    exp, exp_s, exp_w = oracle.dispatch(q_ref, ref, w.topk_weights, x_scales=s_ref,
+                                        zero_padding=True)
+    np.testing.assert_array_equal(fp8_bits(recv), exp[:n])
+    got_s = rs.cpu().numpy()
+    np.testing.assert_array_equal(got_s.view(np.uint8), np.ascontiguousarray(exp_s[:n]).view(np.uint8))
+    np.testing.assert_array_equal(rw.cpu().numpy(), exp_w[:n])
+    assert int(lay.status.item()) & oracle.RECV_OVERFLOW
+
+
 @pytest.mark.parametrize("G", [128, 16, 64, 512, "H"])
 @pytest.mark.parametrize("fused", [False, True])
 def test_dispatch_fp8(gpu, G, fused):
