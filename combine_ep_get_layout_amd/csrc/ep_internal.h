@@ -18,6 +18,7 @@ struct LayoutPlan {
     int block;         // threads per count workgroup (multiple of 64)
     bool fused;        // count and slots in one cooperative launch when it fits
     bool single;       // the whole batch is one tile: count and slots in one workgroup
+    bool prescan;      // many tiles: a scan kernel turns the tile rows into prefixes first
     int chunks_per_wave;
     int G, NG;              // partitions per group, number of groups
     int row_stride;         // ints per tile row: E + P + NG + 1 rounded up to 4

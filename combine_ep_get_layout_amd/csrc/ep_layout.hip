@@ -48,6 +48,11 @@ constexpr int kSlotsBlock = 1024;  // slots workgroup, and the fused tiling: 16 
 constexpr int kReduceBatch = EP_LAYOUT_RBATCH;   // loads in flight per thread in column_sums
 constexpr int kMaxFusedExperts = 512;
 constexpr int64_t kSinglePairs = 256;   // batches up to this many pairs: one workgroup
+#ifndef EP_LAYOUT_PRESCAN_TILES
+#define EP_LAYOUT_PRESCAN_TILES 128   // above this many tiles: scan the tile rows once first
+#endif
+constexpr int kScanBlock = 256;       // scan kernel: one workgroup per 4 columns
+constexpr int kScanMaxRowsPerThread = 8;
 #ifndef EP_LAYOUT_FUSED
 #define EP_LAYOUT_FUSED 0      // cooperative single launch (measured slower to launch)
 #endif
@@ -95,6 +100,8 @@ struct SlotsArgs {
     int32_t *src_of_slot;
     int32_t *status;
     int32_t *cum_stats;
+    int prescanned;             // tile_counts holds exclusive prefixes and, at row
+                                // num_tiles, the totals
 };
 
 // Count phase for tile blockIdx.x.  LDS: [waves][E] counters, [tile pairs]
@@ -363,7 +370,17 @@ __device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_flags,
     uint64_t tmask = 0;
     if (want_tok && tid < ntok) tmask = a.tok_mask[t0 + tid];
 
-    column_sums(a.tile_counts, a.num_tiles, W, tile, s_tot, s_base, s_red);
+    if (a.prescanned) {
+        const int32_t *base = a.tile_counts + (int64_t)tile * W;
+        const int32_t *tot = a.tile_counts + (int64_t)a.num_tiles * W;
+        for (int c = tid; c < W; c += blockDim.x) {
+            s_base[c] = base[c];
+            s_tot[c] = tot[c];
+        }
+        __syncthreads();
+    } else {
+        column_sums(a.tile_counts, a.num_tiles, W, tile, s_tot, s_base, s_red);
+    }
 
     int R;
     if (C == 0) {
@@ -485,6 +502,57 @@ __device__ void slots_phase(const SlotsArgs &a, int32_t *lds, int32_t *s_flags,
     }
 }
 
+// Many tiles: each column of the [tiles, W] count rows scanned once.  A
+// workgroup owns four adjacent columns; thread i takes a run of consecutive
+// tiles, sums it, the runs' sums are scanned across the workgroup (wave
+// scans by shuffles, then the four wave totals), and every row is rewritten
+// with the exclusive prefix of the tiles before it; the totals go to row
+// `tiles`.  The slots kernel then reads two rows per tile instead of
+// reducing the whole matrix in every tile.
+__global__ void __launch_bounds__(kScanBlock) layout_scan_kernel(int32_t *mat, int tiles, int W) {
+    __shared__ ep_u32x4 s_wave[kScanBlock / 64];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int q = blockIdx.x;                       // column group
+    const int per = (tiles + kScanBlock - 1) / kScanBlock;
+    const int r0 = tid * per;
+    ep_u32x4 *col = (ep_u32x4 *)(mat + 4 * q);
+    const int64_t stride = W / 4;                   // row stride in 16-byte vectors
+    ep_u32x4 v[kScanMaxRowsPerThread];
+    ep_u32x4 sum = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kScanMaxRowsPerThread; ++i) {
+        v[i] = ep_u32x4{0u, 0u, 0u, 0u};
+        if (i < per && r0 + i < tiles) v[i] = col[(int64_t)(r0 + i) * stride];
+        sum += v[i];
+    }
+    // inclusive scan of the run sums within the wave, then across waves
+    ep_u32x4 inc = sum;
+    for (int o = 1; o < 64; o <<= 1) {
+        ep_u32x4 up;
+        up.x = __shfl_up(inc.x, o);
+        up.y = __shfl_up(inc.y, o);
+        up.z = __shfl_up(inc.z, o);
+        up.w = __shfl_up(inc.w, o);
+        if (lane >= o) inc += up;
+    }
+    if (lane == 63) s_wave[w] = inc;
+    __syncthreads();
+    ep_u32x4 run = inc - sum;                       // exclusive within the wave
+    for (int ww = 0; ww < w; ++ww) run += s_wave[ww];
+#pragma unroll
+    for (int i = 0; i < kScanMaxRowsPerThread; ++i) {
+        if (i < per && r0 + i < tiles) {
+            col[(int64_t)(r0 + i) * stride] = run;
+            run += v[i];
+        }
+    }
+    if (tid == kScanBlock - 1) {
+        ep_u32x4 tot = {0u, 0u, 0u, 0u};
+        for (int ww = 0; ww < kScanBlock / 64; ++ww) tot += s_wave[ww];
+        col[(int64_t)tiles * stride] = tot;
+    }
+}
+
 __global__ void __launch_bounds__(kSlotsBlock)
 layout_count_kernel(CountArgs a, int32_t *__restrict__ packed) {
     extern __shared__ int32_t lds[];
@@ -583,12 +651,14 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
     L.tile_tokens = tt;
     L.num_tiles = L.T > 0 ? (L.T + tt - 1) / tt : 0;
     L.single = L.single && L.num_tiles == 1;
+    L.prescan = !L.single && !L.fused && L.num_tiles > EP_LAYOUT_PRESCAN_TILES &&
+                L.num_tiles <= kScanBlock * kScanMaxRowsPerThread;
     const size_t nt = (size_t)(L.num_tiles > 0 ? L.num_tiles : 1);
     L.G = p->partitions_per_group > 0 ? p->partitions_per_group : L.P;
     L.NG = L.P / L.G;
     L.row_stride = (L.E + L.P + L.NG + 1 + 3) & ~3;
     L.ws_tile_counts = 0;
-    L.ws_tok_mask = align256(nt * L.row_stride * 4);
+    L.ws_tok_mask = align256((nt + 1) * L.row_stride * 4);   // + a totals row for the scan
     L.ws_bytes = L.ws_tok_mask + align256((size_t)(L.T > 0 ? L.T : 1) * 8);
     *plan = L;
     return true;
@@ -638,6 +708,7 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     sa.src_of_slot = lay->src_of_slot;
     sa.status = lay->status;
     sa.cum_stats = cum_stats;
+    sa.prescanned = L.prescan ? 1 : 0;
 
     const size_t lds_count =
         ((size_t)(L.block / 64) * L.E + ca.tile_pairs_max + L.P + L.NG) * 4;
@@ -665,8 +736,14 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     if (L.num_tiles > 0) {
         hipLaunchKernelGGL(layout_count_kernel, dim3(L.num_tiles), dim3(L.block), lds_count, stream,
                            ca, lay->dst_slot);
-        const hipError_t err = hipGetLastError();
+        hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
+        if (L.prescan) {
+            hipLaunchKernelGGL(layout_scan_kernel, dim3(L.row_stride / 4), dim3(kScanBlock), 0, stream,
+                               ca.tile_counts, L.num_tiles, L.row_stride);
+            err = hipGetLastError();
+            if (err != hipSuccess) return err;
+        }
     }
     hipLaunchKernelGGL(layout_slots_kernel, dim3(L.num_tiles > 0 ? L.num_tiles : 1),
                        dim3(kSlotsBlock), lds_slots, stream, sa);

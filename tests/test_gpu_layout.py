@@ -49,6 +49,8 @@ def test_layout_workloads_full_size(gpu, name):
     (1, 256, 512, 1, 8, 0.0),      # largest K in one workgroup (256 pairs)
     (32, 8, 512, 1, 4, 0.05),      # 256 pairs, the largest one-workgroup batch
     (33, 8, 512, 1, 4, 0.05),      # 264 pairs: the two-kernel path again
+    (9000, 8, 256, 16, 32, 0.05),  # 141 tiles: the tile rows scanned once, ragged tail
+    (20000, 4, 64, 1, 8, 0.1),     # 157 tiles, few experts
 ])
 def test_layout_shapes(gpu, T, K, E, A, P, drop):
     rng = ep_inputs.make_rng(T * 7 + K)

@@ -25,6 +25,7 @@ LAYOUT_CASES = [
     ("prefill", 1025, 6, 64, 64, 16),
     ("prefill", 777, 4, 32, 1, 0),
     ("skewed", 300, 8, 256, 16, 4),
+    ("skewed", 12000, 8, 256, 32, 8),   # 188 tiles: the tile rows scanned once
     ("tiny", 3, 2, 4, 2, 1),
     ("prefill", 1, 1, 8, 8, 2),
 ]
