@@ -24,7 +24,8 @@
 //          cumulative stats and the status word.
 //
 // The phases run as two kernels and the pair ranks travel through dst_slot,
-// packed as (e << kRankBits) | rank.  A very small batch (a few hundred
+// packed as (e << kRankBits) | rank; above EP_LAYOUT_PRESCAN_TILES tiles a
+// third kernel between them scans the tile rows once.  A very small batch (a few hundred
 // pairs) runs both phases in one 1024-thread workgroup, one launch, with
 // only a workgroup barrier between them and the ranks kept in registers.  A
 // cooperative single launch of every tile with a grid barrier
