@@ -1,0 +1,81 @@
+"""Seeded random shapes through the whole path: layout, bf16 dispatch,
+combine, and (where the shape allows fp8 rows) the cast, the fp8 copy and the
+fused cast dispatch, each compared in full with the oracle bit for bit.  The
+shapes are drawn once from a fixed seed, so every run checks the same cases."""
+import numpy as np
+import pytest
+import torch
+
+import ep_inputs
+import oracle
+from gpu_util import announce, bf16_bits, bf16_to_dev, fp8_bits, fp8_to_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n=48, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 5, 8, 16, 33, 64, 128, 256, 300]))
+        K = int(rng.integers(1, min(E, 12) + 1))
+        T = int(rng.choice([0, 1, 2, 31, 64, 257, 700, 1500]))
+        A = int(rng.choice([1, 2, 3, 8, 128]))
+        divs = [p for p in range(1, E + 1) if E % p == 0 and p <= 64]
+        P = int(rng.choice(divs))
+        C = 0 if rng.random() < 0.7 else A * int(rng.integers(1, 5))
+        H = int(rng.choice([16, 64, 256, 1040, 2048]))
+        drop = float(rng.choice([0.0, 0.1, 0.5]))
+        out.append((i, T, K, E, A, P, C, H, drop))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"c{c[0]}")
+def test_random_shape_whole_path(gpu, case):
+    i, T, K, E, A, P, C, H, drop = case
+    announce("random", case)
+    rng = ep_inputs.make_rng(1000 + i)
+    idx, wts = ep_inputs.routing_uniform(rng, T, E, K)
+    idx[rng.random((T, K)) < drop] = -1
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    lay = gpu.ep_get_layout(to_dev(idx), E, A, P, C)
+    ref = oracle.get_layout(idx, E, A, P, C, rows_cap=lay.max_recv_rows)
+    torch.cuda.synchronize()
+    assert int(lay.status.item()) == ref.status
+    np.testing.assert_array_equal(lay.num_tokens_per_expert.cpu().numpy(), ref.count)
+    np.testing.assert_array_equal(lay.expert_offset.cpu().numpy(), ref.offset)
+    np.testing.assert_array_equal(lay.dst_slot.cpu().numpy(), ref.dst)
+    np.testing.assert_array_equal(lay.is_token_in_partition.cpu().numpy(), ref.in_part)
+    np.testing.assert_array_equal(lay.num_tokens_per_partition.cpu().numpy(), ref.tok_per_part)
+    R = min(ref.R, lay.max_recv_rows)
+    np.testing.assert_array_equal(lay.src_of_slot[:R].cpu().numpy(), ref.src_of_slot[:R])
+    if ref.status:                      # capacity overflow: drops are checked above
+        return
+
+    wd = to_dev(wts)
+    recv, _, rw = gpu.ep_dispatch(bf16_to_dev(x), lay, wd, zero_padding=True)
+    exp, _, exp_w = oracle.dispatch(x, ref, wts, zero_padding=True)
+    np.testing.assert_array_equal(bf16_bits(recv[:R]), exp[:R])
+    np.testing.assert_array_equal(rw[:R].cpu().numpy(), exp_w[:R])
+
+    y = ep_inputs.make_y(rng, max(lay.max_recv_rows, 1), H)
+    out, _ = gpu.ep_combine(bf16_to_dev(y), lay, wd)
+    np.testing.assert_array_equal(bf16_bits(out), oracle.combine_f32(y, ref.dst, wts))
+
+    G = 16 if H % 16 == 0 else None
+    if G is None or T == 0:
+        return
+    G = min(128, H) if H % 128 == 0 else 16
+    q, s = oracle.cast_fp8(x, G)
+    gq, gs = gpu.ep_cast_fp8(bf16_to_dev(x), G)
+    np.testing.assert_array_equal(fp8_bits(gq), q)
+    np.testing.assert_array_equal(gs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+    exp8, exp_s, _ = oracle.dispatch(q, ref, wts, x_scales=s, zero_padding=True)
+    for src in ((fp8_to_dev(q), to_dev(s)), bf16_to_dev(x)):
+        fused = not isinstance(src, tuple)
+        r8, rs, _ = gpu.ep_dispatch(src, lay, wd, recv_fp8=fused, scale_group=G,
+                                    zero_padding=True)
+        np.testing.assert_array_equal(fp8_bits(r8[:R]), exp8[:R])
+        np.testing.assert_array_equal(rs[:R].cpu().numpy().view(np.uint32),
+                                      exp_s[:R].view(np.uint32))
+    assert lay.check() == 0
