@@ -1,6 +1,7 @@
 """Seeded random shapes through the whole path: layout, bf16 dispatch,
-combine, and (where the shape allows fp8 rows) the cast, the fp8 copy and the
-fused cast dispatch, each compared in full with the oracle bit for bit.  The
+combine and the two-level combine, the non-expanded layout with its dispatch
+and combine, and (where the shape allows fp8 rows) the cast, the fp8 copy and
+the fused cast dispatch, each compared in full with the oracle bit for bit.  The
 shapes are drawn once from a fixed seed, so every run checks the same cases."""
 import numpy as np
 import pytest
@@ -61,6 +62,25 @@ def test_random_shape_whole_path(gpu, case):
     y = ep_inputs.make_y(rng, max(lay.max_recv_rows, 1), H)
     out, _ = gpu.ep_combine(bf16_to_dev(y), lay, wd)
     np.testing.assert_array_equal(bf16_bits(out), oracle.combine_f32(y, ref.dst, wts))
+    out_r = gpu.ep_combine_reduced(bf16_to_dev(y), lay, to_dev(idx), wd)
+    np.testing.assert_array_equal(bf16_bits(out_r),
+                                  oracle.combine_reduced_f32(y, idx, ref.dst, E, P, wts))
+
+    # the non-expanded layout, its dispatch and combine
+    pl = gpu.ep_get_layout(to_dev(idx), E, A, P, C, partition_layout=True)
+    pref = oracle.partition_layout(idx, E, P)
+    np.testing.assert_array_equal(pl.token_slot.cpu().numpy(), pref.token_slot)
+    np.testing.assert_array_equal(pl.partition_offset.cpu().numpy(), pref.part_offset)
+    np.testing.assert_array_equal(pl.partition_src[:pref.Rp].cpu().numpy(), pref.part_src)
+    px, _, pi, pw = gpu.ep_dispatch_partitioned(bf16_to_dev(x), pl, to_dev(idx), wd)
+    ex, _, ei, ew = oracle.dispatch_partitioned(x, idx, pref, wts)
+    np.testing.assert_array_equal(bf16_bits(px[:pref.Rp]), ex)
+    np.testing.assert_array_equal(pi[:pref.Rp].cpu().numpy(), ei)
+    np.testing.assert_array_equal(pw[:pref.Rp].cpu().numpy(), ew)
+    yp = ep_inputs.make_y(rng, max(pref.Rp, 1), H)
+    outp = gpu.ep_combine_partitioned(bf16_to_dev(yp), pl)
+    np.testing.assert_array_equal(bf16_bits(outp),
+                                  oracle.combine_partitioned_f32(yp, pref.token_slot))
 
     G = 16 if H % 16 == 0 else None
     if G is None or T == 0:
