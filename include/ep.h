@@ -27,6 +27,12 @@
  *     anything is enqueued.  Errors only the device can see set bits in
  *     layout->status (EP_DEV_*), read by the caller after synchronising.
  *   - Counts, offsets and slots are int32; callers keep T*K, R < 2^31.
+ *   - A call may enqueue more than one kernel, all on `stream` in order (the
+ *     layout runs two or three; a zero-padded fixed-capacity dispatch that is
+ *     mostly padding zero-fills the region first).  Calls that share a
+ *     layout, workspace or output buffer must be ordered by the caller (one
+ *     stream, or events): there is no locking, and overlapping calls on such
+ *     buffers race.
  */
 #ifndef EP_H
 #define EP_H
