@@ -50,7 +50,7 @@ constexpr int kReduceBatch = EP_LAYOUT_RBATCH;   // loads in flight per thread i
 constexpr int kMaxFusedExperts = 512;
 constexpr int64_t kSinglePairs = 256;   // batches up to this many pairs: one workgroup
 #ifndef EP_LAYOUT_PRESCAN_TILES
-#define EP_LAYOUT_PRESCAN_TILES 128   // above this many tiles: scan the tile rows once first
+#define EP_LAYOUT_PRESCAN_TILES 96    // above this many tiles: scan the tile rows once first
 #endif
 constexpr int kScanBlock = 256;       // scan kernel: one workgroup per 4 columns
 constexpr int kScanMaxRowsPerThread = 8;
