@@ -51,6 +51,8 @@ def test_layout_workloads_full_size(gpu, name):
     (33, 8, 512, 1, 4, 0.05),      # 264 pairs: the two-kernel path again
     (9000, 8, 256, 16, 32, 0.05),  # 141 tiles: the tile rows scanned once, ragged tail
     (20000, 4, 64, 1, 8, 0.1),     # 157 tiles, few experts
+    (200000, 8, 256, 128, 32, 0.02),  # 1,563 tiles: runs of 7 tiles per scan thread
+    (300000, 8, 256, 1, 8, 0.02),  # 2,344 tiles: past the scan's 2,048, reduced per tile
 ])
 def test_layout_shapes(gpu, T, K, E, A, P, drop):
     rng = ep_inputs.make_rng(T * 7 + K)
