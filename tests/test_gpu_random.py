@@ -3,6 +3,8 @@ combine and the two-level combine, the non-expanded layout with its dispatch
 and combine, and (where the shape allows fp8 rows) the cast, the fp8 copy and
 the fused cast dispatch, each compared in full with the oracle bit for bit.  The
 shapes are drawn once from a fixed seed, so every run checks the same cases."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -14,7 +16,7 @@ from gpu_util import announce, bf16_bits, bf16_to_dev, fp8_bits, fp8_to_dev, to_
 pytestmark = pytest.mark.gpu
 
 
-def _cases(n=48, seed=20261203):
+def _cases(n=int(os.environ.get("EP_RANDOM_CASES", "48")), seed=20261203):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
