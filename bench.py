@@ -375,6 +375,9 @@ def main():
         "dispatch_rows": {"ms": dis_ms, "bytes": rb, "GBps": rb / (dis_ms * 1e-3) / 1e9},
         "combine": {"ms": com_ms, "bytes": cb, "GBps": cb / (com_ms * 1e-3) / 1e9},
     }
+    for v in kern.values():   # each operation as a fraction of the HBM roofline, and tokens/s
+        v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
+        v["tokens_per_s"] = T / (v["ms"] * 1e-3)
     dom = "dispatch_rows" if dis_ms >= com_ms else "combine"
     ach = kern[dom]["GBps"]
     tr = load_traffic(dom)
