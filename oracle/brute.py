@@ -18,10 +18,12 @@ def align(x: int, a: int) -> int:
     return -(-x // a) * a
 
 
-def layout(idx, E, A=1, P=1, C=0):
+def layout(idx, E, A=1, P=1, C=0, rows_cap=None):
     """idx: list of T lists of K ints.  Returns a dict with the same keys as
     the C oracle (count, offset, dst, src_of_slot, in_part, tok_per_part,
-    pairs_per_part, R, status)."""
+    pairs_per_part, R, status).  rows_cap: receive rows the caller holds
+    (None: as many as the layout needs); src_of_slot keeps only the slots
+    below it, dst keeps every slot, and status bit 4 reports R > rows_cap."""
     T = len(idx)
     K = len(idx[0]) if T else 0
     status = 0
@@ -43,6 +45,8 @@ def layout(idx, E, A=1, P=1, C=0):
     else:
         offset = [sum(align(count[j], A) for j in range(e)) for e in range(E + 1)]
     R = offset[E]
+    if rows_cap is not None and R > rows_cap:
+        status |= 4
     dst = [[-1] * K for _ in range(T)]
     src = [-1] * R
     for e in range(E):
@@ -62,6 +66,8 @@ def layout(idx, E, A=1, P=1, C=0):
                 in_part[t][e // m] = 1
     tok_per_part = [sum(in_part[t][q] for t in range(T)) for q in range(P)]
     pairs_per_part = [sum(count[e] for e in range(q * m, (q + 1) * m)) for q in range(P)]
+    if rows_cap is not None:
+        src = src[:rows_cap]
     return dict(count=count, offset=offset, dst=dst, src_of_slot=src, in_part=in_part,
                 tok_per_part=tok_per_part, pairs_per_part=pairs_per_part, R=R, status=status)
 

@@ -106,6 +106,29 @@ def test_brute_force_fixed_capacity(C):
         np.testing.assert_array_equal(o.src_of_slot, b["src_of_slot"])
 
 
+@pytest.mark.parametrize("T,K,E,A,C", [(2, 2, 3, 2, 0), (3, 1, 4, 3, 0), (2, 2, 3, 1, 2)])
+def test_brute_force_receive_rows_cap(T, K, E, A, C):
+    """Every routing, with the caller's receive rows below, at and above the
+    rows the layout needs: src_of_slot keeps exactly the slots under the cap,
+    dst keeps every slot, and the overflow bit is set iff R > cap."""
+    n_over = 0
+    for idx in _routings(T, K, E):
+        arr = np.array(idx, dtype=np.int64)
+        R = brute.layout(idx, E, A, 1, C)["R"]
+        for cap in sorted({0, 1, max(R - 1, 0), R, R + 3}):
+            if C and cap < E * C:
+                continue    # a fixed-capacity layout needs all E*C rows (argument error)
+            b = brute.layout(idx, E, A, 1, C, rows_cap=cap)
+            o = oracle.get_layout(arr, E, A, 1, C, rows_cap=cap)
+            assert o.R == b["R"] == R and o.status == b["status"]
+            assert bool(o.status & oracle.RECV_OVERFLOW) == (R > cap)
+            n_over += R > cap
+            np.testing.assert_array_equal(o.dst, np.array(b["dst"]).reshape(T, K))
+            np.testing.assert_array_equal(o.src_of_slot, b["src_of_slot"])
+            assert len(o.src_of_slot) == min(R, cap)
+    assert n_over > 0 or C
+
+
 def test_bad_expert_ids_flagged_and_ignored():
     idx = np.array([[0, 5], [-2, 1], [1, -1]], np.int64)
     o = oracle.get_layout(idx, 4, 1)
