@@ -6,6 +6,8 @@ library's gfx950 kernels.  The functions carry the C entry points' names:
 
   ep_get_layout(topk_idx, num_experts, ...)        -> Layout
   ep_dispatch(x, layout, ...)                      -> (recv_x, recv_scales, recv_topk_weights)
+  ep_dispatch_with_layout(x, topk_idx, num_experts, ...)
+                                                   -> (layout, recv_x, recv_scales, recv_topk_weights)
   ep_combine(y, layout, ...)                       -> (combined_x, combined_topk_weights)
   ep_cast_fp8(x, group=128)                        -> (x_fp8, scales)
   ep_dispatch_partitioned(x, layout, topk_idx, ...) -> (recv_x, recv_scales, recv_topk_idx,
@@ -29,7 +31,8 @@ from . import _abi
 from ._abi import (EP_DEV_BAD_EXPERT, EP_DEV_CAPACITY, EP_DEV_RECV_OVERFLOW, EpError,
                    LayoutParams, LayoutPtrs)
 
-__all__ = ["load_library", "Layout", "ep_get_layout", "ep_dispatch", "ep_combine", "ep_cast_fp8",
+__all__ = ["load_library", "Layout", "ep_get_layout", "ep_dispatch", "ep_dispatch_with_layout",
+           "ep_combine", "ep_cast_fp8",
            "ep_dispatch_partitioned", "ep_combine_partitioned", "ep_combine_reduced",
            "worst_case_recv_rows", "EpError", "EP_DEV_BAD_EXPERT", "EP_DEV_CAPACITY",
            "EP_DEV_RECV_OVERFLOW"]
@@ -204,6 +207,23 @@ def ep_get_layout(topk_idx: torch.Tensor, num_experts: int, expert_alignment: in
     num_tokens_per_group (0: one group).  A `layout` of the same shape may be
     passed in to be rewritten in place."""
     lib = load_library()
+    layout, params = _prepare_layout(topk_idx, num_experts, expert_alignment, num_partitions,
+                                     capacity, max_recv_rows, cumulative_expert_stats, layout,
+                                     partition_layout, partitions_per_group)
+    ptrs = layout.ptrs()
+    _launch("ep_get_layout", topk_idx.device, lib.ep_get_layout,
+            [cumulative_expert_stats, layout.workspace, layout.status],
+            _ptr(topk_idx), ctypes.byref(params), ctypes.byref(ptrs),
+            _ptr(cumulative_expert_stats), _ptr(layout.workspace),
+            layout.workspace.numel(), _stream(topk_idx.device))
+    return layout
+
+
+def _prepare_layout(topk_idx, num_experts, expert_alignment, num_partitions, capacity,
+                    max_recv_rows, cumulative_expert_stats, layout, partition_layout,
+                    partitions_per_group):
+    """(layout, params) for a layout call: a new Layout, or `layout` checked
+    against these shapes."""
     _need_cuda(topk_idx, "topk_idx")
     if topk_idx.dtype != torch.int64 or topk_idx.dim() != 2:
         raise ValueError("topk_idx must be int64 [T, K]")
@@ -227,13 +247,7 @@ def ep_get_layout(topk_idx: torch.Tensor, num_experts: int, expert_alignment: in
         _need_cuda(cumulative_expert_stats, "cumulative_expert_stats")
         if cumulative_expert_stats.dtype != torch.int32 or cumulative_expert_stats.numel() != num_experts:
             raise ValueError("cumulative_expert_stats must be int32 [num_experts]")
-    ptrs = layout.ptrs()
-    _launch("ep_get_layout", topk_idx.device, lib.ep_get_layout,
-            [cumulative_expert_stats, layout.workspace, layout.status],
-            _ptr(topk_idx), ctypes.byref(params), ctypes.byref(ptrs),
-            _ptr(cumulative_expert_stats), _ptr(layout.workspace),
-            layout.workspace.numel(), _stream(topk_idx.device))
-    return layout
+    return layout, params
 
 
 def _is_fp8(t: torch.Tensor) -> bool:
@@ -272,6 +286,58 @@ def ep_dispatch(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]], layou
     lib = load_library()
     x, x_scales, scale_group, x_dtype, recv_dtype, scale_fmt = _x_and_dtypes(
         x, recv_fp8, scale_group, scale_fmt)
+    bufs = _dispatch_buffers(x, layout, topk_weights, recv_dtype, scale_group, scale_fmt,
+                             num_recv_rows, out)
+    recv_x, recv_s, recv_w, rows = bufs
+    params = layout.params
+    ptrs = layout.ptrs()
+    _launch("ep_dispatch", x.device, lib.ep_dispatch,
+            [x_scales, topk_weights, recv_x, recv_s, recv_w, layout.status],
+            _ptr(x), x_dtype, _ptr(x_scales), recv_dtype, x.shape[1], scale_group,
+            _ptr(topk_weights), ctypes.byref(params), ctypes.byref(ptrs),
+            _ptr(recv_x), _ptr(recv_s), _ptr(recv_w), rows,
+            1 if zero_padding else 0, _stream(x.device))
+    return recv_x, recv_s, recv_w
+
+
+def ep_dispatch_with_layout(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]],
+                            topk_idx: torch.Tensor, num_experts: int, expert_alignment: int = 1,
+                            topk_weights: Optional[torch.Tensor] = None, num_partitions: int = 1,
+                            capacity: int = 0, max_recv_rows: Optional[int] = None,
+                            cumulative_expert_stats: Optional[torch.Tensor] = None,
+                            layout: Optional[Layout] = None, recv_fp8: bool = False,
+                            scale_group: int = 128, zero_padding: bool = False,
+                            num_recv_rows: Optional[int] = None,
+                            out: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                            scale_fmt: str = "fp32"):
+    """ep_get_layout followed by ep_dispatch in one call (the layout's slots
+    are derived by the dispatch kernels).  Arguments as the two calls; returns
+    (layout, recv_x, recv_scales or None, recv_topk_weights or None), bit for
+    bit what the two calls return."""
+    lib = load_library()
+    layout, params = _prepare_layout(topk_idx, num_experts, expert_alignment, num_partitions,
+                                     capacity, max_recv_rows, cumulative_expert_stats, layout,
+                                     False, 0)
+    x, x_scales, scale_group, x_dtype, recv_dtype, scale_fmt = _x_and_dtypes(
+        x, recv_fp8, scale_group, scale_fmt)
+    recv_x, recv_s, recv_w, rows = _dispatch_buffers(x, layout, topk_weights, recv_dtype,
+                                                     scale_group, scale_fmt, num_recv_rows, out)
+    ptrs = layout.ptrs()
+    _launch("ep_dispatch_with_layout", x.device, lib.ep_dispatch_with_layout,
+            [topk_idx, cumulative_expert_stats, layout.workspace, layout.status, x_scales,
+             topk_weights, recv_x, recv_s, recv_w],
+            _ptr(topk_idx), ctypes.byref(params), ctypes.byref(ptrs),
+            _ptr(cumulative_expert_stats), _ptr(layout.workspace), layout.workspace.numel(),
+            _ptr(x), x_dtype, _ptr(x_scales), recv_dtype, x.shape[1], scale_group,
+            _ptr(topk_weights), _ptr(recv_x), _ptr(recv_s), _ptr(recv_w), rows,
+            1 if zero_padding else 0, _stream(x.device))
+    return layout, recv_x, recv_s, recv_w
+
+
+def _dispatch_buffers(x, layout, topk_weights, recv_dtype, scale_group, scale_fmt,
+                      num_recv_rows, out):
+    """(recv_x, recv_scales, recv_topk_weights, rows) of a dispatch: the
+    buffers given in `out`, checked, or new ones."""
     T, H = x.shape
     if T != layout.num_tokens:
         raise ValueError("x rows != layout tokens")
@@ -294,15 +360,7 @@ def ep_dispatch(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]], layou
     if fp8_out:
         _check(recv_s, "recv_scales", (_scale_dtype(scale_fmt),), H // scale_group, min_rows=rows)
     _check(recv_w, "recv_topk_weights", _F32, min_rows=rows)
-    params = layout.params
-    ptrs = layout.ptrs()
-    _launch("ep_dispatch", dev, lib.ep_dispatch,
-            [x_scales, topk_weights, recv_x, recv_s, recv_w, layout.status],
-            _ptr(x), x_dtype, _ptr(x_scales), recv_dtype, H, scale_group,
-            _ptr(topk_weights), ctypes.byref(params), ctypes.byref(ptrs),
-            _ptr(recv_x), _ptr(recv_s), _ptr(recv_w), rows,
-            1 if zero_padding else 0, _stream(dev))
-    return recv_x, recv_s, recv_w
+    return recv_x, recv_s, recv_w, rows
 
 
 def ep_combine(y: torch.Tensor, layout: Layout, topk_weights: Optional[torch.Tensor] = None,
@@ -500,10 +558,11 @@ def ep_combine_partitioned(y: torch.Tensor, layout: Layout,
 def ep_combine_reduced(y: torch.Tensor, layout: Layout, topk_idx: torch.Tensor,
                        topk_weights: Optional[torch.Tensor] = None,
                        bias: Union[None, torch.Tensor, Tuple[torch.Tensor, torch.Tensor]] = None,
-                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       out: Optional[torch.Tensor] = None,
+                       bf16_partials: bool = False) -> torch.Tensor:
     """Two-level combine on the expanded layout: each partition's weighted
-    pairs summed in fp32 and rounded to bf16, then the partials (and bias)
-    summed in fp32 in partition order and rounded to bf16."""
+    pairs summed in fp32 (rounded to bf16 with bf16_partials), then the
+    partials (and bias) summed in fp32 in partition order and rounded to bf16."""
     lib = load_library()
     _need_cuda(y, "y")
     if y.dtype != torch.bfloat16:
@@ -522,5 +581,5 @@ def ep_combine_reduced(y: torch.Tensor, layout: Layout, topk_idx: torch.Tensor,
             [topk_idx, topk_weights, b0, b1, out, layout.status],
             _ptr(y), H, rows, _ptr(topk_idx), _ptr(topk_weights), _ptr(b0),
             _ptr(b1), ctypes.byref(params), ctypes.byref(ptrs), _ptr(out),
-            _stream(y.device))
+            1 if bf16_partials else 0, _stream(y.device))
     return out

@@ -26,10 +26,11 @@ EP_MAX_EXPERTS = 4096
 EP_MAX_PARTITIONS = 1024
 EP_MAX_TOPK = 256
 EP_MAX_SLOT_PARTITIONS = 64
+EP_MAX_HIDDEN = 1 << 20
 
 # Every symbol include/ep.h declares.
 EXPORTS = ("ep_get_layout_workspace_bytes", "ep_worst_case_recv_rows", "ep_get_layout",
-           "ep_dispatch", "ep_combine", "ep_dispatch_partitioned", "ep_combine_partitioned",
+           "ep_dispatch", "ep_dispatch_with_layout", "ep_combine", "ep_dispatch_partitioned", "ep_combine_partitioned",
            "ep_combine_reduced", "ep_cast_fp8", "ep_status_string")
 
 
@@ -79,6 +80,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ep_dispatch.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i32, i32, vp,
                                 P(LayoutParams), P(LayoutPtrs), vp, vp, vp, i64, ctypes.c_int, vp]
     lib.ep_dispatch.restype = ctypes.c_int
+    lib.ep_dispatch_with_layout.argtypes = [vp, P(LayoutParams), P(LayoutPtrs), vp, vp, sz,
+                                            vp, ctypes.c_int, vp, ctypes.c_int, i32, i32, vp,
+                                            vp, vp, vp, i64, ctypes.c_int, vp]
+    lib.ep_dispatch_with_layout.restype = ctypes.c_int
     lib.ep_combine.argtypes = [vp, i32, i64, vp, vp, vp, P(LayoutParams), P(LayoutPtrs), vp, vp,
                                vp, vp]
     lib.ep_combine.restype = ctypes.c_int
@@ -90,7 +95,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                            vp, vp]
     lib.ep_combine_partitioned.restype = ctypes.c_int
     lib.ep_combine_reduced.argtypes = [vp, i32, i64, vp, vp, vp, vp, P(LayoutParams),
-                                       P(LayoutPtrs), vp, vp]
+                                       P(LayoutPtrs), vp, ctypes.c_int, vp]
     lib.ep_combine_reduced.restype = ctypes.c_int
     lib.ep_cast_fp8.argtypes = [vp, i32, i32, i32, ctypes.c_int, vp, vp, vp]
     lib.ep_cast_fp8.restype = ctypes.c_int

@@ -62,9 +62,9 @@ size_t ep_get_layout_workspace_bytes(const ep_layout_params *p) {
     return plan.ws_bytes;
 }
 
-int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *p, const ep_layout *layout,
-                  int32_t *cumulative_expert_stats, void *workspace, size_t workspace_bytes,
-                  void *stream) {
+// Host checks of a layout call; fills the plan.
+static int layout_checks(const int64_t *topk_idx, const ep_layout_params *p, const ep_layout *layout,
+                         void *workspace, size_t workspace_bytes, ep::LayoutPlan *plan) {
     int rc = check_params(p);
     if (rc != EP_OK) return rc;
     if (!layout || !layout->num_tokens_per_expert || !layout->expert_offset ||
@@ -75,10 +75,18 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *p, const ep_l
     if (p->max_recv_rows > 0 && !layout->src_of_slot) return EP_ERR_INVALID_ARG;
     if (layout->token_slot && p->num_partitions > EP_MAX_SLOT_PARTITIONS) return EP_ERR_UNSUPPORTED;
     if (layout->partition_src && !layout->token_slot && p->num_tokens > 0) return EP_ERR_INVALID_ARG;
-    ep::LayoutPlan plan;
-    if (!ep::make_layout_plan(p, &plan)) return EP_ERR_UNSUPPORTED;
-    if (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace))
+    if (!ep::make_layout_plan(p, plan)) return EP_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < plan->ws_bytes || !aligned16(workspace))
         return EP_ERR_WORKSPACE;
+    return EP_OK;
+}
+
+int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *p, const ep_layout *layout,
+                  int32_t *cumulative_expert_stats, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+    ep::LayoutPlan plan;
+    const int rc = layout_checks(topk_idx, p, layout, workspace, workspace_bytes, &plan);
+    if (rc != EP_OK) return rc;
     return to_status(ep::launch_layout(plan, topk_idx, layout, cumulative_expert_stats, workspace,
                                        (hipStream_t)stream));
 }
@@ -103,6 +111,7 @@ static int dispatch_io(int x_dtype, const void *x, const void *x_scales, int rec
                        int32_t hidden, int32_t scale_group, int32_t T, const void *recv_x,
                        const void *recv_scales, int64_t num_recv_rows, int *mode, int *fmt) {
     if (num_recv_rows < 0 || hidden < 1) return EP_ERR_INVALID_ARG;
+    if (hidden > EP_MAX_HIDDEN) return EP_ERR_UNSUPPORTED;
     if (x_dtype == EP_DTYPE_BF16 && recv_dtype == EP_DTYPE_BF16) *mode = 0;
     else if (is_fp8(x_dtype) && x_dtype == recv_dtype) *mode = 1;
     else if (x_dtype == EP_DTYPE_BF16 && is_fp8(recv_dtype)) *mode = 2;
@@ -124,10 +133,13 @@ static int dispatch_io(int x_dtype, const void *x, const void *x_scales, int rec
     return EP_OK;
 }
 
-int ep_dispatch(const void *x, int x_dtype, const void *x_scales, int recv_dtype, int32_t hidden,
-                int32_t scale_group, const float *topk_weights, const ep_layout_params *p,
-                const ep_layout *layout, void *recv_x, void *recv_scales,
-                float *recv_topk_weights, int64_t num_recv_rows, int zero_padding, void *stream) {
+// Host checks of an (expanded) dispatch call; fills everything of the
+// launch arguments but the layout's source (dst_slot, or a fresh layout).
+static int dispatch_checks(const void *x, int x_dtype, const void *x_scales, int recv_dtype,
+                           int32_t hidden, int32_t scale_group, const float *topk_weights,
+                           const ep_layout_params *p, const ep_layout *layout, void *recv_x,
+                           void *recv_scales, float *recv_topk_weights, int64_t num_recv_rows,
+                           int zero_padding, ep::DispatchArgs *out) {
     int rc = check_params(p);
     if (rc != EP_OK) return rc;
     if (!layout || !layout->num_tokens_per_expert || !layout->expert_offset || !layout->status)
@@ -137,7 +149,8 @@ int ep_dispatch(const void *x, int x_dtype, const void *x_scales, int recv_dtype
     rc = dispatch_io(x_dtype, x, x_scales, recv_dtype, hidden, scale_group, p->num_tokens, recv_x,
                      recv_scales, num_recv_rows, &mode, &fmt);
     if (rc != EP_OK) return rc;
-    ep::DispatchArgs a = {};
+    ep::DispatchArgs &a = *out;
+    a = ep::DispatchArgs{};
     a.x = x;
     a.x_scales = x_scales;
     a.scale_fmt = fmt;
@@ -159,7 +172,48 @@ int ep_dispatch(const void *x, int x_dtype, const void *x_scales, int recv_dtype
     a.group = mode == 0 ? 0 : scale_group;
     a.mode = mode;
     a.zero_padding = zero_padding ? 1 : 0;
+    return EP_OK;
+}
+
+int ep_dispatch(const void *x, int x_dtype, const void *x_scales, int recv_dtype, int32_t hidden,
+                int32_t scale_group, const float *topk_weights, const ep_layout_params *p,
+                const ep_layout *layout, void *recv_x, void *recv_scales,
+                float *recv_topk_weights, int64_t num_recv_rows, int zero_padding, void *stream) {
+    ep::DispatchArgs a;
+    const int rc = dispatch_checks(x, x_dtype, x_scales, recv_dtype, hidden, scale_group,
+                                   topk_weights, p, layout, recv_x, recv_scales, recv_topk_weights,
+                                   num_recv_rows, zero_padding, &a);
+    if (rc != EP_OK) return rc;
     return to_status(ep::launch_dispatch(a, (hipStream_t)stream));
+}
+
+int ep_dispatch_with_layout(const int64_t *topk_idx, const ep_layout_params *p,
+                            const ep_layout *layout, int32_t *cumulative_expert_stats,
+                            void *workspace, size_t workspace_bytes, const void *x, int x_dtype,
+                            const void *x_scales, int recv_dtype, int32_t hidden,
+                            int32_t scale_group, const float *topk_weights, void *recv_x,
+                            void *recv_scales, float *recv_topk_weights, int64_t num_recv_rows,
+                            int zero_padding, void *stream) {
+    ep::LayoutPlan plan;
+    int rc = layout_checks(topk_idx, p, layout, workspace, workspace_bytes, &plan);
+    if (rc != EP_OK) return rc;
+    ep::DispatchArgs a;
+    rc = dispatch_checks(x, x_dtype, x_scales, recv_dtype, hidden, scale_group, topk_weights, p,
+                         layout, recv_x, recv_scales, recv_topk_weights, num_recv_rows,
+                         zero_padding, &a);
+    if (rc != EP_OK) return rc;
+    const hipStream_t st = (hipStream_t)stream;
+    // The count kernel alone, then dispatch kernels that derive the slots;
+    // shapes that do not allow it (one tile, the partition layout, tile rows
+    // too large for LDS) run the whole layout first.
+    ep::FreshLayout f;
+    const bool fold = ep::fresh_layout_of(plan, layout, cumulative_expert_stats, workspace, &f);
+    hipError_t err = ep::launch_layout(plan, topk_idx, layout, cumulative_expert_stats, workspace,
+                                       st, fold);
+    if (err != hipSuccess) return to_status(err);
+    if (fold) a.fresh = &f;
+    a.queue = ep::queue_of(plan, workspace);
+    return to_status(ep::launch_dispatch(a, st));
 }
 
 int ep_combine(const void *y, int32_t hidden, int64_t num_y_rows, const float *topk_weights,
@@ -270,7 +324,7 @@ int ep_combine_partitioned(const void *y, int32_t hidden, int64_t num_y_rows, co
 int ep_combine_reduced(const void *y, int32_t hidden, int64_t num_y_rows, const int64_t *topk_idx,
                        const float *topk_weights, const void *bias0, const void *bias1,
                        const ep_layout_params *p, const ep_layout *layout, void *out,
-                       void *stream) {
+                       int bf16_partials, void *stream) {
     int rc = check_params(p);
     if (rc != EP_OK) return rc;
     if (p->num_topk > 64) return EP_ERR_UNSUPPORTED;
@@ -297,6 +351,7 @@ int ep_combine_reduced(const void *y, int32_t hidden, int64_t num_y_rows, const 
     c.topk_idx = topk_idx;
     c.E = p->num_experts;
     c.m = p->num_experts / p->num_partitions;
+    c.bf16_partials = bf16_partials ? 1 : 0;
     return to_status(ep::launch_combine(c, (hipStream_t)stream));
 }
 

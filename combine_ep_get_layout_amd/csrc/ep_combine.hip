@@ -48,6 +48,7 @@ struct CombineK {
     int wpr;
     const int64_t *idx;   // reduced combine: routing [T, K]
     int E, m;             // reduced combine: experts, experts per partition
+    int bf16_partials;    // reduced combine: round each partition's partial to bf16
 };
 
 constexpr int kBlock = 256;
@@ -157,12 +158,17 @@ __global__ void __launch_bounds__(kBlock) combine_kernel(CombineK a) {
     }
 }
 
+// A partition's partial as it enters the level-two sum.
+__device__ __forceinline__ float partial(float p, int to_bf16) {
+    return to_bf16 ? __uint_as_float(bf16_rne(p) << 16) : p;
+}
+
 // Two-level ("reduced") combine.  The token's kept pairs are put in
 // (partition, k) order: each lane ranks its own key against the others and
 // ds_permute moves the lane index to the lane named by that rank.  Rows are
 // then read in that order, U at a time; a partition's fmaf chain starts at 0
-// and is rounded to bf16 before it is added to the running fp32 total, which
-// starts from the biases.  Requires K <= 64.
+// and is added (rounded to bf16 first with bf16_partials) to the running
+// fp32 total, which starts from the biases.  Requires K <= 64.
 template <int VPL>
 __global__ void __launch_bounds__(kBlock) combine_reduced_kernel(CombineK a) {
     constexpr int U = EP_COMBINE_U > 0 ? EP_COMBINE_U
@@ -248,7 +254,7 @@ __global__ void __launch_bounds__(kBlock) combine_reduced_kernel(CombineK a) {
                     for (int i = 0; i < VPL; ++i)
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
-                            acc[i][j] = acc[i][j] + __uint_as_float(bf16_rne(part[i][j]) << 16);
+                            acc[i][j] = acc[i][j] + partial(part[i][j], a.bf16_partials);
                             part[i][j] = 0.0f;
                         }
                 }
@@ -262,8 +268,7 @@ __global__ void __launch_bounds__(kBlock) combine_reduced_kernel(CombineK a) {
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc[i][j] = acc[i][j] + __uint_as_float(bf16_rne(part[i][j]) << 16);
+            for (int j = 0; j < 8; ++j) acc[i][j] = acc[i][j] + partial(part[i][j], a.bf16_partials);
     }
 
     ep_u32x4 *dst = (ep_u32x4 *)(a.out + (int64_t)t * a.row_bytes);
@@ -311,6 +316,7 @@ hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
     k.idx = c.topk_idx;
     k.E = c.E;
     k.m = c.m;
+    k.bf16_partials = c.bf16_partials;
     const int vpl = choose_vpl(k.nvec, EP_COMBINE_VPL);
     k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
     if (k.wpr < 1) k.wpr = 1;

@@ -23,6 +23,38 @@ constexpr int kDevRecvOverflow = 4;
 constexpr int kRankBits = 12;
 constexpr int kMaxChunksPerWave = 4;   // 64-pair chunks per wave in one tile
 
+// Workgroup barrier that orders LDS only: global loads in flight stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Exclusive scan in place over a[0..n) in LDS by one wave (each lane owns a
+// contiguous run of ceil(n/64) entries); returns the total to that wave.
+// The caller synchronises the block afterwards.
+__device__ __forceinline__ int wave_exclusive_scan(int32_t *a, int n) {
+    const int lane = threadIdx.x & 63;
+    const int per = (n + 63) >> 6;
+    const int beg = min(n, lane * per);
+    const int end = min(n, beg + per);
+    int local = 0;
+    for (int i = beg; i < end; ++i) local += a[i];
+    int x = local;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    int excl = x - local;
+    for (int i = beg; i < end; ++i) {
+        const int c = a[i];
+        a[i] = excl;
+        excl += c;
+    }
+    return __shfl(x, 63);
+}
+
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ int lane_read(int v, int lane) {
@@ -51,28 +83,6 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// OCP e4m3fn, round to nearest even, from binary32 bits.
-//  |f| >  464 (or NaN/inf): NaN code S.1111.111 (no finite neighbour);
-//  |f| <  2^-6: subnormal, code = rint(|f| * 2^9) (0..8; 8 is the smallest
-//               normal 0x08), exact power-of-two scaling then RNE;
-//  otherwise:   drop 20 mantissa bits with RNE on the integer pattern; the
-//               exponent rebias (127 -> 7) is a subtraction of 120 << 3 from
-//               the top 12 bits.  A mantissa carry moves into the exponent.
-__device__ __forceinline__ uint32_t e4m3_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t s = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a > 0x43E80000u) {
-        code = 0x7Fu;
-    } else if (a < 0x3C800000u) {
-        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-    } else {
-        code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    }
-    return s | code;
-}
-
 __device__ __forceinline__ float amax8(ep_u32x4 v) {
     float m = fabsf(bf16_lo(v.x));
     m = fmaxf(m, fabsf(bf16_hi(v.x)));
@@ -85,67 +95,46 @@ __device__ __forceinline__ float amax8(ep_u32x4 v) {
     return m;
 }
 
-#ifndef EP_CAST_DIV
-#define EP_CAST_DIV 1   // 1: reciprocal + two residual corrections; 0: plain '/' per element
-#endif
-
 // x / s rounded to nearest even, given y = RN(1/s) (one correctly rounded
-// division per scale group).  Markstein's refinement (P. Markstein, IBM J.
-// Res. Dev. 34(1), 1990): with y = RN(1/s) and q within one ulp of x/s, the
-// residual r = x - s*q is exact in one FMA and RN(q + r*y) = RN(x/s).  q =
-// x*y can be just over one ulp off, so one correction makes it faithful and
-// a second gives the rounded quotient.  Exactness needs the residual to be a
-// normal fp32 number: with s >= 1e-4/448 that holds for every |x/s| >= 2^-12,
-// and every smaller quotient has e4m3 code +-0 whatever its low bits.  The
-// sign is x's (s > 0), which also keeps -0.
+// reciprocal per scale group).  Markstein's refinement (P. Markstein, IBM J.
+// Res. Dev. 34(1), 1990): q = RN(x*y), the residual r = x - s*q is exact in
+// one FMA, and RN(q + r*y) is the correctly rounded quotient when q is
+// close enough.  For the cast's operands, x a bf16 value and s =
+// RN(max(amax, 1e-4)/448) with amax the largest |x| of the group, one
+// correction gives RN(x/s) for every pair: both significands take 128 values
+// (129 for s), all pairs are checked exhaustively against IEEE division
+// with exact rational arithmetic, and the steps scale with the operands'
+// exponents while they stay normal.  Quotients below 2^-12, where the
+// residual could leave the normal range, have e4m3 code +-0 whatever their
+// low bits.  The sign is x's (s > 0), which also keeps -0.
 __device__ __forceinline__ float div_rn(float x, float s, float y) {
-#if EP_CAST_DIV
     float q = x * y;
-    float r = __builtin_fmaf(-q, s, x);
-    q = __builtin_fmaf(r, y, q);
-    r = __builtin_fmaf(-q, s, x);
+    const float r = __builtin_fmaf(-q, s, x);
     q = __builtin_fmaf(r, y, q);
     return __builtin_copysignf(q, x);
-#else
-    (void)y;
-    return x / s;
-#endif
 }
 
-#ifndef EP_CAST_HWCVT
-#define EP_CAST_HWCVT 1   // 1: gfx950's packed fp32 -> e4m3 conversion; 0: e4m3_rne
-#endif
-
-// Four quotients -> four e4m3 codes, little-endian in one dword.  The
-// hardware conversion rounds to nearest even like e4m3_rne; the quotients
-// here never exceed 448 * (1 + 2^-23), so its overflow handling is not met.
+// Four quotients -> four e4m3 codes, little-endian in one dword, by gfx950's
+// packed fp32 -> OCP e4m3 conversion, which rounds to nearest even (checked
+// against the definition over every finite bf16 pattern under several
+// scales).  The quotients never exceed 448 * (1 + 2^-23), so its overflow
+// handling is not met.
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-#if EP_CAST_HWCVT
     uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
-#else
-    return e4m3_rne(a) | (e4m3_rne(b) << 8) | (e4m3_rne(c) << 16) | (e4m3_rne(d) << 24);
-#endif
 }
 
 // 8 bf16 values / s -> 8 e4m3 codes packed little-endian in two dwords,
-// given y = RN(1/s).
+// given y = RN(1/s).  EXACT: s is a power of two, so y is exact and so is
+// x * y (its sign is x's, -0 included): no correction is needed.
+template <bool EXACT>
 __device__ __forceinline__ ep_u32x2 encode8_y(ep_u32x4 v, float s, float y) {
+    auto q = [&](float x) { return EXACT ? x * y : div_rn(x, s, y); };
     ep_u32x2 r;
-    r.x = pack4_e4m3(div_rn(bf16_lo(v.x), s, y), div_rn(bf16_hi(v.x), s, y),
-                     div_rn(bf16_lo(v.y), s, y), div_rn(bf16_hi(v.y), s, y));
-    r.y = pack4_e4m3(div_rn(bf16_lo(v.z), s, y), div_rn(bf16_hi(v.z), s, y),
-                     div_rn(bf16_lo(v.w), s, y), div_rn(bf16_hi(v.w), s, y));
+    r.x = pack4_e4m3(q(bf16_lo(v.x)), q(bf16_hi(v.x)), q(bf16_lo(v.y)), q(bf16_hi(v.y)));
+    r.y = pack4_e4m3(q(bf16_lo(v.z)), q(bf16_hi(v.z)), q(bf16_lo(v.w)), q(bf16_hi(v.w)));
     return r;
 }
-
-__device__ __forceinline__ ep_u32x2 encode8(ep_u32x4 v, float s) {
-    return encode8_y(v, s, 1.0f / s);
-}
-
-#ifndef EP_GROUP_MAX_DPP
-#define EP_GROUP_MAX_DPP 1
-#endif
 
 // v from the lane given by a DPP control code (all lanes active).
 template <int CTRL>
@@ -159,7 +148,6 @@ __device__ __forceinline__ float dpp_f32(float v) {
 // row and inside the row, which pair every lane with one of the other
 // half; wider groups go through ds_bpermute.
 __device__ __forceinline__ float group_max(float v, int width) {
-#if EP_GROUP_MAX_DPP
     if (width <= 16) {
         if (width >= 2) v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
         if (width >= 4) v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
@@ -167,7 +155,6 @@ __device__ __forceinline__ float group_max(float v, int width) {
         if (width >= 16) v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
         return v;
     }
-#endif
     for (int o = 1; o < width; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
 }
@@ -183,30 +170,27 @@ __device__ __forceinline__ float pow2_ceil(float s) {
 // UE8M0 encoding of a power of two: its biased 8-bit exponent.
 __device__ __forceinline__ uint32_t ue8m0_of(float p) { return (__float_as_uint(p) >> 23) & 0xFFu; }
 
+// s = RN(max(amax, 1e-4) / 448) as a multiply by RN(1/448) and one exact
+// residual correction (the refinement of div_rn): the dividend takes 129
+// significands (those of bf16 values, and 1e-4f's), all checked
+// exhaustively against IEEE division.
 __device__ __forceinline__ float scale_of(float amax) {
     const float ap = amax > 1e-4f ? amax : 1e-4f;
-    return ap / 448.0f;
+    const float c = 1.0f / 448.0f;   // RN(1/448), folded at compile time
+    const float q = ap * c;
+    return __builtin_fmaf(__builtin_fmaf(-q, 448.0f, ap), c, q);
 }
-
-#ifndef EP_USE_NT_STORE
-#define EP_USE_NT_STORE 1
-#endif
-#ifndef EP_USE_NT_LOAD
-#define EP_USE_NT_LOAD 1
-#endif
 
 // Streaming accesses: rows are touched once per call, so they are issued with
 // the non-temporal hint and do not displace the routing tables in L2.
 template <typename T>
 __device__ __forceinline__ void store_nt(T *p, T v) {
-    if (EP_USE_NT_STORE) __builtin_nontemporal_store(v, p);
-    else *p = v;
+    __builtin_nontemporal_store(v, p);
 }
 
 template <typename T>
 __device__ __forceinline__ T load_nt(const T *p) {
-    if (EP_USE_NT_LOAD) return __builtin_nontemporal_load(p);
-    return *p;
+    return __builtin_nontemporal_load(p);
 }
 
 }  // namespace ep

@@ -20,6 +20,8 @@
 // reciprocal per group, e4m3 round-to-nearest-even, 8 codes per lane per
 // vector.  Padding rows are handled by extra workgroups of the same launch
 // (one slice of one expert's padding each).
+#include <atomic>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -77,21 +79,155 @@ struct DispatchK {
     int ng;                   // scales per row (fp8 modes)
     int scale_fmt;            // 0: fp32 amax/448; 1: fp32 power of two; 2: UE8M0 byte
     int group_lanes;          // cast: lanes per scale group; 0 = one scale per row
+    int group_shift;          // cast: log2(group_lanes) (a power of two)
+    uint32_t wpr_magic;       // floor(2^32 / wpr)
     int wpr;                  // waves per row
     int n_tok_blocks;
     int n_groups;             // streaming kernel: token-group slots (waves / wpr)
     int pad_slices;           // padding workgroups per expert (0 = none)
     int zero_padding;
+    // A layout whose count kernel just ran (the dispatch derives its
+    // slots): every workgroup turns the tile rows into prefixes, totals and
+    // expert offsets in LDS; each pair's slot is offset[e] + prefix[tile][e]
+    // + its tile rank; dst_slot and src_of_slot are written as slots are
+    // found, and workgroup 0 publishes counts, offsets and totals.
+    const int32_t *packed;    // [T*K], NULL: slots from dst
+    const int32_t *rows;      // [tiles, W] per-tile counts
+    int W;
+    int tile_tokens;
+    int num_tiles;
+    int A, NG;                // (P, the partitions, is shared with the partitioned dispatch)
+    int32_t *dst_out;
+    int32_t *src_out;
+    int64_t max_rows;
+    int32_t *count_out;
+    int32_t *offset_out;
+    int32_t *part_out;
+    int32_t *group_out;
+    int32_t *cum_stats;
+    uint32_t *queue;          // token queue: one counter per XCD, kQueueStride apart (or NULL)
+    int lds_bytes;            // dynamic LDS per workgroup (host side)
 };
 
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / 64;
+constexpr int kQueueStride = 64;   // uint32 between two queue counters (256 bytes)
 
 // Receive-row stores: non-temporal or plain, one switch for every mode.
 template <typename T>
 __device__ __forceinline__ void row_store(T *p, T v) {
     if (EP_DISPATCH_NT_STORE) __builtin_nontemporal_store(v, p);
     else *p = v;
+}
+
+// Dynamic LDS of a dispatch workgroup that derives its layout: [tiles][W]
+// exclusive prefixes of the tile rows, [W] totals, [E+1] expert offsets.
+__device__ __forceinline__ int32_t *fresh_lds() {
+    extern __shared__ __align__(16) int32_t ep_fresh_lds[];
+    return ep_fresh_lds;
+}
+__device__ __forceinline__ const int32_t *fresh_tot(const DispatchK &a) {
+    return fresh_lds() + a.num_tiles * a.W;
+}
+__device__ __forceinline__ const int32_t *fresh_off(const DispatchK &a) {
+    return fresh_tot(a) + a.W;
+}
+
+constexpr int kFreshRegs = 9;   // tile-row vectors per thread loaded before the first row
+
+// The layout's values this workgroup needs, rebuilt in LDS (what the slots
+// phase of the layout computes): the tile rows are loaded (kFreshRegs 16-byte
+// vectors per thread into registers first, then `first_rows` issues the
+// caller's first row loads so they are in flight meanwhile), each column
+// becomes exclusive prefixes over the tiles, the last ones the totals, and
+// align(total, A) is scanned into offsets (e*C with a fixed capacity).
+// Workgroup 0 then publishes counts, offsets, partition and group totals,
+// cumulative stats and its status bits.  Every thread of the workgroup
+// calls this.
+template <typename F>
+__device__ void fresh_setup(const DispatchK &a, F &&first_rows) {
+    int32_t *lds = fresh_lds();
+    const int tid = threadIdx.x, n = a.num_tiles, W = a.W, E = a.E, Q = W >> 2;
+    const int nq = n * Q;
+    ep_u32x4 *pre4 = (ep_u32x4 *)lds;
+    const ep_u32x4 *rows4 = (const ep_u32x4 *)a.rows;
+    ep_u32x4 st[kFreshRegs];
+#pragma unroll
+    for (int i = 0; i < kFreshRegs; ++i) {
+        const int j = tid + i * kBlock;
+        st[i] = j < nq ? rows4[j] : ep_u32x4{0u, 0u, 0u, 0u};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    first_rows();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kFreshRegs; ++i) {
+        const int j = tid + i * kBlock;
+        if (j < nq) pre4[j] = st[i];
+    }
+    for (int j = tid + kFreshRegs * kBlock; j < nq; j += kBlock) pre4[j] = rows4[j];
+    lds_barrier();
+    int32_t *tot = lds + n * W;
+    int32_t *off = tot + W;
+    for (int q = tid; q < Q; q += kBlock) {
+        ep_u32x4 run = {0u, 0u, 0u, 0u};
+        for (int r = 0; r < n; ++r) {
+            const ep_u32x4 v = pre4[r * Q + q];
+            pre4[r * Q + q] = run;
+            run += v;
+        }
+        ((ep_u32x4 *)tot)[q] = run;
+    }
+    lds_barrier();
+    if (a.C == 0) {
+        for (int e = tid; e < E; e += kBlock) off[e] = (tot[e] + a.A - 1) / a.A * a.A;
+        lds_barrier();
+        if (tid < 64) {
+            const int total = wave_exclusive_scan(off, E);
+            if (tid == 0) off[E] = total;
+        }
+    } else {
+        for (int e = tid; e <= E; e += kBlock) off[e] = e * a.C;
+    }
+    lds_barrier();
+    if (blockIdx.x != 0) return;
+    int fl = 0;
+    for (int e = tid; e < E; e += kBlock) {
+        const int c = tot[e];
+        a.count_out[e] = c;
+        a.offset_out[e] = off[e];
+        if (a.cum_stats) a.cum_stats[e] += c;
+        if (a.C > 0 && c > a.C) fl |= kDevCapacity;
+    }
+    for (int q = tid; q < a.P; q += kBlock) a.part_out[q] = tot[E + q];
+    if (a.group_out)
+        for (int g = tid; g < a.NG; g += kBlock) a.group_out[g] = tot[E + a.P + g];
+    if (tid == 0) {
+        a.offset_out[E] = off[E];
+        if ((int64_t)off[E] > a.max_rows) fl |= kDevRecvOverflow;
+        if (tot[E + a.P + a.NG] > 0) fl |= kDevBadExpert;
+    }
+    if (fl) atomicOr(a.status, fl);
+}
+
+// Slot of pair k of token t: the layout's dst entry or, for a layout derived
+// here, offset[e] + prefix[tile of t][e] + tile rank (-1 for no expert and
+// past a fixed capacity), exactly what the layout's slots phase writes.
+__device__ __forceinline__ int pair_slot(const DispatchK &a, int t, int k) {
+    if (!a.packed) return a.dst[(int64_t)t * a.nd + k];
+    const int v = a.packed[(int64_t)t * a.K + k];
+    if (v < 0) return -1;
+    const int e = v >> kRankBits;
+    const int j = fresh_lds()[(t / a.tile_tokens) * a.W + e] + (v & ((1 << kRankBits) - 1));
+    if (a.C > 0 && j >= a.C) return -1;
+    return fresh_off(a)[e] + j;
+}
+
+// The layout's own outputs for a pair whose slot was derived here.
+__device__ __forceinline__ void record_slot(const DispatchK &a, int t, int k, int slot) {
+    const int64_t p = (int64_t)t * a.K + k;
+    a.dst_out[p] = slot;
+    if (slot >= 0 && (int64_t)slot < a.max_rows) a.src_out[slot] = (int32_t)p;
 }
 
 // Scale element size and stores (fp32, or one UE8M0 byte per group).
@@ -122,6 +258,20 @@ __device__ __forceinline__ float group_scale(const DispatchK &a, float amax) {
     return a.scale_fmt == 0 ? s : pow2_ceil(s);
 }
 
+// 8 codes of one vector: with a power-of-two scale the quotient is one
+// exact multiply, else the corrected one.
+__device__ __forceinline__ ep_u32x2 encode8(const DispatchK &a, ep_u32x4 v, float s, float y) {
+    return a.scale_fmt != 0 ? encode8_y<true>(v, s, y) : encode8_y<false>(v, s, y);
+}
+
+// gw / wpr for a wave-uniform gw < 2^31: a multiply-high by
+// floor(2^32 / wpr) (computed on the host) gives the quotient or one less.
+__device__ __forceinline__ int div_wpr(const DispatchK &a, int gw) {
+    int q = (int)__umulhi((uint32_t)gw, a.wpr_magic);
+    if ((q + 1) * a.wpr <= gw) ++q;
+    return q;
+}
+
 // Cast of one wave's chunk: per-group (or, with group_lanes == 0, per-row)
 // scales, then 8 codes per lane per vector.
 template <int VPL>
@@ -139,7 +289,7 @@ __device__ __forceinline__ void cast_chunk(const DispatchK &a, const ep_u32x4 (&
         for (int i = 0; i < VPL; ++i) s[i] = sr;
     }
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) q[i] = encode8(v[i], s[i]);
+    for (int i = 0; i < VPL; ++i) q[i] = encode8(a, v[i], s[i], 1.0f / s[i]);
 }
 
 // Codes and scales of one cast chunk into receive row `slot`.
@@ -294,13 +444,22 @@ __device__ __forceinline__ void record_dest(const DispatchK &a, int t, int q, in
 }
 
 __device__ __forceinline__ void pad_rows(const DispatchK &a, int pb) {
+    if (a.pad_slices == 0) return;
     const int e = pb / a.pad_slices;
     const int sl = pb - e * a.pad_slices;
     if (e >= a.E) return;
-    const int c = a.counts[e];
+    const int32_t *counts = a.packed ? fresh_tot(a) : a.counts;
+    const int32_t *offsets = a.packed ? fresh_off(a) : a.offsets;
+    const int c = counts[e];
     const int used = a.C > 0 ? min(c, a.C) : c;
-    const int64_t beg = (int64_t)a.offsets[e] + used;
-    int64_t end = a.C > 0 ? (int64_t)a.offsets[e] + a.C : (int64_t)a.offsets[e + 1];
+    const int64_t beg = (int64_t)offsets[e] + used;
+    int64_t end = a.C > 0 ? (int64_t)offsets[e] + a.C : (int64_t)offsets[e + 1];
+    if (a.packed) {
+        // the layout's padding slots
+        const int64_t lend = end < a.max_rows ? end : a.max_rows;
+        for (int64_t r = beg + sl * kBlock + threadIdx.x; r < lend; r += (int64_t)a.pad_slices * kBlock)
+            a.src_out[r] = -1;
+    }
     if (end > a.recv_rows) end = a.recv_rows;
     if (!a.zero_padding) {
         // weights only: one thread per padding row
@@ -323,6 +482,7 @@ __device__ __forceinline__ void pad_rows(const DispatchK &a, int pb) {
 
 template <int VPL, int MODE, bool PART>
 __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
+    if (a.packed) fresh_setup(a, [] {});
     if ((int)blockIdx.x >= a.n_tok_blocks) {
         if (PART && a.meta_rows) meta_rows(a, (int)blockIdx.x - a.n_tok_blocks);
         else pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
@@ -333,7 +493,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
     const int t = gw / a.wpr;
     const int ci = gw - t * a.wpr;
     if (t >= a.T) return;
-    const int K = a.dst ? a.nd : 1;
+    const int K = (a.dst || a.packed) ? a.nd : 1;
     const int v0 = ci * VPL * 64;
 
     // Load this wave's chunk of the row once.
@@ -351,7 +511,8 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
         int my_slot = -1;
         float my_w = 1.0f;
         if (kb + lane < K) {
-            my_slot = a.dst ? a.dst[(int64_t)t * a.nd + kb + lane] : t;
+            my_slot = (a.dst || a.packed) ? pair_slot(a, t, kb + lane) : t;
+            if (a.packed && ci == 0) record_slot(a, t, kb + lane, my_slot);
             if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
         }
         if ((int64_t)my_slot >= a.recv_rows) {
@@ -390,6 +551,12 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
 #endif
 #ifndef EP_DISPATCH_PERSIST_PART
 #define EP_DISPATCH_PERSIST_PART 8   // the same for the partitioned instances (two per SIMD)
+#endif
+#ifndef EP_DISPATCH_QUEUE
+#define EP_DISPATCH_QUEUE 4      // copy modes with a token queue: its waves per CU
+#endif
+#ifndef EP_QUEUE_MIN_TOKENS
+#define EP_QUEUE_MIN_TOKENS 16384   // fewer tokens: the strided resident grid instead
 #endif
 #ifndef EP_DISPATCH_PERSIST
 #define EP_DISPATCH_PERSIST 12   // copy modes: waves per CU of the resident grid (the kernel's
@@ -440,7 +607,8 @@ __device__ __forceinline__ void store_token(const DispatchK &a, int t, int ci, i
         int my_slot = -1;
         float my_w = 1.0f;
         if (kb + lane < a.nd) {
-            my_slot = a.dst[(int64_t)t * a.nd + kb + lane];
+            my_slot = pair_slot(a, t, kb + lane);
+            if (a.packed && ci == 0) record_slot(a, t, kb + lane, my_slot);
             if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
         }
         if ((int64_t)my_slot >= a.recv_rows) {
@@ -482,27 +650,33 @@ __device__ __forceinline__ void load_chunk(const DispatchK &a, int t, int v0, in
 // current one, so reads and writes stay interleaved for the whole launch.
 template <int VPL, int MODE, int TPW, bool PART>
 __global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
-    if ((int)blockIdx.x >= a.n_tok_blocks) {
-        if (PART && a.meta_rows) meta_rows(a, (int)blockIdx.x - a.n_tok_blocks);
-        else pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
-        return;
-    }
     const int lane = __lane_id();
     const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
     const int g = gw / a.wpr;
     const int ci = gw - g * a.wpr;
-    if (g >= a.n_groups) return;
     const int v0 = ci * VPL * 64;
     const int64_t stride = (int64_t)a.n_groups * TPW;
     // j-th token of this wave
     auto tok = [&](int j) -> int64_t { return (int64_t)g * TPW + (j / TPW) * stride + (j % TPW); };
     int64_t t = tok(0);
-    if (t >= a.T) return;
+    const bool mine = (int)blockIdx.x < a.n_tok_blocks && g < a.n_groups && t < a.T;
     ep_u32x4 v0b[VPL], v1b[VPL];
     uint32_t s0b[kScaleRegs] = {}, s1b[kScaleRegs] = {};
     const bool regs = MODE == kModeCopyFp8 && ci == 0 && scales_in_regs(a);
-    load_chunk<VPL>(a, (int)t, v0, lane, v0b);
-    if (regs) load_scales(a, (int)t, lane, s0b);
+    auto first = [&] {
+        if (mine) {
+            load_chunk<VPL>(a, (int)t, v0, lane, v0b);
+            if (regs) load_scales(a, (int)t, lane, s0b);
+        }
+    };
+    if (a.packed) fresh_setup(a, first);
+    else first();
+    if ((int)blockIdx.x >= a.n_tok_blocks) {
+        if (PART && a.meta_rows) meta_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        else pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        return;
+    }
+    if (!mine) return;
     for (int j = 0;; j += 2) {
         int64_t tn = tok(j + 1);
         if (tn < a.T) {
@@ -519,6 +693,80 @@ __global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
         }
         store_token<VPL, MODE, PART>(a, (int)t, ci, v0, lane, v1b, s1b);
         if (tn >= a.T) break;
+        t = tn;
+    }
+}
+
+// Token queue of the copy modes (a layout whose count kernel just ran, whole
+// rows per wave).  The tokens are split into kXcds contiguous ranges, one per
+// XCD, each with a counter in the workspace that the layout's scan phase set
+// to zero.  A wave takes one token at a time from the counter of the XCD it
+// runs on (a one-lane global atomic, the next ticket in flight while the
+// current token's rows are stored) and, once that range is used up, from the
+// other XCDs' counters in turn, so an XCD that finishes early takes tokens
+// from a slower one instead of idling.  Every wave stops after at most
+// kXcds empty tickets.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcc_id() {
+    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & (kXcds - 1);   // HW_REG_XCC_ID
+}
+
+// Ticket from queue qx: its counter's old value (one lane's atomic, broadcast).
+__device__ __forceinline__ uint32_t queue_ticket(const DispatchK &a, int qx) {
+    uint32_t v = 0;
+    if (__lane_id() == 0) v = atomicAdd(a.queue + qx * kQueueStride, 1u);
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// The token a ticket of queue qx names, or, past that range, the next token
+// from the following queues (taken now, one ticket each); -1 when all are
+// used up.  qx and tries advance as ranges run out.
+__device__ __forceinline__ int queue_token(const DispatchK &a, uint32_t v, int &qx, int &tries) {
+    for (;;) {
+        const int64_t lo = (int64_t)qx * a.T / kXcds, hi = (int64_t)(qx + 1) * a.T / kXcds;
+        if (lo + (int64_t)v < hi) return (int)(lo + v);
+        if (++tries >= kXcds) return -1;
+        qx = (qx + 1) & (kXcds - 1);
+        v = queue_ticket(a, qx);
+    }
+}
+
+template <int VPL, int MODE>
+__global__ void __launch_bounds__(kBlock) dispatch_queue_kernel(DispatchK a) {
+    if (a.packed) fresh_setup(a, [] {});
+    if ((int)blockIdx.x >= a.n_tok_blocks) {
+        pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
+        return;
+    }
+    const int lane = __lane_id();
+    int qx = xcc_id(), tries = 0;
+    int t = queue_token(a, queue_ticket(a, qx), qx, tries);
+    if (t < 0) return;
+    ep_u32x4 v0b[VPL], v1b[VPL];
+    uint32_t s0b[kScaleRegs] = {}, s1b[kScaleRegs] = {};
+    const bool regs = MODE == kModeCopyFp8 && scales_in_regs(a);
+    load_chunk<VPL>(a, t, 0, lane, v0b);
+    if (regs) load_scales(a, t, lane, s0b);
+    uint32_t pend = queue_ticket(a, qx);
+    for (;;) {
+        int tn = queue_token(a, pend, qx, tries);
+        if (tn >= 0) {
+            load_chunk<VPL>(a, tn, 0, lane, v1b);
+            if (regs) load_scales(a, tn, lane, s1b);
+            pend = queue_ticket(a, qx);
+        }
+        store_token<VPL, MODE, false>(a, t, 0, 0, lane, v0b, s0b);
+        if (tn < 0) break;
+        t = tn;
+        tn = queue_token(a, pend, qx, tries);
+        if (tn >= 0) {
+            load_chunk<VPL>(a, tn, 0, lane, v0b);
+            if (regs) load_scales(a, tn, lane, s0b);
+            pend = queue_ticket(a, qx);
+        }
+        store_token<VPL, MODE, false>(a, t, 0, 0, lane, v1b, s1b);
+        if (tn < 0) break;
         t = tn;
     }
 }
@@ -577,9 +825,9 @@ hipError_t launch_zero_fill(const DispatchK &k, int64_t rows, hipStream_t stream
 // wholly past its end.
 __global__ void __launch_bounds__(kBlock) cast_pairs_kernel(DispatchK a) {
     const int lane = __lane_id();
-    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
-    const int t = (int)(gw / a.wpr);
-    const int c = (int)(gw - (int64_t)t * a.wpr);
+    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int t = div_wpr(a, gw);
+    const int c = gw - t * a.wpr;
     if (t >= a.T) return;
     const int vi = c * 128 + 2 * lane;
     const bool on = vi < a.nvec;
@@ -592,11 +840,11 @@ __global__ void __launch_bounds__(kBlock) cast_pairs_kernel(DispatchK a) {
     const int gl = a.group_lanes >> 1;    // lanes per group here: G / 16
     const float s = group_scale(a, group_max(fmaxf(amax8(v0), amax8(v1)), gl));
     const float y = 1.0f / s;
-    const ep_u32x2 e0 = encode8_y(v0, s, y), e1 = encode8_y(v1, s, y);
+    const ep_u32x2 e0 = encode8(a, v0, s, y), e1 = encode8(a, v1, s, y);
     if (on) {
         row_store((ep_u32x4 *)(a.recv + (int64_t)t * a.out_row_bytes) + (vi >> 1),
                   ep_u32x4{e0.x, e0.y, e1.x, e1.y});
-        if ((vi % a.group_lanes) == 0) store_scale(a, t, vi / a.group_lanes, s);
+        if ((vi & (a.group_lanes - 1)) == 0) store_scale(a, t, vi >> a.group_shift, s);
     }
 }
 
@@ -606,6 +854,7 @@ __global__ void __launch_bounds__(kBlock) cast_pairs_kernel(DispatchK a) {
 // workgroups follow the token ones, as in dispatch_kernel.
 template <bool PART>
 __global__ void __launch_bounds__(kBlock) dispatch_cast_pairs_kernel(DispatchK a) {
+    if (a.packed) fresh_setup(a, [] {});
     if ((int)blockIdx.x >= a.n_tok_blocks) {
         if (PART && a.meta_rows) meta_rows(a, (int)blockIdx.x - a.n_tok_blocks);
         else pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
@@ -613,7 +862,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_cast_pairs_kernel(DispatchK a
     }
     const int lane = __lane_id();
     const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
-    const int t = gw / a.wpr;
+    const int t = div_wpr(a, gw);
     const int ci = gw - t * a.wpr;
     if (t >= a.T) return;
     const int vi = ci * 128 + 2 * lane;
@@ -626,14 +875,15 @@ __global__ void __launch_bounds__(kBlock) dispatch_cast_pairs_kernel(DispatchK a
     }
     const float s = group_scale(a, group_max(fmaxf(amax8(v0), amax8(v1)), a.group_lanes >> 1));
     const float y = 1.0f / s;
-    const ep_u32x2 e0 = encode8_y(v0, s, y), e1 = encode8_y(v1, s, y);
+    const ep_u32x2 e0 = encode8(a, v0, s, y), e1 = encode8(a, v1, s, y);
     const ep_u32x4 q = {e0.x, e0.y, e1.x, e1.y};
-    const bool scale_lane = on && (vi % a.group_lanes) == 0;
+    const bool scale_lane = on && (vi & (a.group_lanes - 1)) == 0;
     for (int kb = 0; kb < a.nd; kb += 64) {
         int my_slot = -1;
         float my_w = 1.0f;
         if (kb + lane < a.nd) {
-            my_slot = a.dst[(int64_t)t * a.nd + kb + lane];
+            my_slot = pair_slot(a, t, kb + lane);
+            if (a.packed && ci == 0) record_slot(a, t, kb + lane, my_slot);
             if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
         }
         if ((int64_t)my_slot >= a.recv_rows) {
@@ -646,25 +896,44 @@ __global__ void __launch_bounds__(kBlock) dispatch_cast_pairs_kernel(DispatchK a
             const int slot = lane_read(my_slot, k);
             if (slot < 0) continue;
             if (on) row_store((ep_u32x4 *)(a.recv + (int64_t)slot * a.out_row_bytes) + (vi >> 1), q);
-            if (scale_lane) store_scale(a, slot, vi / a.group_lanes, s);
+            if (scale_lane) store_scale(a, slot, vi >> a.group_shift, s);
         }
     }
 }
 
+// Rows go through a layout (not the cast's identity map).
+inline bool routed(const DispatchK &k) { return k.dst != nullptr || k.packed != nullptr; }
+
+template <int MODE>
+hipError_t launch_queue(const DispatchK &k, int vpl, int grid, hipStream_t stream) {
+#define EP_CASE(V)                                                                              \
+    case V:                                                                                     \
+        hipLaunchKernelGGL((dispatch_queue_kernel<V, MODE>), dim3(grid), dim3(kBlock), k.lds_bytes, \
+                           stream, k);                                                          \
+        break;
+    switch (vpl) {
+        EP_CASE(1) EP_CASE(2) EP_CASE(4) EP_CASE(7) EP_CASE(8) EP_CASE(14) EP_CASE(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef EP_CASE
+    return hipGetLastError();
+}
+
 template <int MODE, bool PART>
 hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStream_t stream) {
-    if (EP_CAST_PAIRS && MODE == kModeCast && k.dst != nullptr && k.group_lanes > 0 && vpl == 2) {
-        hipLaunchKernelGGL((dispatch_cast_pairs_kernel<PART>), dim3(grid), dim3(kBlock), 0, stream, k);
+    if (EP_CAST_PAIRS && MODE == kModeCast && routed(k) && k.group_lanes > 0 && vpl == 2) {
+        hipLaunchKernelGGL((dispatch_cast_pairs_kernel<PART>), dim3(grid), dim3(kBlock), k.lds_bytes,
+                           stream, k);
         return hipGetLastError();
     }
 #define EP_CASE(V)                                                                              \
     case V:                                                                                     \
         if (MODE != kModeCast && multi)                                                         \
             hipLaunchKernelGGL((dispatch_stream_kernel<V, MODE, EP_DISPATCH_TPW, PART>),        \
-                               dim3(grid), dim3(kBlock), 0, stream, k);                         \
+                               dim3(grid), dim3(kBlock), k.lds_bytes, stream, k);               \
         else                                                                                    \
-            hipLaunchKernelGGL((dispatch_kernel<V, MODE, PART>), dim3(grid), dim3(kBlock), 0,   \
-                               stream, k);                                                      \
+            hipLaunchKernelGGL((dispatch_kernel<V, MODE, PART>), dim3(grid), dim3(kBlock),      \
+                               k.lds_bytes, stream, k);                                         \
         break;
     switch (vpl) {
         EP_CASE(1) EP_CASE(2) EP_CASE(4) EP_CASE(7) EP_CASE(8) EP_CASE(14) EP_CASE(16)
@@ -678,6 +947,19 @@ template <int MODE>
 hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStream_t stream) {
     return k.m > 0 ? launch_mode<MODE, true>(k, vpl, grid, multi, stream)
                    : launch_mode<MODE, false>(k, vpl, grid, multi, stream);
+}
+
+// Compute units of the current device, queried once per device.
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 constexpr int64_t kMinStreamWaves = 1024;   // below this, rows are split over more waves
@@ -698,7 +980,7 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     int vpl = choose_vpl(k.nvec, mode == kModeCast ? EP_CAST_VPL : vpl_limit);
     // cast with a layout and groups narrower than the row: two adjacent vectors
     // per lane (dispatch_cast_pairs_kernel), i.e. 128 vectors per wave
-    if (EP_CAST_PAIRS && mode == kModeCast && k.dst != nullptr && k.group_lanes > 0) vpl = 2;
+    if (EP_CAST_PAIRS && mode == kModeCast && routed(k) && k.group_lanes > 0) vpl = 2;
     if (mode == kModeCast && k.group_lanes == 0) {
         // one scale per row: the whole row must sit in one wave
         const int q = (k.nvec + 63) / 64;
@@ -706,8 +988,8 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
         if (q > 16) return hipErrorInvalidValue;
     }
     // copy modes with a layout: the streaming kernel, TPW tokens per group
-    const int tpw = mode != kModeCast && k.dst != nullptr ? EP_DISPATCH_TPW : 1;
-    const bool multi = mode != kModeCast && k.dst != nullptr;
+    const int tpw = mode != kModeCast && routed(k) ? EP_DISPATCH_TPW : 1;
+    const bool multi = mode != kModeCast && routed(k);
     if (multi) {
         // few tokens: split each row over more waves so the chip has work
         const int64_t groups = ((int64_t)k.T + tpw - 1) / tpw;
@@ -716,14 +998,24 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     }
     k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
     if (k.wpr < 1) k.wpr = 1;
+    k.wpr_magic = (uint32_t)(0xFFFFFFFFu / (uint32_t)k.wpr);
+    // large batches of the copy modes, whole rows per wave: the token queue
+    if (EP_DISPATCH_QUEUE > 0 && multi && k.queue && k.m == 0 && k.wpr == 1 &&
+        k.T >= EP_QUEUE_MIN_TOKENS) {
+        int64_t qw = (int64_t)cu_count() * EP_DISPATCH_QUEUE;
+        if (qw > k.T) qw = k.T;
+        k.n_tok_blocks = (int)((qw + kWavesPerBlock - 1) / kWavesPerBlock);
+        const int64_t qgrid = (int64_t)k.n_tok_blocks + (int64_t)k.E * k.pad_slices;
+        if (qgrid > 0x7FFFFFFF) return hipErrorInvalidValue;
+        return mode == kModeCopy16 ? launch_queue<kModeCopy16>(k, vpl, (int)qgrid, stream)
+                                   : launch_queue<kModeCopyFp8>(k, vpl, (int)qgrid, stream);
+    }
     int64_t waves = (((int64_t)k.T + tpw - 1) / tpw) * k.wpr;
     k.n_groups = (int)(((int64_t)k.T + tpw - 1) / tpw);
     if (EP_DISPATCH_PERSIST > 0 && multi) {
-        int dev = 0, cus = 256;
-        if (hipGetDevice(&dev) == hipSuccess)
-            (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         const int per_cu = k.m > 0 ? EP_DISPATCH_PERSIST_PART : EP_DISPATCH_PERSIST;
-        const int64_t cap = (int64_t)cus * per_cu / k.wpr;                // group slots
+        int64_t cap = (int64_t)cu_count() * per_cu / k.wpr;                // group slots
+        if (cap < 1) cap = 1;
         if (k.n_groups > cap) k.n_groups = (int)cap;
         waves = (int64_t)k.n_groups * k.wpr;
     }
@@ -774,6 +1066,29 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     k.part_offset = a.part_offset;
     k.meta_rows = a.partitioned && a.part_src && a.part_offset && (a.recv_idx || a.recv_wk);
     if (a.partitioned) k.dst = a.token_slot;
+    k.queue = a.partitioned ? nullptr : a.queue;
+    const bool fresh = a.fresh != nullptr && !a.partitioned;
+    if (fresh) {
+        const FreshLayout &f = *a.fresh;
+        k.dst = nullptr;
+        k.packed = f.packed;
+        k.rows = f.rows;
+        k.W = f.W;
+        k.tile_tokens = f.tile_tokens;
+        k.num_tiles = f.num_tiles;
+        k.A = f.A;
+        k.P = f.P;
+        k.NG = f.NG;
+        k.dst_out = f.dst_out;
+        k.src_out = f.src_out;
+        k.max_rows = f.max_rows;
+        k.count_out = f.count_out;
+        k.offset_out = f.offset_out;
+        k.part_out = f.part_out;
+        k.group_out = f.group_out;
+        k.cum_stats = f.cum_stats;
+        k.lds_bytes = (int)f.lds_bytes;
+    }
     if (a.mode == kModeCopy16) {
         k.in_row_bytes = k.out_row_bytes = a.hidden * 2;
         k.nvec = a.hidden / 8;
@@ -787,10 +1102,12 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
         k.nvec = a.hidden / 8;
         k.ng = a.hidden / a.group;
         k.group_lanes = a.group == a.hidden ? 0 : a.group / 8;
+        k.group_shift = k.group_lanes > 0 ? __builtin_ctz((unsigned)k.group_lanes) : 0;
     }
     k.zero_padding = a.zero_padding;
     int maxpad = a.C > 0 ? a.C : a.A - 1;
-    if ((!a.zero_padding && !a.recv_w) || a.partitioned) maxpad = 0;
+    // padding rows are visited for zeros, weights, or (fresh layout) src_of_slot
+    if ((!a.zero_padding && !a.recv_w && !fresh) || a.partitioned) maxpad = 0;
     // Fixed capacity where at most one row in eight can hold a token (decode
     // batches): zero the whole region first, then write the token rows over
     // it, instead of finding each expert's padding rows.
@@ -801,10 +1118,10 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
         const hipError_t err = launch_zero_fill(k, rows, stream);
         if (err != hipSuccess) return err;
         k.zero_padding = 0;
-        maxpad = 0;
+        if (!fresh) maxpad = 0;
     }
     if (maxpad > 0)
-        k.pad_slices = a.zero_padding ? (maxpad + EP_PAD_ROWS_PER_SLICE - 1) / EP_PAD_ROWS_PER_SLICE : 1;
+        k.pad_slices = k.zero_padding ? (maxpad + EP_PAD_ROWS_PER_SLICE - 1) / EP_PAD_ROWS_PER_SLICE : 1;
     return run(k, a.mode, EP_DISPATCH_VPL, stream);
 }
 
@@ -826,8 +1143,10 @@ hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, int scal
     k.nvec = hidden / 8;
     k.ng = hidden / group;
     k.group_lanes = group == hidden ? 0 : group / 8;
+    k.group_shift = k.group_lanes > 0 ? __builtin_ctz((unsigned)k.group_lanes) : 0;
     if (EP_CAST_PAIRS && k.group_lanes > 0) {
         k.wpr = (k.nvec + 127) / 128;
+        k.wpr_magic = (uint32_t)(0xFFFFFFFFu / (uint32_t)k.wpr);
         const int64_t blocks = ((int64_t)T * k.wpr + kWavesPerBlock - 1) / kWavesPerBlock;
         if (blocks == 0) return hipSuccess;
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;

@@ -9,6 +9,9 @@
 
 namespace ep {
 
+// Token-queue counters in the layout workspace: 8 of them, 256 bytes apart.
+constexpr size_t kQueueBytes = 8 * 256;
+
 // Tiling of the layout pass, chosen on the host from the shapes alone.
 struct LayoutPlan {
     int T, K, E, A, P, C;
@@ -16,21 +19,65 @@ struct LayoutPlan {
     int tile_tokens;   // tokens per count tile (one workgroup)
     int num_tiles;     // ceil(T / tile_tokens)
     int block;         // threads per count workgroup (multiple of 64)
-    bool fused;        // count and slots in one cooperative launch when it fits
     bool single;       // the whole batch is one tile: count and slots in one workgroup
     bool prescan;      // many tiles: a scan kernel turns the tile rows into prefixes first
     int chunks_per_wave;
     int G, NG;              // partitions per group, number of groups
     int row_stride;         // ints per tile row: E + P + NG + 1 rounded up to 4
-    size_t ws_tile_counts;  // byte offsets inside the workspace
-    size_t ws_tok_mask;
+    size_t ws_queue;        // byte offsets inside the workspace: the dispatch's token queue,
+    size_t ws_rows;         //   [tiles + 1, row_stride] count rows,
+    size_t ws_packed;       //   [T*K] (expert << 12) | rank in tile,
+    size_t ws_tok_mask;     //   [T] partition masks
     size_t ws_bytes;
 };
 
 bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan);
 
+// The whole layout (count, scan and slots kernels); the count kernel also
+// clears the dispatch's token-queue counters.  With counts_only only the
+// count kernel runs (and clears layout->status too):
+// the dispatch kernels then derive the slots themselves (DispatchArgs::fresh).
 hipError_t launch_layout(const LayoutPlan &plan, const int64_t *topk_idx, const ep_layout *layout,
-                         int32_t *cum_stats, void *workspace, hipStream_t stream);
+                         int32_t *cum_stats, void *workspace, hipStream_t stream,
+                         bool counts_only = false);
+
+// What a dispatch needs to derive a layout's slots after its count kernel:
+// the per-tile count rows and packed ranks in the workspace, and the layout
+// buffers it writes (dst_slot, src_of_slot, counts, offsets, partition and
+// group totals, cumulative stats; status gets its bits OR-ed in).
+struct FreshLayout {
+    const int32_t *packed;     // [T*K]
+    const int32_t *rows;       // [tiles, W]
+    int W;
+    int tile_tokens;
+    int num_tiles;
+    int A, P, NG;
+    size_t lds_bytes;          // dynamic LDS of a dispatch workgroup
+    int32_t *dst_out;
+    int32_t *src_out;
+    int64_t max_rows;
+    int32_t *count_out;
+    int32_t *offset_out;
+    int32_t *part_out;
+    int32_t *group_out;        // or NULL
+    int32_t *cum_stats;        // or NULL
+};
+
+// LDS of a dispatch workgroup that rebuilds the layout's prefixes: the tile
+// rows as prefixes, the totals row, the expert offsets.
+inline size_t fresh_lds_bytes(int tiles, int W, int E) {
+    return ((size_t)tiles * W + W + ((E + 1 + 3) & ~3)) * 4;
+}
+constexpr size_t kFreshLdsMax = 64 * 1024;   // two dispatch workgroups per CU
+
+// Fills `f` for a layout of this plan launched with counts_only; false when
+// the plan does not allow it (one tile, no tiles, the partition layout, or
+// tile rows too large for LDS): then the whole layout runs first.
+bool fresh_layout_of(const LayoutPlan &plan, const ep_layout *layout, int32_t *cum_stats,
+                     void *workspace, FreshLayout *f);
+
+// The token-queue counters in a layout workspace.
+uint32_t *queue_of(const LayoutPlan &plan, void *workspace);
 
 struct DispatchArgs {
     const void *x;
@@ -59,6 +106,8 @@ struct DispatchArgs {
     float *recv_wk;                // [rows*K] or NULL
     const int32_t *part_src;       // [T*P] token of each receive row, or NULL
     const int32_t *part_offset;    // [P+1]
+    const FreshLayout *fresh;      // non-NULL: slots derived here from the count kernel's output
+    uint32_t *queue;               // token-queue counters, zero when the dispatch starts, or NULL
 };
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream);
@@ -78,6 +127,7 @@ struct CombineArgs {
     // reduced (two-level) combine: routing and experts per partition
     const int64_t *topk_idx;
     int E, m;
+    int bf16_partials;
 };
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);

@@ -23,16 +23,14 @@
 //          per-expert counts and offsets, the partition totals, the
 //          cumulative stats and the status word.
 //
-// The phases run as two kernels and the pair ranks travel through dst_slot,
-// packed as (e << kRankBits) | rank; above EP_LAYOUT_PRESCAN_TILES tiles a
-// third kernel between them scans the tile rows once.  A very small batch (a few hundred
-// pairs) runs both phases in one 1024-thread workgroup, one launch, with
-// only a workgroup barrier between them and the ranks kept in registers.  A
-// cooperative single launch of every tile with a grid barrier
-// (EP_LAYOUT_FUSED) is kept as an option: it measured slower to launch than
-// the two kernels.
-#include <hip/hip_cooperative_groups.h>
-
+// The phases run as two kernels, the pair ranks travelling through the
+// workspace packed as (e << kRankBits) | rank; above kPrescanTiles tiles a
+// third kernel between them scans the tile rows once.  A very small batch
+// (a few hundred pairs) runs both phases in one 1024-thread workgroup, one
+// launch, with only a workgroup barrier between them and the ranks kept in
+// registers.  A dispatch that derives its own layout runs the count kernel
+// alone: the dispatch kernels then do the slots phase themselves from the
+// tile rows and the packed ranks.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -42,30 +40,18 @@ namespace {
 
 constexpr int kCountBlock = 256;   // count workgroup of the two-kernel tiling: 4 waves
 constexpr size_t kMaxLdsBytes = 160 * 1024;   // LDS one workgroup may allocate on gfx950
-constexpr int kSlotsBlock = 1024;  // slots workgroup, and the fused tiling: 16 waves
-#ifndef EP_LAYOUT_RBATCH
-#define EP_LAYOUT_RBATCH 8
-#endif
-constexpr int kReduceBatch = EP_LAYOUT_RBATCH;   // loads in flight per thread in column_sums
-constexpr int kMaxFusedExperts = 512;
+constexpr int kSlotsBlock = 1024;  // slots workgroup, and the one-workgroup batch: 16 waves
+constexpr int kReduceBatch = 8;    // loads in flight per thread in column_sums
+constexpr int kMaxSingleExperts = 512;
 constexpr int64_t kSinglePairs = 256;   // batches up to this many pairs: one workgroup
-#ifndef EP_LAYOUT_PRESCAN_TILES
-#define EP_LAYOUT_PRESCAN_TILES 96    // above this many tiles: scan the tile rows once first
-#endif
+constexpr int kPrescanTiles = 96;  // above this many tiles: scan the tile rows once first
 constexpr int kScanBlock = 256;       // scan kernel: one workgroup per 4 columns
 constexpr int kScanMaxRowsPerThread = 8;
-#ifndef EP_LAYOUT_FUSED
-#define EP_LAYOUT_FUSED 0      // cooperative single launch (measured slower to launch)
-#endif
-#ifndef EP_LAYOUT_SINGLE
-#define EP_LAYOUT_SINGLE 1     // batches that fit one workgroup: one launch, no handoff
-#endif
-#ifndef EP_LAYOUT_NT_HANDOFF
-#define EP_LAYOUT_NT_HANDOFF 0  // bit 0: streaming stores of tile rows, bit 1: streaming loads
-#endif
-#ifndef EP_LAYOUT_WAVES
-#define EP_LAYOUT_WAVES 4      // waves per count tile in the two-kernel path
-#endif
+// Tiles the count aims for (at most 4 chunks per wave).  32 measured best for
+// a dispatch that derives its layout (its workgroups hold the tile rows in
+// LDS: 64 tiles took 4.7 µs longer at the prefill shape, 128 did not fit
+// twice per CU) and no worse for the layout alone (two kernels, no scan).
+constexpr int kTargetTiles = 32;
 constexpr int kRedInts = 2 * 4 * kSlotsBlock;
 
 struct CountArgs {
@@ -79,6 +65,10 @@ struct CountArgs {
                             //             NG group counts | bad-id flag
     int W;                  // row stride of tile_counts, a multiple of 4
     uint64_t *tok_mask;     // [T] partition bit mask per token (P <= 64), or NULL
+    int32_t *packed;        // [T*K] (e << kRankBits) | tile rank, or -1
+    uint32_t *zero_words;   // words workgroup 0 sets to zero (the dispatch's token-queue
+    int n_zero;             //   counters, the status word of a counts-only launch)
+    int32_t *status_zero;
 };
 
 struct SlotsArgs {
@@ -101,6 +91,7 @@ struct SlotsArgs {
     int32_t *src_of_slot;
     int32_t *status;
     int32_t *cum_stats;
+    const int32_t *packed;
     int prescanned;             // tile_counts holds exclusive prefixes and, at row
                                 // num_tiles, the totals
 };
@@ -184,11 +175,7 @@ __device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
             wcnt[ww * E + e] = run;
             run += c;
         }
-#if EP_LAYOUT_NT_HANDOFF & 1
-        __builtin_nontemporal_store(run, row_out + e);
-#else
         row_out[e] = run;
-#endif
     }
     __syncthreads();
 #pragma unroll
@@ -268,11 +255,7 @@ __device__ void column_sums(const int32_t *__restrict__ mat, int rows, int cols,
                     if (r < rows) {
                         const int32_t *src = mat + (int64_t)r * cols + q * vec;
                         if (vec == 4) {
-#if EP_LAYOUT_NT_HANDOFF & 2
-                            const ep_u32x4 x = __builtin_nontemporal_load((const ep_u32x4 *)src);
-#else
                             const ep_u32x4 x = *(const ep_u32x4 *)src;
-#endif
                             v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
                         } else {
                             v[u][0] = src[0]; v[u][1] = v[u][2] = v[u][3] = 0;
@@ -316,30 +299,6 @@ __device__ void column_sums(const int32_t *__restrict__ mat, int rows, int cols,
         }
     }
     __syncthreads();
-}
-
-// Exclusive scan in place over a[0..n) in LDS by wave 0 alone (each lane
-// owns a contiguous run of ceil(n/64) entries); returns the total to wave 0.
-// The caller synchronises the block afterwards.
-__device__ int wave_exclusive_scan(int32_t *a, int n) {
-    const int lane = threadIdx.x & 63;
-    const int per = (n + 63) >> 6;
-    const int beg = min(n, lane * per);
-    const int end = min(n, beg + per);
-    int local = 0;
-    for (int i = beg; i < end; ++i) local += a[i];
-    int x = local;
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    int excl = x - local;
-    for (int i = beg; i < end; ++i) {
-        const int c = a[i];
-        a[i] = excl;
-        excl += c;
-    }
-    return __shfl(x, 63);
 }
 
 // Slots phase for tile blockIdx.x (blockDim == kSlotsBlock).  pv[i] holds a
@@ -554,10 +513,13 @@ __global__ void __launch_bounds__(kScanBlock) layout_scan_kernel(int32_t *mat, i
     }
 }
 
-__global__ void __launch_bounds__(kSlotsBlock)
-layout_count_kernel(CountArgs a, int32_t *__restrict__ packed) {
+__global__ void __launch_bounds__(kSlotsBlock) layout_count_kernel(CountArgs a) {
     extern __shared__ int32_t lds[];
     __shared__ int32_t s_flag;
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < a.n_zero; i += blockDim.x) a.zero_words[i] = 0u;
+        if (a.status_zero && threadIdx.x == 0) *a.status_zero = 0;
+    }
     int rank[kMaxChunksPerWave], ex[kMaxChunksPerWave], cpw;
     count_phase(a, lds, &s_flag, rank, ex, cpw);
     const int lane = threadIdx.x & 63;
@@ -569,7 +531,7 @@ layout_count_kernel(CountArgs a, int32_t *__restrict__ packed) {
     for (int c = 0; c < kMaxChunksPerWave; ++c) {
         const int p = (w * cpw + c) * 64 + lane;
         if (c < cpw && p < npairs)
-            packed[p0 + p] = ex[c] >= 0 ? ((ex[c] << kRankBits) | rank[c]) : -1;
+            a.packed[p0 + p] = ex[c] >= 0 ? ((ex[c] << kRankBits) | rank[c]) : -1;
     }
 }
 
@@ -585,34 +547,32 @@ __global__ void __launch_bounds__(kSlotsBlock) layout_slots_kernel(SlotsArgs a) 
     for (int i = 0; i < 4; ++i) {
         const int p = threadIdx.x + i * kSlotsBlock;
         pidx[i] = p < npairs ? p0 + p : -1;
-        pv[i] = p < npairs ? a.dst[p0 + p] : -1;
+        pv[i] = p < npairs ? a.packed[p0 + p] : -1;
     }
     slots_phase(a, lds, &s_flags, pv, pidx);
 }
 
-template <bool SINGLE>
-__global__ void __launch_bounds__(kSlotsBlock) layout_fused_kernel(CountArgs ca, SlotsArgs sa) {
+// The whole layout of a batch that is one tile: both phases in one
+// workgroup, the ranks kept in registers between them.
+__global__ void __launch_bounds__(kSlotsBlock) layout_single_kernel(CountArgs ca, SlotsArgs sa) {
     extern __shared__ int32_t lds[];
     __shared__ int32_t s_flag;
+    for (int i = threadIdx.x; i < ca.n_zero; i += blockDim.x) ca.zero_words[i] = 0u;
     int rank[kMaxChunksPerWave], ex[kMaxChunksPerWave], cpw;
     count_phase(ca, lds, &s_flag, rank, ex, cpw);
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * ca.tile_tokens;
-    const int npairs = (min(ca.T, t0 + ca.tile_tokens) - t0) * ca.K;
-    const int64_t p0 = (int64_t)t0 * ca.K;
+    const int npairs = ca.T * ca.K;
     int pv[4];
     int64_t pidx[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int p = (w * cpw + c) * 64 + lane;
-        const bool ok = c < kMaxChunksPerWave && c < cpw && p < npairs;
-        pidx[c] = ok ? p0 + p : -1;
+        const bool ok = c < cpw && p < npairs;
+        pidx[c] = ok ? p : -1;
         pv[c] = ok && ex[c] >= 0 ? ((ex[c] << kRankBits) | rank[c]) : -1;
     }
-    // Every tile's counts are in memory before any tile reads them.
-    if (SINGLE) __syncthreads();   // one tile: the workgroup reads back its own row
-    else cooperative_groups::this_grid().sync();
+    __syncthreads();   // the workgroup reads back its own tile row
     slots_phase(sa, lds, &s_flag, pv, pidx);
 }
 
@@ -630,19 +590,16 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
     L.C = p->capacity;
     L.max_rows = p->max_recv_rows;
     const int64_t pairs = (int64_t)L.T * L.K;
-    L.fused = EP_LAYOUT_FUSED && L.E <= kMaxFusedExperts;
     // A batch of at most kSinglePairs pairs is one tile: both phases run in
     // one workgroup, in one launch.  (Measured: 12.3 -> 11.1 µs at 128 pairs;
     // already slower than the two kernels at 1,024 pairs, 13.1 -> 15.6 µs.)
-    L.single = EP_LAYOUT_SINGLE && pairs > 0 && L.E <= kMaxFusedExperts &&
-               pairs <= kSinglePairs && L.T <= kSlotsBlock;
-    L.block = (L.single || L.fused || (EP_LAYOUT_WAVES == 16 && L.E <= kMaxFusedExperts))
-                  ? kSlotsBlock : kCountBlock;
+    L.single = pairs > 0 && L.E <= kMaxSingleExperts && pairs <= kSinglePairs && L.T <= kSlotsBlock;
+    L.block = L.single ? kSlotsBlock : kCountBlock;
     const int64_t per_round = L.block;   // pairs when every wave takes one 64-pair chunk
     // Chunks per wave: enough tiles to spread the count over the chip, few
-    // enough that each tile reduces the [tiles, E] count matrix in one or two
-    // round trips (16-wave tiles: ~32 of them; 4-wave tiles: ~256).
-    const int64_t target_tiles = L.single ? 1 : (L.block == kSlotsBlock ? 32 : 256);
+    // enough that each slots workgroup reduces the [tiles, W] count rows in
+    // one or two round trips (and that a dispatch can hold them in LDS).
+    const int64_t target_tiles = L.single ? 1 : kTargetTiles;
     int64_t cpw = (pairs + target_tiles * per_round - 1) / (target_tiles * per_round);
     cpw = cpw < 1 ? 1 : (cpw > kMaxChunksPerWave ? kMaxChunksPerWave : cpw);
     L.chunks_per_wave = (int)cpw;
@@ -652,21 +609,24 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
     L.tile_tokens = tt;
     L.num_tiles = L.T > 0 ? (L.T + tt - 1) / tt : 0;
     L.single = L.single && L.num_tiles == 1;
-    L.prescan = !L.single && !L.fused && L.num_tiles > EP_LAYOUT_PRESCAN_TILES &&
+    L.prescan = !L.single && L.num_tiles > kPrescanTiles &&
                 L.num_tiles <= kScanBlock * kScanMaxRowsPerThread;
     const size_t nt = (size_t)(L.num_tiles > 0 ? L.num_tiles : 1);
     L.G = p->partitions_per_group > 0 ? p->partitions_per_group : L.P;
     L.NG = L.P / L.G;
     L.row_stride = (L.E + L.P + L.NG + 1 + 3) & ~3;
-    L.ws_tile_counts = 0;
-    L.ws_tok_mask = align256((nt + 1) * L.row_stride * 4);   // + a totals row for the scan
+    L.ws_queue = 0;
+    L.ws_rows = kQueueBytes;
+    L.ws_packed = L.ws_rows + align256((nt + 1) * L.row_stride * 4);   // + a totals row for the scan
+    L.ws_tok_mask = L.ws_packed + align256((size_t)(pairs > 0 ? pairs : 1) * 4);
     L.ws_bytes = L.ws_tok_mask + align256((size_t)(L.T > 0 ? L.T : 1) * 8);
     *plan = L;
     return true;
 }
 
 hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_layout *lay,
-                         int32_t *cum_stats, void *workspace, hipStream_t stream) {
+                         int32_t *cum_stats, void *workspace, hipStream_t stream,
+                         bool counts_only) {
     char *ws = (char *)workspace;
     CountArgs ca;
     ca.idx = topk_idx;
@@ -678,12 +638,18 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     ca.tile_tokens = L.tile_tokens;
     ca.tile_pairs_max = L.tile_tokens * L.K;
     ca.in_part = lay->is_token_in_partition;
-    ca.tile_counts = (int32_t *)(ws + L.ws_tile_counts);
+    ca.tile_counts = (int32_t *)(ws + L.ws_rows);
     ca.W = L.row_stride;
     ca.G = L.G;
     ca.NG = L.NG;
     const bool want_part = lay->token_slot != nullptr || lay->partition_offset != nullptr;
     ca.tok_mask = (want_part && L.P <= 64) ? (uint64_t *)(ws + L.ws_tok_mask) : nullptr;
+    ca.packed = (int32_t *)(ws + L.ws_packed);
+    // the count kernel clears the dispatch's token queue, and in a
+    // counts-only launch the status word (the dispatch then ORs its bits in)
+    ca.zero_words = (uint32_t *)(ws + L.ws_queue);
+    ca.n_zero = (int)(kQueueBytes / 4);
+    ca.status_zero = counts_only ? lay->status : nullptr;
     SlotsArgs sa;
     sa.T = L.T;
     sa.K = L.K;
@@ -709,6 +675,7 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     sa.src_of_slot = lay->src_of_slot;
     sa.status = lay->status;
     sa.cum_stats = cum_stats;
+    sa.packed = ca.packed;
     sa.prescanned = L.prescan ? 1 : 0;
 
     const size_t lds_count =
@@ -719,26 +686,14 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
 
     if (L.single) {
         const size_t lds = lds_count > lds_slots ? lds_count : lds_slots;
-        hipLaunchKernelGGL(layout_fused_kernel<true>, dim3(1), dim3(kSlotsBlock), lds, stream, ca, sa);
+        hipLaunchKernelGGL(layout_single_kernel, dim3(1), dim3(kSlotsBlock), lds, stream, ca, sa);
         return hipGetLastError();
-    }
-    if (L.fused && L.num_tiles > 0) {
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
-            const size_t lds = lds_count > lds_slots ? lds_count : lds_slots;
-            void *args[] = {&ca, &sa};
-            const hipError_t err = hipLaunchCooperativeKernel(
-                (const void *)layout_fused_kernel<false>, dim3(L.num_tiles), dim3(kSlotsBlock), args,
-                (unsigned)lds, stream);
-            if (err == hipSuccess) return hipSuccess;
-            (void)hipGetLastError();   // not co-resident: two launches instead
-        }
     }
     if (L.num_tiles > 0) {
         hipLaunchKernelGGL(layout_count_kernel, dim3(L.num_tiles), dim3(L.block), lds_count, stream,
-                           ca, lay->dst_slot);
+                           ca);
         hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        if (err != hipSuccess || counts_only) return err;
         if (L.prescan) {
             hipLaunchKernelGGL(layout_scan_kernel, dim3(L.row_stride / 4), dim3(kScanBlock), 0, stream,
                                ca.tile_counts, L.num_tiles, L.row_stride);
@@ -749,6 +704,39 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     hipLaunchKernelGGL(layout_slots_kernel, dim3(L.num_tiles > 0 ? L.num_tiles : 1),
                        dim3(kSlotsBlock), lds_slots, stream, sa);
     return hipGetLastError();
+}
+
+bool fresh_layout_of(const LayoutPlan &L, const ep_layout *lay, int32_t *cum_stats, void *workspace,
+                     FreshLayout *f) {
+    // one tile: the single kernel writes the slots itself; no tiles: nothing
+    // to derive; the partition layout needs the slots kernel; and the tile
+    // rows must fit a dispatch workgroup's LDS
+    if (L.single || L.num_tiles == 0 || lay->token_slot || lay->partition_offset) return false;
+    const size_t lds = fresh_lds_bytes(L.num_tiles, L.row_stride, L.E);
+    if (lds > kFreshLdsMax) return false;
+    char *ws = (char *)workspace;
+    f->packed = (const int32_t *)(ws + L.ws_packed);
+    f->rows = (const int32_t *)(ws + L.ws_rows);
+    f->W = L.row_stride;
+    f->tile_tokens = L.tile_tokens;
+    f->num_tiles = L.num_tiles;
+    f->A = L.A;
+    f->P = L.P;
+    f->NG = L.NG;
+    f->lds_bytes = lds;
+    f->dst_out = lay->dst_slot;
+    f->src_out = lay->src_of_slot;
+    f->max_rows = L.max_rows;
+    f->count_out = lay->num_tokens_per_expert;
+    f->offset_out = lay->expert_offset;
+    f->part_out = lay->num_tokens_per_partition;
+    f->group_out = lay->num_tokens_per_group;
+    f->cum_stats = cum_stats;
+    return true;
+}
+
+uint32_t *queue_of(const LayoutPlan &L, void *workspace) {
+    return (uint32_t *)((char *)workspace + L.ws_queue);
 }
 
 }  // namespace ep

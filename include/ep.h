@@ -28,7 +28,7 @@
  *     layout->status (EP_DEV_*), read by the caller after synchronising.
  *   - Counts, offsets and slots are int32; callers keep T*K, R < 2^31.
  *   - A call may enqueue more than one kernel, all on `stream` in order (the
- *     layout runs two or three; a zero-padded fixed-capacity dispatch that is
+ *     layout runs one to three; a zero-padded fixed-capacity dispatch that is
  *     mostly padding zero-fills the region first).  Calls that share a
  *     layout, workspace or output buffer must be ordered by the caller (one
  *     stream, or events): there is no locking, and overlapping calls on such
@@ -72,7 +72,7 @@ enum { EP_DTYPE_BF16 = 0, EP_DTYPE_FP8_E4M3 = 1, EP_DTYPE_FP8_E4M3_POW2 = 2,
 
 /* Limits of the library. */
 enum { EP_MAX_EXPERTS = 4096, EP_MAX_PARTITIONS = 1024, EP_MAX_TOPK = 256,
-       EP_MAX_SLOT_PARTITIONS = 64 };
+       EP_MAX_SLOT_PARTITIONS = 64, EP_MAX_HIDDEN = 1 << 20 };
 
 /* Shape of one layout ([API] 2.1 parameter table: num_experts,
  * expert_alignment, num_max_tokens_per_rank; 3.1 num_tokens_per_rank). */
@@ -188,13 +188,34 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,
  *                0: their bytes are left as they were.
  * recv_x[dst_slot[t,k]] = x[t] byte for byte (fp8: codes and scale row).
  * Errors: EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED (a scale_group outside the
- * set above, or one scale per row, G = hidden, above 8192 channels in a cast:
- * the row must fit one wave). */
+ * set above, one scale per row, G = hidden, above 8192 channels in a cast:
+ * the row must fit one wave, or hidden > EP_MAX_HIDDEN). */
 int ep_dispatch(const void *x, int x_dtype, const void *x_scales, int recv_dtype,
                 int32_t hidden, int32_t scale_group, const float *topk_weights,
                 const ep_layout_params *params, const ep_layout *layout,
                 void *recv_x, void *recv_scales, float *recv_topk_weights,
                 int64_t num_recv_rows, int zero_padding, void *stream);
+
+/* ep_dispatch_with_layout - ep_get_layout followed by ep_dispatch, in one
+ * call ([API] 2.1: V2's dispatch derives the layout from topk_idx itself and
+ * returns the handle for combine).  Arguments are those of the two calls;
+ * every output (the layout buffers, cumulative stats and the receive
+ * buffers) is bit for bit what the two calls in sequence write.  Only the
+ * layout's count kernel runs before the rows: each dispatch workgroup
+ * derives the offsets and its pairs' slots from the count kernel's tile rows
+ * in LDS and writes dst_slot / src_of_slot as it goes.  Shapes where that
+ * does not apply (a batch of one count tile, the partition layout requested
+ * through layout->token_slot or partition_offset, tile rows beyond 64 KB)
+ * run the two calls' kernels as they are.  The workspace is ep_get_layout's.
+ * Errors: those of ep_get_layout and ep_dispatch, checked before anything is
+ * enqueued. */
+int ep_dispatch_with_layout(const int64_t *topk_idx, const ep_layout_params *params,
+                            const ep_layout *layout, int32_t *cumulative_expert_stats,
+                            void *workspace, size_t workspace_bytes, const void *x, int x_dtype,
+                            const void *x_scales, int recv_dtype, int32_t hidden,
+                            int32_t scale_group, const float *topk_weights, void *recv_x,
+                            void *recv_scales, float *recv_topk_weights, int64_t num_recv_rows,
+                            int zero_padding, void *stream);
 
 /* ep_combine - gather expert outputs back to their tokens and reduce.
  * ([API] 2.2: weighted reduction back to the source, bias 0/1/2 tensors,
@@ -257,14 +278,15 @@ int ep_combine_partitioned(const void *y, int32_t hidden, int64_t num_y_rows, co
 /* ep_combine_reduced - the two-level ("reduced") combine on the expanded
  * layout ([API] 2.2: reduced combine, multi-level reduction).  Level 1, per
  * partition q: p_q = fmaf chain from 0 over the token's pairs in q (k
- * ascending), rounded to bf16 (the dtype a partial travels in).  Level 2:
- * acc = 0; acc += bias0; acc += bias1; acc += p_q for q ascending (fp32);
+ * ascending), fp32; with bf16_partials = 1 each p_q is rounded to bf16 (the
+ * dtype a partial would travel in between ranks).  Level 2: acc = 0;
+ * acc += bias0; acc += bias1; acc += p_q for q ascending (fp32);
  * out = bf16_rne(acc).  topk_idx is the routing (device int64 [T, K]); the
  * other arguments are as ep_combine.  EP_ERR_UNSUPPORTED when K > 64. */
 int ep_combine_reduced(const void *y, int32_t hidden, int64_t num_y_rows, const int64_t *topk_idx,
                        const float *topk_weights, const void *bias0, const void *bias1,
                        const ep_layout_params *params, const ep_layout *layout, void *out,
-                       void *stream);
+                       int bf16_partials, void *stream);
 
 /* ep_cast_fp8 - per (token, group) cast of bf16 rows to OCP e4m3
  * ([API] 4.2 per_token_cast_to_fp8, with one scale per group of G channels;

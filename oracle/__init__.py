@@ -137,6 +137,24 @@ def dispatch(x_rows, layout: Layout, topk_weights=None, x_scales=None, zero_padd
     return recv, recv_s, recv_w
 
 
+def dispatch_tokens(x_rows, layout: Layout, topk_weights, recv, recv_w, t0, t1):
+    """oracle_dispatch over tokens [t0, t1) only, into caller-owned recv
+    [R, ...] and recv_w [R] (no zero padding): lets disjoint token ranges run
+    on separate threads (ctypes releases the GIL during the call)."""
+    lib = _load()
+    x = np.ascontiguousarray(x_rows)
+    K = layout.dst.shape[1]
+    row_bytes = x[0].nbytes
+    dst = np.ascontiguousarray(layout.dst, np.int32)
+    w = _c(topk_weights, np.float32)
+    src = np.ascontiguousarray(layout.src_of_slot, np.int32)
+    lib.oracle_dispatch(ctypes.c_void_p(x.ctypes.data + t0 * row_bytes), _i64(row_bytes), None,
+                        _i64(0), None if w is None else ctypes.c_void_p(w.ctypes.data + t0 * K * 4),
+                        _i64(t1 - t0), _i64(K), ctypes.c_void_p(dst.ctypes.data + t0 * K * 4),
+                        _p(src), _i64(min(layout.R, len(src))), ctypes.c_int(0), _p(recv), None,
+                        _p(recv_w))
+
+
 def cast_fp8(x_bits, group=128):
     """Per (token, group) e4m3 cast.  Returns (codes uint8 [T,H], scales f32 [T,H/G])."""
     lib = _load()
@@ -342,9 +360,10 @@ def combine_partitioned_f64(y, token_slot, bias0=None, bias1=None, tokens=None):
 
 
 def combine_reduced_f32(y, topk_idx, dst, num_experts, num_partitions, topk_weights=None,
-                        bias0=None, bias1=None, tokens=None):
-    """Two-level combine: per-partition fp32 partial rounded to bf16, then the
-    partials summed over partitions in ascending order (with the biases first)."""
+                        bias0=None, bias1=None, tokens=None, bf16_partials=False):
+    """Two-level combine: per-partition fp32 partial (rounded to bf16 with
+    bf16_partials), then the partials summed over partitions in ascending
+    order (with the biases first), bf16 result."""
     lib = _load()
     y = _c(y, np.uint16)
     H = y.shape[1]
@@ -357,5 +376,6 @@ def combine_reduced_f32(y, topk_idx, dst, num_experts, num_partitions, topk_weig
     out = np.zeros((n, H), np.uint16)
     lib.oracle_combine_reduced_f32(_p(y), _i64(H), _p(idx), _p(w), _p(b0), _p(b1), _i64(T),
                                    _i64(K), _i64(num_experts), _i64(num_partitions), _p(dst),
-                                   _p(tk), _i64(n), _p(out))
+                                   ctypes.c_int(1 if bf16_partials else 0), _p(tk), _i64(n),
+                                   _p(out))
     return out

@@ -575,13 +575,16 @@ void oracle_combine_partitioned_f64(const uint16_t *y, int64_t H, const uint16_t
 /* "Reduced" combine on the expanded layout ([API] sec. 2.2: reduced combine,
  * multi-level reduction under allow_multiple_reduction).  Reading: level 1
  * sums a token's pairs inside each partition (k ascending, fp32 fmaf from
- * 0) and rounds that partial to bf16, the dtype a partial travels in;
- * level 2 adds bias0, bias1, then the partials for q ascending (fp32), and
- * rounds to bf16.  The float64 reference is oracle_combine_f64.            */
+ * 0); level 2 adds bias0, bias1, then the partials for q ascending (fp32),
+ * and rounds to bf16.  The page gives the partials no rounding, so they stay
+ * fp32; with bf16_partials each partial is first rounded to bf16, the dtype
+ * it would travel in between ranks.  The float64 reference is
+ * oracle_combine_f64.                                                      */
 void oracle_combine_reduced_f32(const uint16_t *y, int64_t H, const int64_t *idx,
                                 const float *w, const uint16_t *bias0, const uint16_t *bias1,
                                 int64_t T, int64_t K, int64_t E, int64_t P, const int32_t *dst,
-                                const int64_t *tokens, int64_t n_out, uint16_t *out)
+                                int bf16_partials, const int64_t *tokens, int64_t n_out,
+                                uint16_t *out)
 {
     int64_t m = E / P;
     int64_t n = tokens ? n_out : T;
@@ -602,7 +605,9 @@ void oracle_combine_reduced_f32(const uint16_t *y, int64_t H, const int64_t *idx
                     float wk = w ? w[t * K + k] : 1.0f;
                     part = fmaf(wk, oracle_bf16_to_float(y[slot * H + c]), part);
                 }
-                if (any) acc = acc + oracle_bf16_to_float(oracle_bf16_from_float(part));
+                if (!any) continue;
+                if (bf16_partials) acc = acc + oracle_bf16_to_float(oracle_bf16_from_float(part));
+                else acc = acc + part;
             }
             out[i * H + c] = oracle_bf16_from_float(acc);
         }

@@ -169,11 +169,11 @@ def test_partitioned_calls_reject_bad_arguments():
                                       None) == _abi.EP_ERR_UNSUPPORTED
     assert lib.ep_combine_reduced(ctypes.c_void_p(16), 64, 16, None, None, None, None,
                                   ctypes.byref(p), ctypes.byref(lay), ctypes.c_void_p(16),
-                                  None) == _abi.EP_ERR_INVALID_ARG   # no topk_idx
+                                  0, None) == _abi.EP_ERR_INVALID_ARG   # no topk_idx
     k100 = _params(T=4, K=100, E=128, P=4)
     assert lib.ep_combine_reduced(ctypes.c_void_p(16), 64, 16, ctypes.c_void_p(16), None, None,
                                   None, ctypes.byref(k100), ctypes.byref(lay),
-                                  ctypes.c_void_p(16), None) == _abi.EP_ERR_UNSUPPORTED
+                                  ctypes.c_void_p(16), 0, None) == _abi.EP_ERR_UNSUPPORTED
 
 
 def test_status_strings():

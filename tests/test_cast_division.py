@@ -1,11 +1,21 @@
-"""The division the fp8 cast kernels use: y = RN(1/s) once per scale group,
-then per element q = RN(x*y) and two corrections q = RN(q + y*RN(x - s*q))
-(Markstein's refinement, P. Markstein, IBM J. Res. Dev. 34(1), 1990), with
-x's sign.  Restated here with exact rational FMAs and compared bit for bit
-with IEEE float32 division on sampled inputs of the cast's range: bf16 x,
-s = max(amax, 1e-4) / 448 for the group's amax >= |x|.  Bitwise equality is
-asked wherever an e4m3 code can be non-zero or sit on a rounding boundary
-(|x/s| >= 2^-12, with margin); below that, the codes are signed zeros."""
+"""The divisions the fp8 cast kernels use, restated with exact rational
+arithmetic and compared bit for bit with IEEE float32 division.
+
+* Scale: s = RN(ap / 448) with ap = max(amax, 1e-4f), computed as q =
+  RN(ap * c) with c = RN(1/448), then one residual correction
+  q + RN(ap - 448 q) * c (Markstein's refinement, P. Markstein, IBM J. Res.
+  Dev. 34(1), 1990).
+* Quotient: x / s computed as y = RN(1/s) once per scale group, then per
+  element q = RN(x*y) and one correction q = RN(q + y*RN(x - s*q)), with x's
+  sign.
+
+Both are asked to equal IEEE division on every input the kernels can meet:
+x is a bf16 value and amax the largest |x| of its group (a bf16 value, or
+the 1e-4f floor), so the dividends take 128 significands (129 with 1e-4f)
+and s one of 129; every pair of significands is checked, at more than one
+exponent (the steps scale with the operands' exponents while they stay
+normal).  Quotients below 2^-12 have e4m3 code +-0: there only the sign and
+the magnitude class are asked for."""
 from fractions import Fraction
 
 import numpy as np
@@ -35,54 +45,87 @@ def _fma32(a, b, c):
     return _rn32(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c)))
 
 
+C448 = np.float32(1.0) / np.float32(448.0)          # RN(1/448)
+FLOOR = np.float32(1e-4)
+
+
+def _scale_kernel(amax):
+    ap = max(np.float32(amax), FLOOR)
+    q = np.float32(ap * C448)
+    return _fma32(_fma32(-q, np.float32(448.0), ap), C448, q)
+
+
 def _div_kernel(x, s):
     y = np.float32(1.0) / s
     q = np.float32(x * y)
     r = _fma32(-q, s, x)
     q = _fma32(r, y, q)
-    r = _fma32(-q, s, x)
-    q = _fma32(r, y, q)
     return np.copysign(q, x).astype(np.float32)
 
 
-def _check(xs, ss):
-    for x, s in zip(xs, ss):
-        x, s = np.float32(x), np.float32(s)
-        ref = x / s
-        got = _div_kernel(x, s)
-        if abs(ref) >= np.float32(2.0 ** -12):
-            assert got.view(np.uint32) == ref.view(np.uint32), (x, s, got, ref)
-        else:
-            # Every e4m3 code of |q| < 2^-10 is a signed zero.  Down here the
-            # residual of a tiny x can fall below fp32's normal range, where
-            # the corrections are no longer exact: only sign and magnitude class
-            # are asked for.
-            assert np.signbit(got) == np.signbit(ref) and abs(got) < 2.0 ** -10
+def _check_div(x, s):
+    x, s = np.float32(x), np.float32(s)
+    ref = x / s
+    got = _div_kernel(x, s)
+    if abs(ref) >= np.float32(2.0 ** -12):
+        assert got.view(np.uint32) == ref.view(np.uint32), (x, s, got, ref)
+    else:
+        assert np.signbit(got) == np.signbit(ref) and abs(got) < 2.0 ** -10
 
 
-def test_division_matches_ieee_on_cast_inputs():
-    rng = ep_inputs.make_rng(21)
-    n = 6000
-    x = ep_inputs.bf16_normal(rng, (n,))
-    xf = (x.astype(np.uint32) << 16).view(np.float32)
-    # group amax at or above |x|: |x| times a factor in [1, 2^12]
-    amax = np.abs(xf) * np.exp2(rng.uniform(0, 12, n)).astype(np.float32)
-    s = (np.maximum(amax, np.float32(1e-4)) / np.float32(448)).astype(np.float32)
-    _check(xf, s)
+def _bf16_significands():
+    """The 128 bf16 significands as float32 values in [1, 2)."""
+    return ((np.arange(128, dtype=np.uint32) | 0x3F80) << 16).view(np.float32)
 
 
-def test_division_matches_ieee_on_all_bf16_magnitudes():
-    """Every bf16 exponent and several significands, against a few scales."""
+def test_scale_matches_ieee_for_every_amax_significand():
+    amaxes = [m * np.float32(2.0 ** e) for e in (-13, -3, 0, 7, 40, 126) for m in _bf16_significands()]
+    amaxes += [np.float32(0.0), FLOOR, np.float32(9.9e-5), np.float32(3.3895314e38)]
+    for a in amaxes:
+        a = np.float32(a)
+        ref = np.float32(max(a, FLOOR) / np.float32(448.0))
+        got = _scale_kernel(a)
+        assert got.view(np.uint32) == ref.view(np.uint32), (a, got, ref)
+
+
+def test_division_matches_ieee_for_every_significand_pair():
+    sig = _bf16_significands()
+    scales = [np.float32(m / np.float32(448.0)) for m in sig] + [np.float32(FLOOR / np.float32(448.0))]
+    for s in scales:
+        for shift in (np.float32(0.5), np.float32(2.0 ** -9)):
+            for X in sig:
+                x = np.float32(X * shift)
+                _check_div(x, s)
+                _check_div(-x, s)
+
+
+def test_division_at_scale_exponents_and_tiny_quotients():
+    """The same significand pairs with the scale far from 1 (amax 2^-13 ..
+    2^126) and dividends down to the tiny-quotient region."""
     rng = ep_inputs.make_rng(22)
-    bits = np.concatenate([np.arange(0, 0x7F80, 97), [0x0000, 0x8000, 0x0001, 0x8001, 0x7F7F]])
-    bits = np.concatenate([bits, bits | 0x8000]).astype(np.uint16)
-    xf = (bits.astype(np.uint32) << 16).view(np.float32)
-    for lead in (np.float32(448.0), np.float32(3.0e38), np.float32(0.37), np.float32(1e-4)):
-        a = np.maximum(np.abs(xf).max(initial=0), lead) if lead > 1 else lead
-        keep = np.abs(xf) <= a
-        s = np.float32(max(a, np.float32(1e-4)) / np.float32(448))
-        _check(xf[keep][:1500], np.full(min(keep.sum(), 1500), s, np.float32))
-    # random scales
-    s = (np.exp2(rng.uniform(-20, 20, 3000)) / 448).astype(np.float32)
-    x = np.clip(rng.standard_normal(3000).astype(np.float32) * s * 448, -448 * s, 448 * s)
-    _check(x.astype(np.float32), s)
+    sig = _bf16_significands()
+    for e in (-13, 40, 126):
+        for m in sig[rng.choice(128, 16, replace=False)]:
+            amax = np.float32(m * np.float32(2.0 ** e))
+            s = _scale_kernel(amax)
+            for X in sig[rng.choice(128, 24, replace=False)]:
+                for d in (0, 3, 11, 20, 40):
+                    x = np.float32(X * np.float32(2.0 ** (e - 1 - d)))
+                    if abs(x) <= amax:
+                        _check_div(x, s)
+                        _check_div(-x, s)
+    # +-0 and the smallest bf16 magnitudes
+    for x in (0.0, -0.0, 9.2e-41, -9.2e-41, 1.18e-38):
+        _check_div(np.float32(x), _scale_kernel(FLOOR))
+
+
+def test_division_on_cast_workload_inputs():
+    """bf16 N(0,1) rows in groups of 128: each element against its group's
+    scale, as the cast computes them."""
+    rng = ep_inputs.make_rng(21)
+    x = ep_inputs.bf16_normal(rng, (48, 128))
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    for row in xf:
+        s = _scale_kernel(np.abs(row).max())
+        for v in row:
+            _check_div(v, s)

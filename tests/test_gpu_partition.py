@@ -3,8 +3,9 @@ partition_offset, num_tokens_per_group), ep_dispatch_partitioned,
 ep_combine_partitioned and the two-level ep_combine_reduced against the
 oracle: bit-exact for the layout, the rows and the metadata; bitwise equal to
 the ordered-fp32 oracle for the combines, and within rtol = atol = 1e-2 of the
-float64 reference (the reduced combine: within the bound its bf16 partials
-allow, 2^-8 of the result plus the partials' magnitudes)."""
+float64 reference (the reduced combine with fp32 partials too; with bf16
+partials, within the bound they allow, 2^-8 of the result plus the
+partials' magnitudes)."""
 import numpy as np
 import pytest
 import torch
@@ -173,8 +174,9 @@ def test_partitioned_round_trip(gpu):
 ])
 @pytest.mark.parametrize("bias", [0, 2])
 @pytest.mark.parametrize("weighted", [True, False])
-def test_combine_reduced_parity(gpu, name, T, K, E, P, A, H, bias, weighted):
-    announce("combine_reduced", name, T, K, E, P, A, H, bias, weighted)
+@pytest.mark.parametrize("b16", [False, True])
+def test_combine_reduced_parity(gpu, name, T, K, E, P, A, H, bias, weighted, b16):
+    announce("combine_reduced", name, T, K, E, P, A, H, bias, weighted, b16)
     w = ep_inputs.make_workload(name, seed=3, T=T, K=K, E=E, with_x=False,
                                 **({} if name == "tiny" else {"A": A, "drop_p": 0.05}))
     lay = gpu.ep_get_layout(to_dev(w.topk_idx), E, A, num_partitions=P)
@@ -184,19 +186,24 @@ def test_combine_reduced_parity(gpu, name, T, K, E, P, A, H, bias, weighted):
     wt = w.topk_weights if weighted else None
     out = gpu.ep_combine_reduced(bf16_to_dev(y), lay, to_dev(w.topk_idx),
                                  to_dev(wt) if weighted else None,
-                                 bias=tuple(bf16_to_dev(bb) for bb in b) if b else None)
+                                 bias=tuple(bf16_to_dev(bb) for bb in b) if b else None,
+                                 bf16_partials=b16)
     bb = b + [None] * (2 - len(b))
     got = bf16_bits(out)
     np.testing.assert_array_equal(
-        got, oracle.combine_reduced_f32(y, w.topk_idx, exp.dst, E, P, wt, *bb))
-    # Each partition's partial is rounded to bf16 (relative error 2^-9 of the
-    # partial) and so is the result: |got - exact| <= 2^-8 (|exact| + S),
-    # S = sum of |w y| + |bias| bounding the sum of the partials' magnitudes.
+        got, oracle.combine_reduced_f32(y, w.topk_idx, exp.dst, E, P, wt, *bb, bf16_partials=b16))
     f64 = oracle.combine_f64(y, exp.dst, wt, *bb)
+    g = oracle.bf16_to_float(got).astype(np.float64)
+    if not b16:
+        # fp32 partials: the stated tolerance against float64
+        assert np.all(np.abs(g - f64) <= 1e-2 + 1e-2 * np.abs(f64))
+        return
+    # bf16 partials: each partial is rounded to bf16 (relative error 2^-9 of
+    # the partial) and so is the result: |got - exact| <= 2^-8 (|exact| + S),
+    # S = sum of |w y| + |bias| bounding the sum of the partials' magnitudes.
     absy = y & np.uint16(0x7FFF)                          # |y|: sign bit cleared
     absb = [None if v is None else v & np.uint16(0x7FFF) for v in bb]
     S = oracle.combine_f64(absy, exp.dst, None if wt is None else np.abs(wt), *absb)
-    g = oracle.bf16_to_float(got).astype(np.float64)
     assert np.all(np.abs(g - f64) <= 2.0 ** -8 * (np.abs(f64) + S) + 1e-6)
 
 

@@ -6,8 +6,8 @@ instead of scatter_add) is read as: acc = 0; acc += bias0; acc += bias1;
 then acc = fmaf(w[t,k], y[dst[t,k]], acc) for k ascending over kept pairs;
 out = bf16 round to nearest even.  The partitioned combine adds rows for
 partitions in ascending order; the two-level combine folds each partition's
-pairs (k ascending, fmaf from 0), rounds that partial to bf16, and adds the
-partials in ascending partition order after the biases.
+pairs (k ascending, fmaf from 0) and adds the partials (fp32, or rounded to
+bf16 first on request) in ascending partition order after the biases.
 
 Each step is simulated here with exact rational arithmetic and one
 round-to-nearest-even to float32 per operation (an independent fmaf), the
@@ -266,11 +266,15 @@ def test_combine_reduced_f32_two_levels(weighted, big2):
     idx, dst, y, w, b0, b1 = _reduced_case(11, 24, E, P, [1, 3, 1, 0, 1, 2, 1, 1], big2, weighted)
     if not weighted:
         w = None
-    got = oracle.combine_reduced_f32(y, idx, dst, E, P, w, b0, b1)
+    # bf16 partials
+    got = oracle.combine_reduced_f32(y, idx, dst, E, P, w, b0, b1, bf16_partials=True)
     spec = _reduced_sim(y, idx, dst, w, E, P, b0, b1)
     np.testing.assert_array_equal(got, spec)
     for order in ("k_desc",) + (("q_desc",) if big2 else ("no_round",)):
         assert (_reduced_sim(y, idx, dst, w, E, P, b0, b1, order) != spec).sum() >= 3, order
+    # fp32 partials (the default)
+    got = oracle.combine_reduced_f32(y, idx, dst, E, P, w, b0, b1)
+    np.testing.assert_array_equal(got, _reduced_sim(y, idx, dst, w, E, P, b0, b1, "no_round"))
 
 
 def test_combine_f32_uses_fused_multiply_add():

@@ -133,25 +133,31 @@ def test_reduced_combine_special_cases():
     w = ep_inputs.make_workload("prefill", T=200, H=64, E=32, K=4, A=2)
     lay = oracle.get_layout(w.topk_idx, 32, 2)
     y = ep_inputs.bf16_normal(rng, (lay.R, 64))
-    np.testing.assert_array_equal(
-        oracle.combine_reduced_f32(y, w.topk_idx, lay.dst, 32, 1, w.topk_weights),
-        oracle.combine_f32(y, lay.dst, w.topk_weights))
-    # every pair in its own partition: bf16(fp32 product) per pair, then fp32
-    # adds in partition order (numpy float32 + torch bf16 cast)
+    for b16 in (False, True):
+        np.testing.assert_array_equal(
+            oracle.combine_reduced_f32(y, w.topk_idx, lay.dst, 32, 1, w.topk_weights,
+                                       bf16_partials=b16),
+            oracle.combine_f32(y, lay.dst, w.topk_weights))
+    # every pair in its own partition: the fp32 product per pair (bf16 of it
+    # with bf16 partials), then fp32 adds in partition order (numpy float32 +
+    # torch bf16 cast)
     idx = np.stack([rng.permutation(8)[:4] for _ in range(50)]).astype(np.int64)
     wt = rng.standard_normal((50, 4)).astype(np.float32)
     lay = oracle.get_layout(idx, 8, 1)
     y = ep_inputs.bf16_normal(rng, (lay.R, 32))
-    got = oracle.combine_reduced_f32(y, idx, lay.dst, 8, 8, wt)
     yf = oracle.bf16_to_float(y)
-    expect = np.zeros((50, 32), np.uint16)
-    for t in range(50):
-        acc = np.zeros(32, np.float32)
-        for k in np.argsort(idx[t], kind="stable"):
-            prod = (wt[t, k] * yf[lay.dst[t, k]]).astype(np.float32)
-            acc = (acc + oracle.bf16_to_float(_bf16_torch(prod))).astype(np.float32)
-        expect[t] = _bf16_torch(acc)
-    np.testing.assert_array_equal(got, expect)
+    for b16 in (False, True):
+        got = oracle.combine_reduced_f32(y, idx, lay.dst, 8, 8, wt, bf16_partials=b16)
+        expect = np.zeros((50, 32), np.uint16)
+        for t in range(50):
+            acc = np.zeros(32, np.float32)
+            for k in np.argsort(idx[t], kind="stable"):
+                prod = (wt[t, k] * yf[lay.dst[t, k]]).astype(np.float32)
+                if b16:
+                    prod = oracle.bf16_to_float(_bf16_torch(prod))
+                acc = (acc + prod).astype(np.float32)
+            expect[t] = _bf16_torch(acc)
+        np.testing.assert_array_equal(got, expect)
 
 
 def test_reduced_combine_within_tolerance_of_float64():
@@ -171,14 +177,18 @@ def test_reduced_combine_error_bound(weighted):
     """With bf16 partials the error against the exact sum is at most
     2^-9 of each partial's magnitude plus 2^-9 of the result (and fp32
     rounding far below that): |out - exact| <= 2^-8 (|exact| + S) with
-    S = sum_k |w y|.  Unit weights over 8 pairs exceed a flat 1e-2 bound."""
+    S = sum_k |w y|.  Unit weights over 8 pairs exceed a flat 1e-2 bound.
+    The default fp32 partials stay within rtol = atol = 1e-2."""
     w = ep_inputs.make_workload("skewed", seed=3, T=256, K=8, E=256, A=128, drop_p=0.05,
                                 with_x=False)
     lay = oracle.get_layout(w.topk_idx, 256, 128, 32)
     y = ep_inputs.make_y(w.rng, lay.R, 512)
     wt = w.topk_weights if weighted else None
-    red = oracle.bf16_to_float(oracle.combine_reduced_f32(y, w.topk_idx, lay.dst, 256, 32, wt))
+    red = oracle.bf16_to_float(oracle.combine_reduced_f32(y, w.topk_idx, lay.dst, 256, 32, wt,
+                                                          bf16_partials=True))
     f64 = oracle.combine_f64(y, lay.dst, wt)
+    f32p = oracle.bf16_to_float(oracle.combine_reduced_f32(y, w.topk_idx, lay.dst, 256, 32, wt))
+    assert np.all(np.abs(f32p.astype(np.float64) - f64) <= 1e-2 + 1e-2 * np.abs(f64))
     S = oracle.combine_f64(y & np.uint16(0x7FFF), lay.dst, None if wt is None else np.abs(wt))
     err = np.abs(red.astype(np.float64) - f64)
     assert np.all(err <= 2.0 ** -8 * (np.abs(f64) + S) + 1e-6)
