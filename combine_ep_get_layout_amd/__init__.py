@@ -5,6 +5,7 @@ device memory and the current HIP stream; every step of the path runs in the
 library's gfx950 kernels.  The functions carry the C entry points' names:
 
   ep_get_layout(topk_idx, num_experts, ...)        -> Layout
+  ep_get_layout_noalloc(topk_idx, layout, ...)     -> layout (the library's own scratch)
   ep_dispatch(x, layout, ...)                      -> (recv_x, recv_scales, recv_topk_weights)
   ep_dispatch_with_layout(x, topk_idx, num_experts, ...)
                                                    -> (layout, recv_x, recv_scales, recv_topk_weights)
@@ -31,7 +32,8 @@ from . import _abi
 from ._abi import (EP_DEV_BAD_EXPERT, EP_DEV_CAPACITY, EP_DEV_RECV_OVERFLOW, EpError,
                    LayoutParams, LayoutPtrs)
 
-__all__ = ["load_library", "Layout", "ep_get_layout", "ep_dispatch", "ep_dispatch_with_layout",
+__all__ = ["load_library", "Layout", "ep_get_layout", "ep_get_layout_noalloc", "ep_dispatch",
+           "ep_dispatch_with_layout",
            "ep_combine", "ep_cast_fp8",
            "ep_dispatch_partitioned", "ep_combine_partitioned", "ep_combine_reduced",
            "worst_case_recv_rows", "EpError", "EP_DEV_BAD_EXPERT", "EP_DEV_CAPACITY",
@@ -216,6 +218,26 @@ def ep_get_layout(topk_idx: torch.Tensor, num_experts: int, expert_alignment: in
             _ptr(topk_idx), ctypes.byref(params), ctypes.byref(ptrs),
             _ptr(cumulative_expert_stats), _ptr(layout.workspace),
             layout.workspace.numel(), _stream(topk_idx.device))
+    return layout
+
+
+def ep_get_layout_noalloc(topk_idx: torch.Tensor, layout: Layout,
+                          cumulative_expert_stats: Optional[torch.Tensor] = None) -> Layout:
+    """ep_get_layout into an existing `layout` (same shapes) with no
+    workspace: the library's static per-GPU scratch is used instead (calls
+    that overlap on one GPU race).  Allocates nothing."""
+    lib = load_library()
+    p = layout.params
+    layout, params = _prepare_layout(topk_idx, p.num_experts, p.expert_alignment,
+                                     p.num_partitions, p.capacity, p.max_recv_rows,
+                                     cumulative_expert_stats, layout,
+                                     layout.partition_offset is not None,
+                                     p.partitions_per_group)
+    ptrs = layout.ptrs()
+    _launch("ep_get_layout_noalloc", topk_idx.device, lib.ep_get_layout_noalloc,
+            [cumulative_expert_stats, layout.status],
+            _ptr(topk_idx), ctypes.byref(params), ctypes.byref(ptrs),
+            _ptr(cumulative_expert_stats), _stream(topk_idx.device))
     return layout
 
 

@@ -30,6 +30,7 @@ EP_MAX_HIDDEN = 1 << 20
 
 # Every symbol include/ep.h declares.
 EXPORTS = ("ep_get_layout_workspace_bytes", "ep_worst_case_recv_rows", "ep_get_layout",
+           "ep_get_layout_noalloc",
            "ep_dispatch", "ep_dispatch_with_layout", "ep_combine", "ep_dispatch_partitioned", "ep_combine_partitioned",
            "ep_combine_reduced", "ep_cast_fp8", "ep_status_string")
 
@@ -77,6 +78,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ep_worst_case_recv_rows.restype = i64
     lib.ep_get_layout.argtypes = [vp, P(LayoutParams), P(LayoutPtrs), vp, vp, sz, vp]
     lib.ep_get_layout.restype = ctypes.c_int
+    lib.ep_get_layout_noalloc.argtypes = [vp, P(LayoutParams), P(LayoutPtrs), vp, vp]
+    lib.ep_get_layout_noalloc.restype = ctypes.c_int
     lib.ep_dispatch.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i32, i32, vp,
                                 P(LayoutParams), P(LayoutPtrs), vp, vp, vp, i64, ctypes.c_int, vp]
     lib.ep_dispatch.restype = ctypes.c_int

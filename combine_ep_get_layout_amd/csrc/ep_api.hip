@@ -5,6 +5,8 @@
 // build_ep_routing_table).  Nothing here allocates or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "../../include/ep.h"
 #include "ep_internal.h"
 
@@ -41,6 +43,28 @@ int check_params(const ep_layout_params *p) {
     if (p->capacity > 0 && (int64_t)p->num_experts * p->capacity > p->max_recv_rows)
         return EP_ERR_INVALID_ARG;
     return EP_OK;
+}
+
+// Scratch of ep_get_layout_noalloc: the layout workspace in device memory
+// the library itself holds for the life of the process, one copy per GPU.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// This device's copy of the scratch, looked up once per device with that
+// device current (the array's host-side name is not a device address);
+// NULL if the runtime cannot give it.
+void *device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void *q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    return q;
 }
 
 }  // namespace
@@ -88,6 +112,22 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *p, const ep_l
     const int rc = layout_checks(topk_idx, p, layout, workspace, workspace_bytes, &plan);
     if (rc != EP_OK) return rc;
     return to_status(ep::launch_layout(plan, topk_idx, layout, cumulative_expert_stats, workspace,
+                                       (hipStream_t)stream));
+}
+
+int ep_get_layout_noalloc(const int64_t *topk_idx, const ep_layout_params *p,
+                          const ep_layout *layout, int32_t *cumulative_expert_stats,
+                          void *stream) {
+    int rc = check_params(p);
+    if (rc != EP_OK) return rc;
+    ep::LayoutPlan plan;
+    if (!ep::make_layout_plan(p, &plan)) return EP_ERR_UNSUPPORTED;
+    if (plan.ws_bytes > kScratchBytes) return EP_ERR_WORKSPACE;   // before any GPU call
+    void *ws = device_scratch();
+    if (!ws) return EP_ERR_LAUNCH;
+    rc = layout_checks(topk_idx, p, layout, ws, kScratchBytes, &plan);
+    if (rc != EP_OK) return rc;
+    return to_status(ep::launch_layout(plan, topk_idx, layout, cumulative_expert_stats, ws,
                                        (hipStream_t)stream));
 }
 

@@ -159,6 +159,19 @@ int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,
                   const ep_layout *layout, int32_t *cumulative_expert_stats,
                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* ep_get_layout_noalloc - ep_get_layout with no workspace argument, for
+ * callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid it).  The workspace is a static device array
+ * the library holds for the life of the process, one per GPU, of 8 MiB;
+ * layouts whose workspace (ep_get_layout_workspace_bytes) exceeds it return
+ * EP_ERR_WORKSPACE before anything is enqueued.  Nothing is allocated.  All
+ * calls on one GPU share that array (it keeps the last call's contents;
+ * nothing in it needs to start at zero): calls that overlap on one GPU, on
+ * different streams, race.  Arguments and outputs are ep_get_layout's. */
+int ep_get_layout_noalloc(const int64_t *topk_idx, const ep_layout_params *params,
+                          const ep_layout *layout, int32_t *cumulative_expert_stats,
+                          void *stream);
+
 /* ep_dispatch - permute token rows into the receive buffer.
  * ([API] 2.1: x is bf16 [T, hidden] or the pair (fp8 codes, scales); recv_x
  *  has the input's type; do_zero_padding; 4.2 per-token cast to e4m3;

@@ -69,6 +69,19 @@ def test_get_layout_rejects_bad_params_before_launch(kw, code):
     assert rc == code
 
 
+def test_get_layout_noalloc_rejects_layouts_beyond_its_scratch():
+    """More than the static scratch holds (8 MiB) is refused on the host,
+    before any GPU call (so this runs without a GPU)."""
+    lib = _abi.load()
+    p = _params(T=2_000_000, K=8, E=256, A=1)
+    assert lib.ep_get_layout_workspace_bytes(ctypes.byref(p)) > 8 << 20
+    lay = _abi.LayoutPtrs(*([16] * 7))
+    assert lib.ep_get_layout_noalloc(ctypes.c_void_p(16), ctypes.byref(p), ctypes.byref(lay), None,
+                                     None) == _abi.EP_ERR_WORKSPACE
+    assert lib.ep_get_layout_noalloc(ctypes.c_void_p(16), ctypes.byref(_params(E=6, P=4)),
+                                     ctypes.byref(lay), None, None) == _abi.EP_ERR_INVALID_ARG
+
+
 def test_get_layout_rejects_null_buffers_and_small_workspace():
     lib = _abi.load()
     p = _params()
