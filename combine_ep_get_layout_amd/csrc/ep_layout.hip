@@ -38,7 +38,12 @@ namespace ep {
 
 namespace {
 
-constexpr int kCountBlock = 256;   // count workgroup of the two-kernel tiling: 4 waves
+// Count workgroups of the two-kernel tiling: 16 waves, one 64-pair chunk
+// each at the prefill shape (1.1 µs faster than 4 waves of four chunks),
+// while their per-wave expert counters fit LDS easily; 4 waves above that.
+constexpr int kCountBlock = 1024;
+constexpr int kCountBlockLargeE = 256;
+constexpr int kCountBlockMaxE = 1024;
 constexpr size_t kMaxLdsBytes = 160 * 1024;   // LDS one workgroup may allocate on gfx950
 constexpr int kSlotsBlock = 1024;  // slots workgroup, and the one-workgroup batch: 16 waves
 constexpr int kReduceBatch = 8;    // loads in flight per thread in column_sums
@@ -594,7 +599,7 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
     // one workgroup, in one launch.  (Measured: 12.3 -> 11.1 µs at 128 pairs;
     // already slower than the two kernels at 1,024 pairs, 13.1 -> 15.6 µs.)
     L.single = pairs > 0 && L.E <= kMaxSingleExperts && pairs <= kSinglePairs && L.T <= kSlotsBlock;
-    L.block = L.single ? kSlotsBlock : kCountBlock;
+    L.block = L.single ? kSlotsBlock : (L.E <= kCountBlockMaxE ? kCountBlock : kCountBlockLargeE);
     const int64_t per_round = L.block;   // pairs when every wave takes one 64-pair chunk
     // Chunks per wave: enough tiles to spread the count over the chip, few
     // enough that each slots workgroup reduces the [tiles, W] count rows in
