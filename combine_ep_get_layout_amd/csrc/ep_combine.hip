@@ -20,13 +20,6 @@
 #include "ep_device.h"
 #include "ep_internal.h"
 
-#ifndef EP_COMBINE_VPL
-#define EP_COMBINE_VPL 1    // 16-byte vectors per lane per row chunk (1: measured best)
-#endif
-#ifndef EP_COMBINE_U
-#define EP_COMBINE_U 4      // rows in flight per wave (0: by VPL; 4: measured best)
-#endif
-
 namespace ep {
 
 namespace {
@@ -53,6 +46,12 @@ struct CombineK {
 
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / 64;
+// One 16-byte vector per lane (1 KB of a row per wave) and four rows in
+// flight: 1.5 us faster at the prefill shape than two vectors and eight
+// rows, 0.7 us at the decode shape; eight rows in flight or two vectors
+// per lane at four rows measured no better.
+constexpr int kVpl = 1;
+constexpr int kRowsInFlight = 4;
 
 __device__ __forceinline__ void add_bf16x8(float *acc, ep_u32x4 v) {
     acc[0] = acc[0] + bf16_lo(v.x);
@@ -78,8 +77,7 @@ __device__ __forceinline__ void fma_bf16x8(float *acc, float w, ep_u32x4 v) {
 
 template <int VPL>
 __global__ void __launch_bounds__(kBlock) combine_kernel(CombineK a) {
-    constexpr int U = EP_COMBINE_U > 0 ? EP_COMBINE_U
-                                       : (VPL >= 16 ? 1 : (VPL >= 8 ? 2 : (VPL >= 4 ? 4 : 8)));
+    constexpr int U = kRowsInFlight;
     const int lane = __lane_id();
     const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
     const int t = gw / a.wpr;
@@ -171,8 +169,7 @@ __device__ __forceinline__ float partial(float p, int to_bf16) {
 // fp32 total, which starts from the biases.  Requires K <= 64.
 template <int VPL>
 __global__ void __launch_bounds__(kBlock) combine_reduced_kernel(CombineK a) {
-    constexpr int U = EP_COMBINE_U > 0 ? EP_COMBINE_U
-                                       : (VPL >= 16 ? 1 : (VPL >= 8 ? 2 : (VPL >= 4 ? 4 : 8)));
+    constexpr int U = kRowsInFlight;
     const int lane = __lane_id();
     const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
     const int t = gw / a.wpr;
@@ -285,16 +282,6 @@ __global__ void __launch_bounds__(kBlock) combine_reduced_kernel(CombineK a) {
     }
 }
 
-int choose_vpl(int nvec, int limit) {
-    static const int cand[] = {16, 14, 8, 7, 4, 2, 1};
-    const int q = (nvec + 63) / 64;
-    for (int c : cand)
-        if (c <= limit && c <= q && q % c == 0 && nvec % 64 == 0) return c;
-    for (int c : cand)
-        if (c <= limit && c <= q) return c;
-    return 1;
-}
-
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
@@ -317,26 +304,16 @@ hipError_t launch_combine(const CombineArgs &c, hipStream_t stream) {
     k.E = c.E;
     k.m = c.m;
     k.bf16_partials = c.bf16_partials;
-    const int vpl = choose_vpl(k.nvec, EP_COMBINE_VPL);
-    k.wpr = (k.nvec + vpl * 64 - 1) / (vpl * 64);
+    k.wpr = (k.nvec + kVpl * 64 - 1) / (kVpl * 64);
     if (k.wpr < 1) k.wpr = 1;
     const int64_t waves = (int64_t)k.T * k.wpr;
     const int64_t grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-#define EP_CASE(V)                                                                              \
-    case V:                                                                                     \
-        if (k.idx)                                                                              \
-            hipLaunchKernelGGL(combine_reduced_kernel<V>, dim3((unsigned)grid), dim3(kBlock), 0, \
-                               stream, k);                                                      \
-        else                                                                                    \
-            hipLaunchKernelGGL(combine_kernel<V>, dim3((unsigned)grid), dim3(kBlock), 0, stream, k); \
-        break;
-    switch (vpl) {
-        EP_CASE(1) EP_CASE(2) EP_CASE(4) EP_CASE(7) EP_CASE(8) EP_CASE(14) EP_CASE(16)
-        default: return hipErrorInvalidValue;
-    }
-#undef EP_CASE
+    if (k.idx)
+        hipLaunchKernelGGL(combine_reduced_kernel<kVpl>, dim3((unsigned)grid), dim3(kBlock), 0, stream, k);
+    else
+        hipLaunchKernelGGL(combine_kernel<kVpl>, dim3((unsigned)grid), dim3(kBlock), 0, stream, k);
     return hipGetLastError();
 }
 

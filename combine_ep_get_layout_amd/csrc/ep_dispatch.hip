@@ -25,25 +25,6 @@
 #include "ep_device.h"
 #include "ep_internal.h"
 
-#ifndef EP_DISPATCH_VPL
-#define EP_DISPATCH_VPL 16
-#endif
-#ifndef EP_CAST_VPL
-#define EP_CAST_VPL 4
-#endif
-#ifndef EP_CAST_PAIRS
-#define EP_CAST_PAIRS 1          // cast without a layout: two adjacent vectors per lane
-#endif
-#ifndef EP_DISPATCH_TPW
-#define EP_DISPATCH_TPW 2        // consecutive tokens per group in the copy modes (2: measured best)
-#endif
-#ifndef EP_PAD_ROWS_PER_SLICE
-#define EP_PAD_ROWS_PER_SLICE 4  // padding rows per workgroup when zeroing
-#endif
-#ifndef EP_DISPATCH_NT_STORE
-#define EP_DISPATCH_NT_STORE 0   // plain stores measured faster for the receive rows
-#endif
-
 namespace ep {
 
 namespace {
@@ -113,11 +94,21 @@ constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / 64;
 constexpr int kQueueStride = 64;   // uint32 between two queue counters (256 bytes)
 
-// Receive-row stores: non-temporal or plain, one switch for every mode.
+// Launch geometry, fixed from measurements at the prefill shape:
+constexpr int kRowVplLimit = 16;      // 16-byte vectors per lane: up to a 16 KB row per wave
+constexpr int kTokensPerGroup = 2;    // consecutive tokens per group in the copy modes
+                                      // (1 within noise; 4: 8% slower)
+constexpr int kPadRowsPerSlice = 4;   // padding rows per workgroup when zeroing
+constexpr int kResidentWavesPerCu = 12;      // copy modes: resident grid (156 VGPRs, three per SIMD)
+constexpr int kResidentWavesPerCuPart = 8;   // partitioned instances (179 VGPRs, two per SIMD)
+constexpr int kQueueWavesPerCu = 4;          // copy modes with the token queue
+constexpr int64_t kQueueMinTokens = 16384;   // fewer tokens: the strided resident grid instead
+
+// Receive-row stores are plain: non-temporal stores measured 3-8% slower
+// for the scattered 14 KB receive rows.
 template <typename T>
 __device__ __forceinline__ void row_store(T *p, T v) {
-    if (EP_DISPATCH_NT_STORE) __builtin_nontemporal_store(v, p);
-    else *p = v;
+    *p = v;
 }
 
 // Dynamic LDS of a dispatch workgroup that derives its layout: [tiles][W]
@@ -272,45 +263,33 @@ __device__ __forceinline__ int div_wpr(const DispatchK &a, int gw) {
     return q;
 }
 
-// Cast of one wave's chunk: per-group (or, with group_lanes == 0, per-row)
-// scales, then 8 codes per lane per vector.
+// Cast of a whole row held by one wave, with one scale per row (groups
+// narrower than the row go through the pairs kernels): the row's amax, its
+// scale, then 8 codes per lane per vector.  Returns the scale.
 template <int VPL>
-__device__ __forceinline__ void cast_chunk(const DispatchK &a, const ep_u32x4 (&v)[VPL],
-                                           float (&s)[VPL], ep_u32x2 (&q)[VPL]) {
-    if (a.group_lanes > 0) {
+__device__ __forceinline__ float cast_row(const DispatchK &a, const ep_u32x4 (&v)[VPL],
+                                          ep_u32x2 (&q)[VPL]) {
+    float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) s[i] = group_scale(a, group_max(amax8(v[i]), a.group_lanes));
-    } else {
-        float m = 0.0f;
+    for (int i = 0; i < VPL; ++i) m = fmaxf(m, amax8(v[i]));
+    const float s = group_scale(a, group_max(m, 64));
+    const float y = 1.0f / s;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) m = fmaxf(m, amax8(v[i]));
-        const float sr = group_scale(a, group_max(m, 64));
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) s[i] = sr;
-    }
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) q[i] = encode8(a, v[i], s[i], 1.0f / s[i]);
+    for (int i = 0; i < VPL; ++i) q[i] = encode8(a, v[i], s, y);
+    return s;
 }
 
-// Codes and scales of one cast chunk into receive row `slot`.
+// Codes and the scale of one cast row into receive row `slot`.
 template <int VPL>
-__device__ __forceinline__ void store_cast(const DispatchK &a, int64_t slot, int v0, int lane,
-                                           const float (&s)[VPL], const ep_u32x2 (&q)[VPL]) {
+__device__ __forceinline__ void store_cast_row(const DispatchK &a, int64_t slot, int lane, float s,
+                                               const ep_u32x2 (&q)[VPL]) {
     ep_u32x2 *dstrow = (ep_u32x2 *)(a.recv + slot * a.out_row_bytes);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        const int vi = v0 + i * 64 + lane;
+        const int vi = i * 64 + lane;
         if (vi < a.nvec) row_store(dstrow + vi, q[i]);
     }
-    if (a.group_lanes > 0) {
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int vi = v0 + i * 64 + lane;
-            if (vi < a.nvec && (vi % a.group_lanes) == 0) store_scale(a, slot, vi / a.group_lanes, s[i]);
-        }
-    } else if (lane == 0) {
-        store_scale(a, slot, 0, s[0]);
-    }
+    if (lane == 0) store_scale(a, slot, 0, s);
 }
 
 // Partitioned metadata of row (t, q) (slot; -1: this lane has no row) for
@@ -523,12 +502,11 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
         const int kn = min(64, K - kb);
 
         if (MODE == kModeCast) {
-            float s[VPL];
             ep_u32x2 q[VPL];
-            cast_chunk<VPL>(a, v, s, q);
+            const float s = cast_row<VPL>(a, v, q);
             for (int k = 0; k < kn; ++k) {
                 const int slot = lane_read(my_slot, k);
-                if (slot >= 0) store_cast<VPL>(a, slot, v0, lane, s, q);
+                if (slot >= 0) store_cast_row<VPL>(a, slot, lane, s, q);
             }
         } else {
             for (int k = 0; k < kn; ++k) {
@@ -545,23 +523,6 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
         }
     }
 }
-
-#ifndef EP_DENSE_PADDING_FILL
-#define EP_DENSE_PADDING_FILL 1   // fixed capacity, mostly padding: zero fill, then token rows
-#endif
-#ifndef EP_DISPATCH_PERSIST_PART
-#define EP_DISPATCH_PERSIST_PART 8   // the same for the partitioned instances (two per SIMD)
-#endif
-#ifndef EP_DISPATCH_QUEUE
-#define EP_DISPATCH_QUEUE 4      // copy modes with a token queue: its waves per CU
-#endif
-#ifndef EP_QUEUE_MIN_TOKENS
-#define EP_QUEUE_MIN_TOKENS 16384   // fewer tokens: the strided resident grid instead
-#endif
-#ifndef EP_DISPATCH_PERSIST
-#define EP_DISPATCH_PERSIST 12   // copy modes: waves per CU of the resident grid (the kernel's
-                                 // registers allow three per SIMD); 0: one group per wave
-#endif
 
 // fp8 copy: the token's scale row held in registers across its destinations
 // (element j in lane j % 64, slot j / 64; rows of up to 64 * kScaleRegs
@@ -699,8 +660,8 @@ __global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
 
 // Token queue of the copy modes (a layout whose count kernel just ran, whole
 // rows per wave).  The tokens are split into kXcds contiguous ranges, one per
-// XCD, each with a counter in the workspace that the layout's scan phase set
-// to zero.  A wave takes one token at a time from the counter of the XCD it
+// XCD, each with a counter in the workspace that the layout's count launch,
+// just before on the same stream, set to zero.  A wave takes one token at a time from the counter of the XCD it
 // runs on (a one-lane global atomic, the next ticket in flight while the
 // current token's rows are stored) and, once that range is used up, from the
 // other XCDs' counters in turn, so an XCD that finishes early takes tokens
@@ -921,7 +882,7 @@ hipError_t launch_queue(const DispatchK &k, int vpl, int grid, hipStream_t strea
 
 template <int MODE, bool PART>
 hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStream_t stream) {
-    if (EP_CAST_PAIRS && MODE == kModeCast && routed(k) && k.group_lanes > 0 && vpl == 2) {
+    if (MODE == kModeCast && routed(k) && k.group_lanes > 0) {
         hipLaunchKernelGGL((dispatch_cast_pairs_kernel<PART>), dim3(grid), dim3(kBlock), k.lds_bytes,
                            stream, k);
         return hipGetLastError();
@@ -929,7 +890,7 @@ hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStr
 #define EP_CASE(V)                                                                              \
     case V:                                                                                     \
         if (MODE != kModeCast && multi)                                                         \
-            hipLaunchKernelGGL((dispatch_stream_kernel<V, MODE, EP_DISPATCH_TPW, PART>),        \
+            hipLaunchKernelGGL((dispatch_stream_kernel<V, MODE, kTokensPerGroup, PART>),        \
                                dim3(grid), dim3(kBlock), k.lds_bytes, stream, k);               \
         else                                                                                    \
             hipLaunchKernelGGL((dispatch_kernel<V, MODE, PART>), dim3(grid), dim3(kBlock),      \
@@ -976,11 +937,11 @@ int choose_vpl(int nvec, int limit) {
     return 1;
 }
 
-hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
-    int vpl = choose_vpl(k.nvec, mode == kModeCast ? EP_CAST_VPL : vpl_limit);
+hipError_t run(DispatchK k, int mode, hipStream_t stream) {
+    int vpl = choose_vpl(k.nvec, kRowVplLimit);
     // cast with a layout and groups narrower than the row: two adjacent vectors
     // per lane (dispatch_cast_pairs_kernel), i.e. 128 vectors per wave
-    if (EP_CAST_PAIRS && mode == kModeCast && routed(k) && k.group_lanes > 0) vpl = 2;
+    if (mode == kModeCast && routed(k) && k.group_lanes > 0) vpl = 2;
     if (mode == kModeCast && k.group_lanes == 0) {
         // one scale per row: the whole row must sit in one wave
         const int q = (k.nvec + 63) / 64;
@@ -988,7 +949,7 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
         if (q > 16) return hipErrorInvalidValue;
     }
     // copy modes with a layout: the streaming kernel, TPW tokens per group
-    const int tpw = mode != kModeCast && routed(k) ? EP_DISPATCH_TPW : 1;
+    const int tpw = mode != kModeCast && routed(k) ? kTokensPerGroup : 1;
     const bool multi = mode != kModeCast && routed(k);
     if (multi) {
         // few tokens: split each row over more waves so the chip has work
@@ -1000,9 +961,8 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     if (k.wpr < 1) k.wpr = 1;
     k.wpr_magic = (uint32_t)(0xFFFFFFFFu / (uint32_t)k.wpr);
     // large batches of the copy modes, whole rows per wave: the token queue
-    if (EP_DISPATCH_QUEUE > 0 && multi && k.queue && k.m == 0 && k.wpr == 1 &&
-        k.T >= EP_QUEUE_MIN_TOKENS) {
-        int64_t qw = (int64_t)cu_count() * EP_DISPATCH_QUEUE;
+    if (multi && k.queue && k.m == 0 && k.wpr == 1 && k.T >= kQueueMinTokens) {
+        int64_t qw = (int64_t)cu_count() * kQueueWavesPerCu;
         if (qw > k.T) qw = k.T;
         k.n_tok_blocks = (int)((qw + kWavesPerBlock - 1) / kWavesPerBlock);
         const int64_t qgrid = (int64_t)k.n_tok_blocks + (int64_t)k.E * k.pad_slices;
@@ -1012,8 +972,8 @@ hipError_t run(DispatchK k, int mode, int vpl_limit, hipStream_t stream) {
     }
     int64_t waves = (((int64_t)k.T + tpw - 1) / tpw) * k.wpr;
     k.n_groups = (int)(((int64_t)k.T + tpw - 1) / tpw);
-    if (EP_DISPATCH_PERSIST > 0 && multi) {
-        const int per_cu = k.m > 0 ? EP_DISPATCH_PERSIST_PART : EP_DISPATCH_PERSIST;
+    if (multi) {
+        const int per_cu = k.m > 0 ? kResidentWavesPerCuPart : kResidentWavesPerCu;
         int64_t cap = (int64_t)cu_count() * per_cu / k.wpr;                // group slots
         if (cap < 1) cap = 1;
         if (k.n_groups > cap) k.n_groups = (int)cap;
@@ -1111,7 +1071,7 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     // Fixed capacity where at most one row in eight can hold a token (decode
     // batches): zero the whole region first, then write the token rows over
     // it, instead of finding each expert's padding rows.
-    if (EP_DENSE_PADDING_FILL && a.zero_padding && a.C > 0 && !a.partitioned &&
+    if (a.zero_padding && a.C > 0 && !a.partitioned &&
         (int64_t)a.T * a.K * 8 <= (int64_t)a.E * a.C) {
         int64_t rows = (int64_t)a.E * a.C;
         if (rows > a.recv_rows) rows = a.recv_rows;
@@ -1121,8 +1081,8 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
         if (!fresh) maxpad = 0;
     }
     if (maxpad > 0)
-        k.pad_slices = k.zero_padding ? (maxpad + EP_PAD_ROWS_PER_SLICE - 1) / EP_PAD_ROWS_PER_SLICE : 1;
-    return run(k, a.mode, EP_DISPATCH_VPL, stream);
+        k.pad_slices = k.zero_padding ? (maxpad + kPadRowsPerSlice - 1) / kPadRowsPerSlice : 1;
+    return run(k, a.mode, stream);
 }
 
 hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, int scale_fmt, uint8_t *q,
@@ -1144,7 +1104,7 @@ hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, int scal
     k.ng = hidden / group;
     k.group_lanes = group == hidden ? 0 : group / 8;
     k.group_shift = k.group_lanes > 0 ? __builtin_ctz((unsigned)k.group_lanes) : 0;
-    if (EP_CAST_PAIRS && k.group_lanes > 0) {
+    if (k.group_lanes > 0) {
         k.wpr = (k.nvec + 127) / 128;
         k.wpr_magic = (uint32_t)(0xFFFFFFFFu / (uint32_t)k.wpr);
         const int64_t blocks = ((int64_t)T * k.wpr + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -1153,7 +1113,7 @@ hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, int scal
         hipLaunchKernelGGL(cast_pairs_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream, k);
         return hipGetLastError();
     }
-    return run(k, kModeCast, EP_DISPATCH_VPL, stream);
+    return run(k, kModeCast, stream);
 }
 
 }  // namespace ep

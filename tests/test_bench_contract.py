@@ -27,7 +27,7 @@ def test_kernel_hash_follows_code_not_comments(tmp_path, monkeypatch):
     text = f.read_text()
     f.write_text("// a new comment line\n" + text.replace("\n", "\n  ", 3) + "\n/* trailing */\n")
     assert bench.kernel_source_hash() == h0
-    f.write_text(text.replace("EP_COMBINE_U 4", "EP_COMBINE_U 2", 1))
+    f.write_text(text.replace("kRowsInFlight = 4", "kRowsInFlight = 2", 1))
     assert bench.kernel_source_hash() != h0
     (copy / "ep_api.hip").write_text("// host layer, not hashed\n")
     f.write_text(text)
