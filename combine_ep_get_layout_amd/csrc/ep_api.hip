@@ -243,11 +243,15 @@ int ep_dispatch_with_layout(const int64_t *topk_idx, const ep_layout_params *p,
                          zero_padding, &a);
     if (rc != EP_OK) return rc;
     const hipStream_t st = (hipStream_t)stream;
-    // The count kernel alone, then dispatch kernels that derive the slots;
-    // shapes that do not allow it (one tile, the partition layout, tile rows
-    // too large for LDS) run the whole layout first.
+    // The count kernel alone, then dispatch kernels that derive the slots.
+    // Only the copy modes do: their rows run on a resident grid of a few
+    // hundred workgroups, while the cast launches one workgroup per row piece
+    // (thousands), each of which would repeat the derivation.  Shapes that do
+    // not allow it (one tile, the partition layout, tile rows too large for
+    // LDS) and the cast run the whole layout first.
     ep::FreshLayout f;
-    const bool fold = ep::fresh_layout_of(plan, layout, cumulative_expert_stats, workspace, &f);
+    const bool fold = a.mode != ep::kModeCast &&
+                      ep::fresh_layout_of(plan, layout, cumulative_expert_stats, workspace, &f);
     hipError_t err = ep::launch_layout(plan, topk_idx, layout, cumulative_expert_stats, workspace,
                                        st, fold);
     if (err != hipSuccess) return to_status(err);

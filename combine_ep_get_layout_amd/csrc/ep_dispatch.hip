@@ -29,8 +29,6 @@ namespace ep {
 
 namespace {
 
-enum { kModeCopy16 = 0, kModeCopyFp8 = 1, kModeCast = 2 };
-
 struct DispatchK {
     const uint8_t *x;
     const uint8_t *x_scales;  // [T, ng] scales of fp8 x: fp32, or UE8M0 bytes
@@ -461,7 +459,6 @@ __device__ __forceinline__ void pad_rows(const DispatchK &a, int pb) {
 
 template <int VPL, int MODE, bool PART>
 __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
-    if (a.packed) fresh_setup(a, [] {});
     if ((int)blockIdx.x >= a.n_tok_blocks) {
         if (PART && a.meta_rows) meta_rows(a, (int)blockIdx.x - a.n_tok_blocks);
         else pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
@@ -472,7 +469,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
     const int t = gw / a.wpr;
     const int ci = gw - t * a.wpr;
     if (t >= a.T) return;
-    const int K = (a.dst || a.packed) ? a.nd : 1;
+    const int K = a.dst ? a.nd : 1;
     const int v0 = ci * VPL * 64;
 
     // Load this wave's chunk of the row once.
@@ -490,8 +487,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_kernel(DispatchK a) {
         int my_slot = -1;
         float my_w = 1.0f;
         if (kb + lane < K) {
-            my_slot = (a.dst || a.packed) ? pair_slot(a, t, kb + lane) : t;
-            if (a.packed && ci == 0) record_slot(a, t, kb + lane, my_slot);
+            my_slot = a.dst ? a.dst[(int64_t)t * a.nd + kb + lane] : t;
             if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
         }
         if ((int64_t)my_slot >= a.recv_rows) {
@@ -815,7 +811,6 @@ __global__ void __launch_bounds__(kBlock) cast_pairs_kernel(DispatchK a) {
 // workgroups follow the token ones, as in dispatch_kernel.
 template <bool PART>
 __global__ void __launch_bounds__(kBlock) dispatch_cast_pairs_kernel(DispatchK a) {
-    if (a.packed) fresh_setup(a, [] {});
     if ((int)blockIdx.x >= a.n_tok_blocks) {
         if (PART && a.meta_rows) meta_rows(a, (int)blockIdx.x - a.n_tok_blocks);
         else pad_rows(a, (int)blockIdx.x - a.n_tok_blocks);
@@ -843,8 +838,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_cast_pairs_kernel(DispatchK a
         int my_slot = -1;
         float my_w = 1.0f;
         if (kb + lane < a.nd) {
-            my_slot = pair_slot(a, t, kb + lane);
-            if (a.packed && ci == 0) record_slot(a, t, kb + lane, my_slot);
+            my_slot = a.dst[(int64_t)t * a.nd + kb + lane];
             if (a.w && a.m == 0) my_w = a.w[(int64_t)t * a.K + kb + lane];
         }
         if ((int64_t)my_slot >= a.recv_rows) {
@@ -1027,7 +1021,8 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
     k.meta_rows = a.partitioned && a.part_src && a.part_offset && (a.recv_idx || a.recv_wk);
     if (a.partitioned) k.dst = a.token_slot;
     k.queue = a.partitioned ? nullptr : a.queue;
-    const bool fresh = a.fresh != nullptr && !a.partitioned;
+    // a layout derived in the row kernels: the copy modes' resident grids only
+    const bool fresh = a.fresh != nullptr && !a.partitioned && a.mode != kModeCast;
     if (fresh) {
         const FreshLayout &f = *a.fresh;
         k.dst = nullptr;

@@ -79,6 +79,10 @@ bool fresh_layout_of(const LayoutPlan &plan, const ep_layout *layout, int32_t *c
 // The token-queue counters in a layout workspace.
 uint32_t *queue_of(const LayoutPlan &plan, void *workspace);
 
+// Row modes of a dispatch: bf16 rows copied, fp8 rows copied with their
+// scales, bf16 rows cast to fp8 on the way.
+enum { kModeCopy16 = 0, kModeCopyFp8 = 1, kModeCast = 2 };
+
 struct DispatchArgs {
     const void *x;
     const void *x_scales;          // fp32 or UE8M0 bytes [T, hidden/group]
@@ -94,7 +98,7 @@ struct DispatchArgs {
     int T, K, E, A, C;
     int hidden;
     int group;                     // fp8 scale group (0 when bf16 -> bf16)
-    int mode;                      // 0 copy bf16, 1 copy fp8 (+scales), 2 cast bf16 -> fp8
+    int mode;                      // kModeCopy16, kModeCopyFp8 or kModeCast
     int scale_fmt;                 // 0 fp32 amax/448, 1 fp32 power of two, 2 UE8M0 byte
     int zero_padding;
     // partitioned (non-expanded) dispatch

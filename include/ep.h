@@ -216,10 +216,11 @@ int ep_dispatch(const void *x, int x_dtype, const void *x_scales, int recv_dtype
  * buffers) is bit for bit what the two calls in sequence write.  Only the
  * layout's count kernel runs before the rows: each dispatch workgroup
  * derives the offsets and its pairs' slots from the count kernel's tile rows
- * in LDS and writes dst_slot / src_of_slot as it goes.  Shapes where that
- * does not apply (a batch of one count tile, the partition layout requested
- * through layout->token_slot or partition_offset, tile rows beyond 64 KB)
- * run the two calls' kernels as they are.  The workspace is ep_get_layout's.
+ * in LDS and writes dst_slot / src_of_slot as it goes.  That applies to
+ * the copy modes (bf16 and fp8 rows as they are); the bf16 -> fp8 cast, a
+ * batch of one count tile, the partition layout requested through
+ * layout->token_slot or partition_offset, and tile rows beyond 64 KB run the
+ * two calls' kernels as they are.  The workspace is ep_get_layout's.
  * Errors: those of ep_get_layout and ep_dispatch, checked before anything is
  * enqueued. */
 int ep_dispatch_with_layout(const int64_t *topk_idx, const ep_layout_params *params,
