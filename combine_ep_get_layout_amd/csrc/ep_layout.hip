@@ -296,7 +296,9 @@ __device__ void column_sums(const int32_t *__restrict__ mat, int rows, int cols,
                 tot[c] = s;
                 pre[c] = sp;
             }
-        } else if (q < Q) {
+        } else if (g < G && q < Q) {
+            // one partial per column: only the threads that summed it write
+            // (with Q in (nt/2, nt] the threads past the first span hold none)
             for (int j = 0; j < vec; ++j) {
                 tot[q * vec + j] = at[j];
                 pre[q * vec + j] = ap[j];

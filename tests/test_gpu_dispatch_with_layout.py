@@ -144,6 +144,9 @@ def test_with_layout_skewed_full_size(gpu):
     (33, 8, 512, 1, 7168, 0.05),   # 264 pairs: just past the one-workgroup batch
     (9000, 8, 256, 16, 2048, 0.05),  # many tiles, ragged tail
     (5, 3, 4, 2, 8, 0.0),
+    (150, 8, 2048, 4, 256, 0.1),   # E > 1024: 4-wave count workgroups, slots still derived
+    (2000, 8, 2048, 1, 128, 0.0),  # tile rows beyond the row kernels' LDS: two-kernel layout
+    (16387, 4, 64, 2, 256, 0.05),  # token queue, XCD ranges of unequal length
 ])
 def test_with_layout_shapes(gpu, T, K, E, A, H, drop):
     rng = ep_inputs.make_rng(T * 13 + K)
@@ -199,6 +202,38 @@ def test_with_layout_fp8_copy_and_zero_padding(gpu):
     exp, exp_s, _ = oracle.dispatch(q, ref, wt, x_scales=s, zero_padding=True)
     np.testing.assert_array_equal(recv[:ref.R].view(torch.uint8).cpu().numpy(), exp)
     np.testing.assert_array_equal(rs[:ref.R].cpu().numpy(), exp_s)
+
+
+@pytest.mark.parametrize("zero_padding", [False, True])
+def test_with_layout_fp8_copy_token_queue(gpu, zero_padding):
+    """fp8 rows with fp32 scales at T >= 16,384: the queue kernel's fp8 copy
+    (scale rows held in registers), padding workgroups appended to it."""
+    T, H, G = 16400, 512, 128
+    idx, wt = _prefill_like(T, seed=31)
+    xb = ep_inputs.bf16_normal(ep_inputs.make_rng(32), (T, H))
+    q, s = oracle.cast_fp8(xb, G)
+    x8 = (torch.from_numpy(q).to(DEV).view(torch.float8_e4m3fn), to_dev(s))
+    _, (recv, rs, rw), ref = _run(gpu, idx, wt, x8, 256, 128, G=G, zero_padding=zero_padding)
+    exp, exp_s, exp_w = oracle.dispatch(q, ref, wt, x_scales=s, zero_padding=zero_padding)
+    used = ref.src_of_slot >= 0
+    rows = slice(None) if zero_padding else used
+    np.testing.assert_array_equal(recv[:ref.R].view(torch.uint8).cpu().numpy()[rows], exp[rows])
+    np.testing.assert_array_equal(rs[:ref.R].cpu().numpy()[rows], exp_s[rows])
+    np.testing.assert_array_equal(rw[:ref.R].cpu().numpy(), exp_w)
+
+
+def test_with_layout_token_queue_fixed_capacity(gpu):
+    """The queue kernel with a fixed capacity: pairs past C dropped (status
+    bit), every expert's unused rows visited by the padding workgroups."""
+    T, K, E, C, H = 16500, 2, 64, 512, 64
+    rng = ep_inputs.make_rng(33)
+    idx, wt = ep_inputs.routing_uniform(rng, T, E, K)
+    xb = ep_inputs.bf16_normal(rng, (T, H))
+    _, (recv, _, rw), ref = _run(gpu, idx, wt, bf16_to_dev(xb), E, 1, 1, C, zero_padding=True)
+    assert ref.status & oracle.CAPACITY
+    exp, _, exp_w = oracle.dispatch(xb, ref, wt, zero_padding=True)
+    np.testing.assert_array_equal(recv.view(torch.int16).cpu().numpy().view(np.uint16), exp)
+    np.testing.assert_array_equal(rw.cpu().numpy(), exp_w)
 
 
 def test_with_layout_decode_fixed_capacity(gpu):

@@ -41,6 +41,12 @@ def test_layout_workloads_full_size(gpu, name):
     (1, 1, 1, 1, 1, 0.0),
     (3, 8, 256, 128, 32, 0.3),
     (777, 8, 4096, 2, 64, 0.02),   # largest E; 64-bit partition masks
+    # tile rows of 513..1024 column quads: one partial per column in the slots
+    # kernel's column sums, with threads past the first span holding none
+    (150, 8, 2048, 4, 1, 0.1),     # 513 quads
+    (600, 8, 3000, 1, 8, 0.05),    # 753 quads
+    (300, 4, 4080, 1, 4, 0.0),     # 1,022 quads
+    (700, 8, 1500, 2, 4, 0.05),    # 377 quads: two partials per column
     (513, 4, 256, 16, 128, 0.05),  # more than 64 partitions
     (2049, 1, 7, 5, 7, 0.0),       # K = 1, odd E
     (300, 64, 512, 1, 2, 0.5),     # K = 64: a token fills a whole wave chunk
