@@ -101,3 +101,56 @@ def test_random_shape_whole_path(gpu, case):
         np.testing.assert_array_equal(rs[:R].cpu().numpy().view(np.uint32),
                                       exp_s[:R].view(np.uint32))
     assert lay.check() == 0
+
+
+def _layout_cases(n=int(os.environ.get("EP_RANDOM_LAYOUT_CASES", "32")), seed=20261204):
+    """Layout-heavy shapes over the whole expert range: E log-uniform in
+    [1, 4096] (so the tile rows take every width the column sums and the row
+    kernels' LDS see), T up to 20,000, K up to 16, P up to 1,024."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(np.clip(np.round(np.exp(rng.uniform(0, np.log(4096)))), 1, 4096))
+        K = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.choice([0, 1, 100, 257, 1000, 3000, 9000, 20000]))
+        A = int(rng.choice([1, 2, 4, 16, 128]))
+        divs = [p for p in range(1, min(E, 1024) + 1) if E % p == 0]
+        P = int(rng.choice(divs))
+        C = 0 if rng.random() < 0.75 else A * int(rng.integers(1, 9))
+        drop = float(rng.choice([0.0, 0.05, 0.5]))
+        out.append((i, T, K, E, A, P, C, drop))
+    return out
+
+
+@pytest.mark.parametrize("case", _layout_cases(), ids=lambda c: f"l{c[0]}")
+def test_random_layout_both_paths(gpu, case):
+    """ep_get_layout and ep_dispatch_with_layout against the oracle: every
+    layout buffer, and the one-call path's receive rows (H = 16)."""
+    i, T, K, E, A, P, C, drop = case
+    announce("random layout", case)
+    rng = ep_inputs.make_rng(5000 + i)
+    idx, wts = ep_inputs.routing_uniform(rng, T, E, K)
+    idx[rng.random((T, K)) < drop] = -1
+    H = 16
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    lay = gpu.ep_get_layout(to_dev(idx), E, A, P, C)
+    ref = oracle.get_layout(idx, E, A, P, C, rows_cap=lay.max_recv_rows)
+    R = min(ref.R, lay.max_recv_rows)
+
+    def check(l):
+        torch.cuda.synchronize()
+        assert int(l.status.item()) == ref.status
+        np.testing.assert_array_equal(l.num_tokens_per_expert.cpu().numpy(), ref.count)
+        np.testing.assert_array_equal(l.expert_offset.cpu().numpy(), ref.offset)
+        np.testing.assert_array_equal(l.dst_slot.cpu().numpy(), ref.dst)
+        np.testing.assert_array_equal(l.is_token_in_partition.cpu().numpy(), ref.in_part)
+        np.testing.assert_array_equal(l.num_tokens_per_partition.cpu().numpy(), ref.tok_per_part)
+        np.testing.assert_array_equal(l.src_of_slot[:R].cpu().numpy(), ref.src_of_slot[:R])
+
+    check(lay)
+    lay2, recv, _, rw = gpu.ep_dispatch_with_layout(bf16_to_dev(x), to_dev(idx), E, A,
+                                                    to_dev(wts), P, C, zero_padding=True)
+    check(lay2)
+    exp, _, exp_w = oracle.dispatch(x, ref, wts, zero_padding=True)
+    np.testing.assert_array_equal(bf16_bits(recv[:R]), exp[:R])
+    np.testing.assert_array_equal(rw[:R].cpu().numpy(), exp_w[:R])
