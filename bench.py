@@ -1,8 +1,9 @@
 """Benchmark: MoE dispatch + combine on one MI355X.
 
-One step = the whole hot path over one batch: ep_get_layout (routing count,
-padded scan, slot map) -> ep_dispatch (bf16 row scatter) -> ep_combine
-(weighted reduction back to the tokens), on the prefill workload: 4096
+One step = the whole hot path over one batch: ep_dispatch_with_layout
+(routing count, padded scan and slot map, bf16 row scatter, in one call)
+-> ep_combine (weighted reduction back to the tokens), on the prefill
+workload: 4096
 tokens x hidden 7168 bf16, 256 experts, top-8 from unbalanced gate scores,
 ~2% of slots -1, expert_alignment 128.  Inputs are resident in HBM before
 the timed region.
@@ -15,9 +16,12 @@ The headline region runs the K steps back to back between two events on
 the launch stream.  Per-kernel durations come from HIP events on the same
 stream around K back-to-back launches of each operation (an event record
 between launches would leave a few microseconds of idle GPU time);
-`roofline` reports the longer of the two row kernels against MI355X's 8 TB/s
-HBM peak.  `cpu_baseline` times the CPU
-oracle on the same whole batch, on one thread and on the host's threads.
+`roofline` reports the longer of the two row kernels (the dispatch rows are
+timed on a reused layout, where the call is that one kernel) against
+MI355X's 8 TB/s HBM peak.  `cold_cache` times each operation after a 768 MiB
+flush, `torch_reference` PyTorch's own index_copy_ / index_select over the
+same routed slots, and `cpu_baseline` the CPU oracle on the same whole batch,
+on one thread and on the host's threads.
 """
 from __future__ import annotations
 
