@@ -106,15 +106,19 @@ _F32 = (torch.float32,)
 _I64 = (torch.int64,)
 
 
-def worst_case_recv_rows(num_tokens, num_topk, num_experts, expert_alignment=1, capacity=0) -> int:
-    p = LayoutParams(num_tokens, num_topk, num_experts, expert_alignment, 1, capacity, 0, 0)
+def worst_case_recv_rows(num_tokens, num_topk, num_experts, expert_alignment=1, capacity=0,
+                         num_partitions=1, partition_major=False) -> int:
+    p = LayoutParams(num_tokens=num_tokens, num_topk=num_topk, num_experts=num_experts,
+                     expert_alignment=expert_alignment, num_partitions=num_partitions,
+                     capacity=capacity, partition_major=1 if partition_major else 0)
     return int(load_library().ep_worst_case_recv_rows(ctypes.byref(p)))
 
 
 class Layout:
     """Device-resident receive layout (the dispatch "handle").
 
-    Tensors: num_tokens_per_expert [E], expert_offset [E+1] (R at [E]),
+    Tensors: num_tokens_per_expert [S], expert_offset [S+1] (R at [S]), S the
+    receive segments (E, or P for a partition-major layout),
     num_tokens_per_partition [P], is_token_in_partition [T, P] uint8,
     dst_slot [T, K], src_of_slot [max_recv_rows], status [1]; with the
     partition layout also partition_offset [P+1], num_tokens_per_group [P/G]
@@ -122,12 +126,13 @@ class Layout:
     each partition row) (else None)."""
 
     def __init__(self, params: LayoutParams, device, partition_layout: bool = False):
-        T, K, E, P = params.num_tokens, params.num_topk, params.num_experts, params.num_partitions
+        T, K, P = params.num_tokens, params.num_topk, params.num_partitions
+        S = P if params.partition_major else params.num_experts
         i32 = dict(dtype=torch.int32, device=device)
         self.params = params
         self.device = device
-        self.num_tokens_per_expert = torch.empty(E, **i32)
-        self.expert_offset = torch.empty(E + 1, **i32)
+        self.num_tokens_per_expert = torch.empty(S, **i32)
+        self.expert_offset = torch.empty(S + 1, **i32)
         self.num_tokens_per_partition = torch.empty(P, **i32)
         self.is_token_in_partition = torch.empty((T, P), dtype=torch.uint8, device=device)
         self.dst_slot = torch.empty((T, K), **i32)
@@ -156,6 +161,15 @@ class Layout:
     @property
     def num_experts(self):
         return self.params.num_experts
+
+    @property
+    def partition_major(self) -> bool:
+        return bool(self.params.partition_major)
+
+    @property
+    def num_segments(self) -> int:
+        """Receive segments: experts, or partitions when partition-major."""
+        return self.params.num_partitions if self.params.partition_major else self.params.num_experts
 
     @property
     def max_recv_rows(self) -> int:
@@ -201,17 +215,20 @@ def ep_get_layout(topk_idx: torch.Tensor, num_experts: int, expert_alignment: in
                   max_recv_rows: Optional[int] = None,
                   cumulative_expert_stats: Optional[torch.Tensor] = None,
                   layout: Optional[Layout] = None, partition_layout: bool = False,
-                  partitions_per_group: int = 0) -> Layout:
+                  partitions_per_group: int = 0, partition_major: bool = False) -> Layout:
     """Derive the receive layout from topk_idx (int64 [T, K], -1 = none).
     capacity > 0 selects the fixed-capacity ("expand") layout.
     partition_layout=True also derives the non-expanded per-partition layout
     (token_slot etc., P <= 64); partitions_per_group sets G for
-    num_tokens_per_group (0: one group).  A `layout` of the same shape may be
-    passed in to be rewritten in place."""
+    num_tokens_per_group (0: one group).  partition_major=True groups the
+    receive rows by partition instead of expert (pairs in (t, k) order inside
+    each partition's segment; the per-expert tables then hold one entry per
+    partition).  A `layout` of the same shape may be passed in to be
+    rewritten in place."""
     lib = load_library()
     layout, params = _prepare_layout(topk_idx, num_experts, expert_alignment, num_partitions,
                                      capacity, max_recv_rows, cumulative_expert_stats, layout,
-                                     partition_layout, partitions_per_group)
+                                     partition_layout, partitions_per_group, partition_major)
     ptrs = layout.ptrs()
     _launch("ep_get_layout", topk_idx.device, lib.ep_get_layout,
             [cumulative_expert_stats, layout.workspace, layout.status],
@@ -232,7 +249,7 @@ def ep_get_layout_noalloc(topk_idx: torch.Tensor, layout: Layout,
                                      p.num_partitions, p.capacity, p.max_recv_rows,
                                      cumulative_expert_stats, layout,
                                      layout.partition_offset is not None,
-                                     p.partitions_per_group)
+                                     p.partitions_per_group, bool(p.partition_major))
     ptrs = layout.ptrs()
     _launch("ep_get_layout_noalloc", topk_idx.device, lib.ep_get_layout_noalloc,
             [cumulative_expert_stats, layout.status],
@@ -243,32 +260,37 @@ def ep_get_layout_noalloc(topk_idx: torch.Tensor, layout: Layout,
 
 def _prepare_layout(topk_idx, num_experts, expert_alignment, num_partitions, capacity,
                     max_recv_rows, cumulative_expert_stats, layout, partition_layout,
-                    partitions_per_group):
+                    partitions_per_group, partition_major=False):
     """(layout, params) for a layout call: a new Layout, or `layout` checked
     against these shapes."""
     _need_cuda(topk_idx, "topk_idx")
     if topk_idx.dtype != torch.int64 or topk_idx.dim() != 2:
         raise ValueError("topk_idx must be int64 [T, K]")
     T, K = topk_idx.shape
+    pm = 1 if partition_major else 0
     if max_recv_rows is None:
-        max_recv_rows = worst_case_recv_rows(T, K, num_experts, expert_alignment, capacity)
-    params = LayoutParams(T, K, num_experts, expert_alignment, num_partitions, capacity,
-                          partitions_per_group, int(max_recv_rows))
+        max_recv_rows = worst_case_recv_rows(T, K, num_experts, expert_alignment, capacity,
+                                             num_partitions, partition_major)
+    params = LayoutParams(num_tokens=T, num_topk=K, num_experts=num_experts,
+                          expert_alignment=expert_alignment, num_partitions=num_partitions,
+                          capacity=capacity, partitions_per_group=partitions_per_group,
+                          partition_major=pm, max_recv_rows=int(max_recv_rows))
     if layout is None:
         layout = Layout(params, topk_idx.device, partition_layout)
     elif ((layout.params.num_tokens, layout.params.num_topk, layout.params.num_experts,
            layout.params.num_partitions, layout.params.max_recv_rows,
-           layout.params.partitions_per_group or num_partitions)
+           layout.params.partitions_per_group or num_partitions, layout.params.partition_major)
           != (T, K, num_experts, num_partitions, int(max_recv_rows),
-              partitions_per_group or num_partitions)
+              partitions_per_group or num_partitions, pm)
           or (layout.partition_offset is not None) != partition_layout):
         raise ValueError("layout buffers do not match these shapes")
     else:
         layout.params = params
     if cumulative_expert_stats is not None:
         _need_cuda(cumulative_expert_stats, "cumulative_expert_stats")
-        if cumulative_expert_stats.dtype != torch.int32 or cumulative_expert_stats.numel() != num_experts:
-            raise ValueError("cumulative_expert_stats must be int32 [num_experts]")
+        S = num_partitions if partition_major else num_experts
+        if cumulative_expert_stats.dtype != torch.int32 or cumulative_expert_stats.numel() != S:
+            raise ValueError("cumulative_expert_stats must be int32 [receive segments]")
     return layout, params
 
 
@@ -331,7 +353,7 @@ def ep_dispatch_with_layout(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Ten
                             scale_group: int = 128, zero_padding: bool = False,
                             num_recv_rows: Optional[int] = None,
                             out: Optional[Sequence[Optional[torch.Tensor]]] = None,
-                            scale_fmt: str = "fp32"):
+                            scale_fmt: str = "fp32", partition_major: bool = False):
     """ep_get_layout followed by ep_dispatch in one call (the layout's slots
     are derived by the dispatch kernels).  Arguments as the two calls; returns
     (layout, recv_x, recv_scales or None, recv_topk_weights or None), bit for
@@ -339,7 +361,7 @@ def ep_dispatch_with_layout(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Ten
     lib = load_library()
     layout, params = _prepare_layout(topk_idx, num_experts, expert_alignment, num_partitions,
                                      capacity, max_recv_rows, cumulative_expert_stats, layout,
-                                     False, 0)
+                                     False, 0, partition_major)
     x, x_scales, scale_group, x_dtype, recv_dtype, scale_fmt = _x_and_dtypes(
         x, recv_fp8, scale_group, scale_fmt)
     recv_x, recv_s, recv_w, rows = _dispatch_buffers(x, layout, topk_weights, recv_dtype,

@@ -39,7 +39,8 @@ class LayoutParams(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("num_topk", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("expert_alignment", ctypes.c_int32),
                 ("num_partitions", ctypes.c_int32), ("capacity", ctypes.c_int32),
-                ("partitions_per_group", ctypes.c_int32), ("max_recv_rows", ctypes.c_int64)]
+                ("partitions_per_group", ctypes.c_int32), ("partition_major", ctypes.c_int32),
+                ("max_recv_rows", ctypes.c_int64)]
 
 
 class LayoutPtrs(ctypes.Structure):

@@ -21,6 +21,11 @@ int to_status(hipError_t e) {
     return e == hipErrorInvalidConfiguration ? EP_ERR_UNSUPPORTED : EP_ERR_LAUNCH;
 }
 
+// Receive segments of a layout: one per expert, or one per partition.
+int64_t segments(const ep_layout_params *p) {
+    return p->partition_major ? p->num_partitions : p->num_experts;
+}
+
 // Shape checks shared by every call that takes layout params.
 int check_params(const ep_layout_params *p) {
     if (!p) return EP_ERR_INVALID_ARG;
@@ -31,6 +36,7 @@ int check_params(const ep_layout_params *p) {
     if (p->partitions_per_group < 0 ||
         (p->partitions_per_group > 0 && p->num_partitions % p->partitions_per_group != 0))
         return EP_ERR_INVALID_ARG;
+    if (p->partition_major != 0 && p->partition_major != 1) return EP_ERR_INVALID_ARG;
     if (p->capacity > 0 && p->capacity % p->expert_alignment != 0) return EP_ERR_INVALID_ARG;
     if (p->num_experts > EP_MAX_EXPERTS || p->num_partitions > EP_MAX_PARTITIONS)
         return EP_ERR_UNSUPPORTED;
@@ -40,7 +46,7 @@ int check_params(const ep_layout_params *p) {
     const int64_t worst = ep_worst_case_recv_rows(p);
     if (worst >= ((int64_t)1 << 31)) return EP_ERR_INVALID_ARG;
     if ((int64_t)p->num_tokens * p->num_partitions >= ((int64_t)1 << 40)) return EP_ERR_INVALID_ARG;
-    if (p->capacity > 0 && (int64_t)p->num_experts * p->capacity > p->max_recv_rows)
+    if (p->capacity > 0 && segments(p) * p->capacity > p->max_recv_rows)
         return EP_ERR_INVALID_ARG;
     return EP_OK;
 }
@@ -73,9 +79,10 @@ extern "C" {
 
 int64_t ep_worst_case_recv_rows(const ep_layout_params *p) {
     if (!p) return 0;
-    if (p->capacity > 0) return (int64_t)p->num_experts * p->capacity;
+    const int64_t S = p->partition_major == 1 ? p->num_partitions : p->num_experts;
+    if (p->capacity > 0) return S * p->capacity;
     const int64_t pairs = (int64_t)p->num_tokens * p->num_topk;
-    const int64_t ne = pairs < p->num_experts ? pairs : p->num_experts;
+    const int64_t ne = pairs < S ? pairs : S;
     return pairs + ne * (int64_t)(p->expert_alignment - 1);
 }
 
@@ -205,7 +212,7 @@ static int dispatch_checks(const void *x, int x_dtype, const void *x_scales, int
     a.recv_rows = num_recv_rows;
     a.T = p->num_tokens;
     a.K = p->num_topk;
-    a.E = p->num_experts;
+    a.E = (int)segments(p);   // the receive segments the padding workgroups visit
     a.A = p->expert_alignment;
     a.C = p->capacity;
     a.hidden = hidden;

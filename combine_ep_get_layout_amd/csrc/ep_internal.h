@@ -14,7 +14,9 @@ constexpr size_t kQueueBytes = 8 * 256;
 
 // Tiling of the layout pass, chosen on the host from the shapes alone.
 struct LayoutPlan {
-    int T, K, E, A, P, C;
+    int T, K, E, A, P, C;   // E: receive segments (experts, or partitions when partition-major)
+    int E_ids;              // expert ids are valid in [0, E_ids)
+    int seg_div;            // an expert's segment is id / seg_div (1, or E_ids / P)
     int64_t max_rows;
     int tile_tokens;   // tokens per count tile (one workgroup)
     int num_tiles;     // ceil(T / tile_tokens)
@@ -23,7 +25,7 @@ struct LayoutPlan {
     bool prescan;      // many tiles: a scan kernel turns the tile rows into prefixes first
     int chunks_per_wave;
     int G, NG;              // partitions per group, number of groups
-    int row_stride;         // ints per tile row: E + P + NG + 1 rounded up to 4
+    int row_stride;         // ints per tile row: E + P + NG + 1 rounded up to 4 (E segments)
     size_t ws_queue;        // byte offsets inside the workspace: the dispatch's token queue,
     size_t ws_rows;         //   [tiles + 1, row_stride] count rows,
     size_t ws_packed;       //   [T*K] (expert << 12) | rank in tile,
@@ -95,7 +97,7 @@ struct DispatchArgs {
     void *recv_scales;
     float *recv_w;
     int64_t recv_rows;
-    int T, K, E, A, C;
+    int T, K, E, A, C;             // E: receive segments (expanded), experts (partitioned)
     int hidden;
     int group;                     // fp8 scale group (0 when bf16 -> bf16)
     int mode;                      // kModeCopy16, kModeCopyFp8 or kModeCast

@@ -1,5 +1,10 @@
 // Layout pass: routing histogram, padded per-expert offsets and the
-// source -> destination slot map.
+// source -> destination slot map.  "Expert" below stands for the receive
+// segment: the expert itself, or with partition_major its partition (the
+// pair's expert id divided by E/P).  Partitions stand for the ranks of
+// "DeepEP test target API reference" sec. 3.1 (per-rank layout tensors), and
+// the multi-level combine of sec. 2.2 reduces rank by rank; a receive buffer
+// grouped by partition is that rank-major order.
 //
 // Computes what the DeepEP v2 test page ("DeepEP test target API reference",
 // sec. 2.1 dispatch parameters, sec. 3.1 V1 layout tensors, sec. 4.2 align)
@@ -61,7 +66,9 @@ constexpr int kRedInts = 2 * 4 * kSlotsBlock;
 
 struct CountArgs {
     const int64_t *idx;
-    int T, K, E, P, m;
+    int T, K, E, P, m;      // E: receive segments; m: experts per partition
+    int E_ids;              // ids are valid in [0, E_ids)
+    int seg_div;            // segment of an id: id / seg_div
     int tile_tokens;
     int tile_pairs_max;
     int G, NG;              // partitions per group, groups
@@ -101,9 +108,10 @@ struct SlotsArgs {
                                 // num_tiles, the totals
 };
 
-// Count phase for tile blockIdx.x.  LDS: [waves][E] counters, [tile pairs]
-// expert ids, [P] partition counters.  On return rank[c] / ex[c] hold the
-// tile rank and expert of pair (wave * cpw + c) * 64 + lane (ex = -1: none).
+// Count phase for tile blockIdx.x.  LDS: [waves][E] counters (one per
+// receive segment), [tile pairs] expert ids, [P] partition counters.  On
+// return rank[c] / ex[c] hold the tile rank and segment of pair
+// (wave * cpw + c) * 64 + lane (ex = -1: none).
 __device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
                             int rank[kMaxChunksPerWave], int ex[kMaxChunksPerWave], int &cpw) {
     const int nw = blockDim.x >> 6;
@@ -144,10 +152,12 @@ __device__ void count_phase(const CountArgs &a, int32_t *lds, int32_t *s_flag,
         if (c < cpw) {
             const int p = (w * cpw + c) * 64 + lane;
             const int64_t v = raw[c];
-            int e = -1;
-            if (v >= 0 && v < E) e = (int)v;
+            int id = -1;
+            if (v >= 0 && v < a.E_ids) id = (int)v;
             else if (v != -1) flag = 1;
-            if (p < npairs) pe[p] = e;
+            if (p < npairs) pe[p] = id;   // the expert id, for partition membership
+            // the pair's receive segment: its expert, or its partition
+            const int e = id < 0 ? -1 : (a.seg_div == 1 ? id : id / a.seg_div);
             // Lanes naming the same expert: intersect one ballot per id bit.
             const uint64_t active = __ballot(e >= 0);
             uint64_t match = active;
@@ -591,7 +601,9 @@ bool make_layout_plan(const ep_layout_params *p, LayoutPlan *plan) {
     LayoutPlan L;
     L.T = p->num_tokens;
     L.K = p->num_topk;
-    L.E = p->num_experts;
+    L.E_ids = p->num_experts;
+    L.seg_div = p->partition_major ? p->num_experts / p->num_partitions : 1;
+    L.E = p->num_experts / L.seg_div;   // receive segments
     L.A = p->expert_alignment;
     L.P = p->num_partitions;
     L.C = p->capacity;
@@ -640,8 +652,10 @@ hipError_t launch_layout(const LayoutPlan &L, const int64_t *topk_idx, const ep_
     ca.T = L.T;
     ca.K = L.K;
     ca.E = L.E;
+    ca.E_ids = L.E_ids;
+    ca.seg_div = L.seg_div;
     ca.P = L.P;
-    ca.m = L.E / L.P;
+    ca.m = L.E_ids / L.P;
     ca.tile_tokens = L.tile_tokens;
     ca.tile_pairs_max = L.tile_tokens * L.K;
     ca.in_part = lay->is_token_in_partition;

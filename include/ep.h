@@ -88,16 +88,29 @@ typedef struct ep_layout_params {
                                /* [e*C, (e+1)*C); requires C % A == 0             */
     int32_t partitions_per_group; /* G: partitions per group (0 = P, one group);  */
                                /* P % G == 0; [API] 3.1 num_tokens_per_rdma_rank  */
+    int32_t partition_major;   /* 0: one receive segment per expert (expert-      */
+                               /* major order); 1: one segment per partition,     */
+                               /* the pairs of its experts in (t, k) order        */
+                               /* (partition- or rank-major receive order)        */
     int64_t max_recv_rows;     /* rows of src_of_slot the caller allocated        */
 } ep_layout_params;
+
+/* Receive segments.  The receive rows are split into S segments laid out
+ * back to back: S = E (segment e holds the pairs routed to expert e), or,
+ * with partition_major, S = P (segment q holds the pairs whose expert is in
+ * partition q, [q*E/P, (q+1)*E/P)).  Inside a segment the pairs are in
+ * ascending t*K+k order, and each segment is padded to a multiple of
+ * expert_alignment (or has C rows with a fixed capacity).  The per-segment
+ * tables (num_tokens_per_expert, expert_offset, cumulative_expert_stats)
+ * have S (S + 1) entries; their names keep the expert-major reading. */
 
 /* The layout ("handle", [API] 2.1 return values and 3.1 layout tensors):
  * caller-owned device buffers, written by ep_get_layout and read by
  * ep_dispatch / ep_combine. */
 typedef struct ep_layout {
-    int32_t *num_tokens_per_expert;     /* [E]   pairs routed to each expert          */
-    int32_t *expert_offset;             /* [E+1] first receive row of each expert;   */
-                                        /*       [E] = R, the receive rows in use     */
+    int32_t *num_tokens_per_expert;     /* [S]   pairs routed to each segment         */
+    int32_t *expert_offset;             /* [S+1] first receive row of each segment;  */
+                                        /*       [S] = R, the receive rows in use     */
     int32_t *num_tokens_per_partition;  /* [P]   tokens with >= 1 pair in partition   */
     uint8_t *is_token_in_partition;     /* [T*P] 0/1                                  */
     int32_t *dst_slot;                  /* [T*K] receive row of pair (t,k), or -1     */
@@ -118,8 +131,9 @@ typedef struct ep_layout {
  * no GPU work).  Returns 0 when the params are invalid. */
 size_t ep_get_layout_workspace_bytes(const ep_layout_params *params);
 
-/* Worst-case receive rows for these params (host call): E*C in fixed mode,
- * else T*K + min(E, T*K)*(A-1).  Buffers of this many rows never overflow. */
+/* Worst-case receive rows for these params (host call): S*C in fixed mode,
+ * else T*K + min(S, T*K)*(A-1), S the number of receive segments.  Buffers
+ * of this many rows never overflow. */
 int64_t ep_worst_case_recv_rows(const ep_layout_params *params);
 
 /* ep_get_layout - derive the receive layout from top-k routing.
@@ -131,16 +145,18 @@ int64_t ep_worst_case_recv_rows(const ep_layout_params *params);
  *   params     host; shape of the layout.
  *   layout     host struct of device buffers (all seven required, except that
  *              arrays with zero elements may be NULL).
- *   cumulative_expert_stats  device int32 [E] or NULL: += per-expert counts
+ *   cumulative_expert_stats  device int32 [S] or NULL: += per-segment counts
  *              ([API] 2.1 cumulative_local_expert_recv_stats).
  *   workspace  device, >= ep_get_layout_workspace_bytes(params) bytes, 16-byte
  *              aligned; contents need no initialisation and are scratch.
  *
- * Computes count[e] = #{(t,k): idx = e}; padded[e] = align(count[e], A);
- * expert_offset = exclusive scan of padded (compact) or e*C (fixed);
- * dst_slot[t,k] = expert_offset[e] + j where j is the rank of (t,k) among
- * the pairs of e in ascending t*K+k order (-1 for idx = -1, for an invalid
- * id, and for pairs with j >= C in fixed mode); src_of_slot[s] = t*K+k for
+ * Computes, with s(t,k) the segment of pair (t,k) (its expert, or with
+ * partition_major its partition): count[s] = #{(t,k): segment s};
+ * padded[s] = align(count[s], A); expert_offset = exclusive scan of padded
+ * (compact) or s*C (fixed); dst_slot[t,k] = expert_offset[s] + j where j is
+ * the rank of (t,k) among the pairs of segment s in ascending t*K+k order
+ * (-1 for idx = -1, for an invalid id, and for pairs with j >= C in fixed
+ * mode); src_of_slot[r] = t*K+k for
  * used slots and -1 for padding slots (slots >= max_recv_rows are not
  * written); partition membership and per-partition token counts; and, for
  * the optional pointers that are set, the partition layout (offsets,
@@ -150,9 +166,10 @@ int64_t ep_worst_case_recv_rows(const ep_layout_params *params);
  * layout->status is overwritten with EP_DEV_BAD_EXPERT / EP_DEV_CAPACITY /
  * EP_DEV_RECV_OVERFLOW (R > max_recv_rows).  T = 0 is valid.
  * Errors: EP_ERR_INVALID_ARG (null pointer, T < 0, K < 1, E < 1, A < 1,
- * P < 1, E % P != 0, partitions_per_group < 0 or not dividing P, C < 0,
- * C % A != 0, fixed mode with E*C > max_recv_rows, int32 overflow of T*K or
- * of the worst-case rows), EP_ERR_UNSUPPORTED
+ * P < 1, E % P != 0, partitions_per_group < 0 or not dividing P,
+ * partition_major not 0 or 1, C < 0, C % A != 0, fixed mode with
+ * S*C > max_recv_rows, int32 overflow of T*K or of the worst-case rows),
+ * EP_ERR_UNSUPPORTED
  * (E > EP_MAX_EXPERTS, P > EP_MAX_PARTITIONS, K > EP_MAX_TOPK),
  * EP_ERR_WORKSPACE. */
 int ep_get_layout(const int64_t *topk_idx, const ep_layout_params *params,

@@ -80,15 +80,18 @@ class Layout(dict):
 
 
 def get_layout(topk_idx, num_experts, expert_alignment=1, num_partitions=1,
-               capacity=0, rows_cap=None) -> Layout:
+               capacity=0, rows_cap=None, partition_major=False) -> Layout:
+    """oracle_get_layout: count, offset (per receive segment: expert, or
+    partition when partition_major), dst, src_of_slot, partition membership."""
     lib = _load()
     idx = _c(topk_idx, np.int64)
     T, K = idx.shape
     E, A, P, C = int(num_experts), int(expert_alignment), int(num_partitions), int(capacity)
+    S = P if partition_major else E
     if rows_cap is None:
-        rows_cap = E * C if C > 0 else T * K + min(E, T * K) * (A - 1)
-    count = np.zeros(E, np.int32)
-    offset = np.zeros(E + 1, np.int32)
+        rows_cap = S * C if C > 0 else T * K + min(S, T * K) * (A - 1)
+    count = np.zeros(S, np.int32)
+    offset = np.zeros(S + 1, np.int32)
     dst = np.zeros(T * K, np.int32)
     src = np.full(max(int(rows_cap), 1), -1, np.int32)
     in_part = np.zeros(max(T * P, 1), np.uint8)
@@ -97,7 +100,7 @@ def get_layout(topk_idx, num_experts, expert_alignment=1, num_partitions=1,
     R = ctypes.c_int64(0)
     st = ctypes.c_int32(0)
     rc = lib.oracle_get_layout(_p(idx), _i64(T), _i64(K), _i64(E), _i64(A), _i64(P), _i64(C),
-                               _p(count), _p(offset), _p(dst), _p(src), _i64(rows_cap),
+                               _i64(1 if partition_major else 0), _p(count), _p(offset), _p(dst), _p(src), _i64(rows_cap),
                                _p(in_part), _p(tpp), _p(ppp), ctypes.byref(R), ctypes.byref(st))
     if rc != 0:
         raise ValueError("oracle_get_layout: invalid arguments")

@@ -28,6 +28,9 @@
  *     order, i.e. flat index t*K + k ([RUST] scan order);
  *   - padding rows sit at the tail of each expert's segment; an expert with no
  *     pair gets align(0, A) = 0 rows;
+ *   - partition-major receive order (partitions standing for ranks): one
+ *     segment per partition holding the pairs of its experts in (t, k) order,
+ *     padded like an expert's segment;
  *   - an expert id outside [-1, E) is treated as -1 and reported with status
  *     bit 1; in fixed-capacity mode a pair whose rank j >= C is dropped
  *     (dst = -1) and reported with status bit 2;
@@ -63,14 +66,18 @@ static int64_t or_align(int64_t x, int64_t y) { return ((x + y - 1) / y) * y; }
  * (num_tokens_per_expert, is_token_in_rank, num_tokens_per_rank), sec. 3.1
  * "V2 derives the routing from topk_idx"; [RUST] partition by expert range.
  *
- * Inputs: idx int64 [T*K]; T, K, E, A, P (E % P == 0), C (0 = compact).
+ * Inputs: idx int64 [T*K]; T, K, E, A, P (E % P == 0), C (0 = compact),
+ * partition_major (0: one receive segment per expert; 1: one per partition,
+ * the rank-major receive order of partitions standing for ranks, sec. 3.1).
+ * S, the number of segments, is E or P; the segment of expert e is e, or
+ * its partition e / (E/P).
  * Outputs (all caller-allocated, host memory):
- *   count [E], offset [E+1], dst [T*K], src_of_slot [rows_cap] (written for
+ *   count [S], offset [S+1], dst [T*K], src_of_slot [rows_cap] (written for
  *   slots < rows_cap), in_part [T*P] (0/1), tok_per_part [P],
  *   pairs_per_part [P], *R_out, *status_out.
  * Returns OR_OK or OR_EINVAL for bad sizes.                                 */
 int oracle_get_layout(const int64_t *idx, int64_t T, int64_t K, int64_t E,
-                      int64_t A, int64_t P, int64_t C,
+                      int64_t A, int64_t P, int64_t C, int64_t partition_major,
                       int32_t *count, int32_t *offset, int32_t *dst,
                       int32_t *src_of_slot, int64_t rows_cap,
                       uint8_t *in_part, int32_t *tok_per_part,
@@ -80,51 +87,57 @@ int oracle_get_layout(const int64_t *idx, int64_t T, int64_t K, int64_t E,
         return OR_EINVAL;
     if (C > 0 && C % A != 0)
         return OR_EINVAL;
+    if (partition_major != 0 && partition_major != 1)
+        return OR_EINVAL;
     int32_t status = 0;
     int64_t m = E / P;
+    int64_t S = partition_major ? P : E;         /* receive segments */
+    int64_t seg_div = partition_major ? m : 1;   /* segment of expert e: e / seg_div */
 
-    /* O-1: count[e] = number of (t, k) with idx[t, k] == e. */
-    for (int64_t e = 0; e < E; ++e) count[e] = 0;
+    /* O-1: count[s] = number of (t, k) whose expert idx[t, k] lies in
+     * segment s. */
+    for (int64_t s = 0; s < S; ++s) count[s] = 0;
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t k = 0; k < K; ++k) {
             int64_t e = idx[t * K + k];
             if (e == -1) continue;
             if (e < -1 || e >= E) { status |= OR_BAD_EXPERT; continue; }
-            count[e] += 1;
+            count[e / seg_div] += 1;
         }
     }
 
-    /* O-2: padded[e] = align(count[e], A); offsets are the exclusive scan
-     * of the padded counts (compact) or e*C (fixed capacity). */
+    /* O-2: padded[s] = align(count[s], A); offsets are the exclusive scan
+     * of the padded counts (compact) or s*C (fixed capacity). */
     int64_t R;
     if (C == 0) {
         offset[0] = 0;
-        for (int64_t e = 0; e < E; ++e)
-            offset[e + 1] = (int32_t)(offset[e] + or_align(count[e], A));
-        R = offset[E];
+        for (int64_t s = 0; s < S; ++s)
+            offset[s + 1] = (int32_t)(offset[s] + or_align(count[s], A));
+        R = offset[S];
     } else {
-        for (int64_t e = 0; e <= E; ++e) offset[e] = (int32_t)(e * C);
-        R = E * C;
-        for (int64_t e = 0; e < E; ++e)
-            if (count[e] > C) status |= OR_CAPACITY;
+        for (int64_t s = 0; s <= S; ++s) offset[s] = (int32_t)(s * C);
+        R = S * C;
+        for (int64_t s = 0; s < S; ++s)
+            if (count[s] > C) status |= OR_CAPACITY;
     }
     if (R > rows_cap) status |= OR_RECV_OVERFLOW;
 
-    /* O-3: the j-th pair of expert e, in ascending (t, k) order, takes slot
-     * offset[e] + j.  Walk the pairs in that order with one cursor per
-     * expert. */
-    int32_t *cursor = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    /* O-3: the j-th pair of segment s, in ascending (t, k) order, takes slot
+     * offset[s] + j.  Walk the pairs in that order with one cursor per
+     * segment. */
+    int32_t *cursor = (int32_t *)calloc((size_t)S, sizeof(int32_t));
     if (!cursor) return OR_EINVAL;
-    for (int64_t s = 0; s < R && s < rows_cap; ++s) src_of_slot[s] = -1;
+    for (int64_t r = 0; r < R && r < rows_cap; ++r) src_of_slot[r] = -1;
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t k = 0; k < K; ++k) {
             int64_t p = t * K + k;
             int64_t e = idx[p];
             dst[p] = -1;
             if (e < 0 || e >= E) continue;
-            int64_t j = cursor[e]++;
+            int64_t s = e / seg_div;
+            int64_t j = cursor[s]++;
             if (C > 0 && j >= C) continue;       /* dropped by capacity */
-            int64_t slot = offset[e] + j;
+            int64_t slot = offset[s] + j;
             dst[p] = (int32_t)slot;
             if (slot < rows_cap) src_of_slot[slot] = (int32_t)p;
         }

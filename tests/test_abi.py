@@ -28,8 +28,8 @@ def test_library_exports_every_symbol():
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
-def _params(T=16, K=2, E=8, A=1, P=1, C=0, rows=None, G=0):
-    p = _abi.LayoutParams(T, K, E, A, P, C, G)
+def _params(T=16, K=2, E=8, A=1, P=1, C=0, rows=None, G=0, PM=0):
+    p = _abi.LayoutParams(T, K, E, A, P, C, G, PM)
     p.max_recv_rows = rows if rows is not None else _abi.load().ep_worst_case_recv_rows(ctypes.byref(p))
     return p
 
@@ -39,6 +39,11 @@ def test_worst_case_rows():
     assert lib.ep_worst_case_recv_rows(ctypes.byref(_params(4096, 8, 256, 128))) == 32768 + 256 * 127
     assert lib.ep_worst_case_recv_rows(ctypes.byref(_params(2, 2, 256, 128))) == 4 + 4 * 127
     assert lib.ep_worst_case_recv_rows(ctypes.byref(_params(128, 8, 256, 1, C=128))) == 32768
+    # partition-major: one segment per partition
+    assert lib.ep_worst_case_recv_rows(ctypes.byref(_params(4096, 8, 256, 128, P=32, PM=1))) \
+        == 32768 + 32 * 127
+    assert lib.ep_worst_case_recv_rows(ctypes.byref(_params(128, 8, 256, 1, P=8, C=128, PM=1))) \
+        == 8 * 128
 
 
 def test_workspace_bytes():
@@ -59,6 +64,8 @@ def test_workspace_bytes():
     (dict(K=300, E=512), _abi.EP_ERR_UNSUPPORTED),
     (dict(E=8, P=4, G=3), _abi.EP_ERR_INVALID_ARG),   # P % G != 0
     (dict(E=8, P=4, G=-1), _abi.EP_ERR_INVALID_ARG),
+    (dict(PM=2), _abi.EP_ERR_INVALID_ARG),            # partition_major not 0 or 1
+    (dict(E=8, P=2, C=4, rows=7, PM=1), _abi.EP_ERR_INVALID_ARG),   # P*C > max_recv_rows
 ])
 def test_get_layout_rejects_bad_params_before_launch(kw, code):
     lib = _abi.load()
