@@ -45,11 +45,14 @@ def load_library() -> ctypes.CDLL:
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
-def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+def _stream(device) -> int:
+    """The raw handle of the current stream of `device` (torch's current
+    stream, which HIP graph capture also records into)."""
+    idx = device.index if device.index is not None else torch._C._cuda_getDevice()
+    return torch._C._cuda_getCurrentRawStream(idx)
 
 
 def _launch(name: str, device, fn, *tensors_then_args):
@@ -58,7 +61,7 @@ def _launch(name: str, device, fn, *tensors_then_args):
     before the plain arguments lives on it.  Usage:
     _launch(name, dev, fn, [tensors...], arg0, arg1, ...)."""
     tensors, args = tensors_then_args[0], tensors_then_args[1:]
-    cur = torch.cuda.current_device()
+    cur = torch._C._cuda_getDevice()
     idx = cur if device.index is None else device.index
     for t in tensors:
         if t is not None and t.get_device() != idx:
@@ -149,6 +152,7 @@ class Layout:
                 self.partition_src = torch.empty(max(T * P, 1), **i32)
         nbytes = load_library().ep_get_layout_workspace_bytes(ctypes.byref(params))
         self.workspace = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        self._ptrs = None
 
     @property
     def num_tokens(self):
@@ -180,13 +184,18 @@ class Layout:
         return self.params.num_partitions
 
     def ptrs(self) -> LayoutPtrs:
-        opt = [None if t is None else t.data_ptr()
-               for t in (self.partition_offset, self.token_slot, self.num_tokens_per_group,
-                         self.partition_src)]
-        return LayoutPtrs(self.num_tokens_per_expert.data_ptr(), self.expert_offset.data_ptr(),
-                          self.num_tokens_per_partition.data_ptr(),
-                          self.is_token_in_partition.data_ptr(), self.dst_slot.data_ptr(),
-                          self.src_of_slot.data_ptr(), self.status.data_ptr(), *opt)
+        """The buffers' device pointers as the C struct (built once: the
+        buffers live as long as the layout)."""
+        if self._ptrs is None:
+            opt = [None if t is None else t.data_ptr()
+                   for t in (self.partition_offset, self.token_slot, self.num_tokens_per_group,
+                             self.partition_src)]
+            self._ptrs = LayoutPtrs(self.num_tokens_per_expert.data_ptr(),
+                                    self.expert_offset.data_ptr(),
+                                    self.num_tokens_per_partition.data_ptr(),
+                                    self.is_token_in_partition.data_ptr(), self.dst_slot.data_ptr(),
+                                    self.src_of_slot.data_ptr(), self.status.data_ptr(), *opt)
+        return self._ptrs
 
     def num_partition_rows(self) -> int:
         """Rp, rows of the non-expanded partition layout (synchronises)."""
