@@ -27,16 +27,14 @@ CFLAGS = [
 ]
 
 
-def build(out: str = LIB, defines=(), build_dir: str | None = None, verbose: bool = False) -> str:
-    """Compile every source to an object file, then link the shared library.
-    `defines` are extra -D flags (used for launch-shape sweeps)."""
+def build(out: str = LIB, build_dir: str | None = None, verbose: bool = False) -> str:
+    """Compile every source to an object file, then link the shared library."""
     build_dir = build_dir or os.path.join(HERE, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    extra = [f"-D{d}" for d in defines]
 
     def compile_one(src):
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-        cmd = [HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -270,3 +270,44 @@ def test_dispatch_empty(gpu):
                                  lay, zero_padding=True)
     torch.cuda.synchronize()
     assert lay.num_recv_rows() == 0
+
+
+def test_widest_rows(gpu):
+    """Rows of EP_MAX_HIDDEN channels (2 MiB in bf16): many waves per row in
+    every kernel.  bf16 dispatch with zero padding (two calls and one call),
+    the fused cast, the fp8 copy with its 8,192 scales per row, the
+    standalone cast and the combine, all bit-exact."""
+    from combine_ep_get_layout_amd import _abi
+    H = _abi.EP_MAX_HIDDEN
+    T, E, K, A, G = 5, 4, 2, 2, 128
+    announce("widest rows", T, H)
+    rng = ep_inputs.make_rng(77)
+    idx, wts = ep_inputs.routing_uniform(rng, T, E, K)
+    idx[1, 1] = -1
+    x = ep_inputs.bf16_normal(rng, (T, H))
+    xd = bf16_to_dev(x)
+    lay = gpu.ep_get_layout(to_dev(idx), E, A)
+    ref = oracle.get_layout(idx, E, A, rows_cap=lay.max_recv_rows)
+    recv, _, rw = gpu.ep_dispatch(xd, lay, to_dev(wts), zero_padding=True)
+    exp, _, exp_w = oracle.dispatch(x, ref, wts, zero_padding=True)
+    np.testing.assert_array_equal(bf16_bits(recv[:ref.R]), exp)
+    np.testing.assert_array_equal(rw[:ref.R].cpu().numpy(), exp_w)
+    _, recv1, _, _ = gpu.ep_dispatch_with_layout(xd, to_dev(idx), E, A, to_dev(wts),
+                                                 zero_padding=True)
+    np.testing.assert_array_equal(bf16_bits(recv1[:ref.R]), exp)
+    q_ref, s_ref = oracle.cast_fp8(x, G)
+    q, s = gpu.ep_cast_fp8(xd, G)
+    np.testing.assert_array_equal(fp8_bits(q), q_ref)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    exp8, exp_s, _ = oracle.dispatch(q_ref, ref, wts, x_scales=s_ref, zero_padding=True)
+    for fused in (True, False):
+        src = xd if fused else (fp8_to_dev(q_ref), to_dev(s_ref))
+        r8, rs, _ = gpu.ep_dispatch(src, lay, to_dev(wts), recv_fp8=fused, scale_group=G,
+                                    zero_padding=True)
+        np.testing.assert_array_equal(fp8_bits(r8[:ref.R]), exp8)
+        np.testing.assert_array_equal(rs[:ref.R].cpu().numpy().view(np.uint32),
+                                      exp_s.view(np.uint32))
+    y = ep_inputs.make_y(rng, ref.R, H)
+    out, _ = gpu.ep_combine(bf16_to_dev(y), lay, to_dev(wts))
+    np.testing.assert_array_equal(bf16_bits(out), oracle.combine_f32(y, ref.dst, wts))
+    assert lay.check() == 0
