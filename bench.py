@@ -220,6 +220,57 @@ def other_workloads(ep, torch, dev, steps, cold_iters=0):
     return out
 
 
+def row_placement(ep, torch, dev, steps, iters):
+    """The same dispatch kernel moving the same kind of bytes, with only the
+    placement of the receive rows changed: the prefill routing (top-8 of 256
+    experts: ~256 receive segments written at once), and a routing that sends
+    every token's k-th pair to expert 32k (8 segments, each written in
+    address order, one front per segment).  Also the sequential write of the
+    same receive buffer by torch's fill kernel.  Back to back and cold."""
+    import ep_inputs
+    w = ep_inputs.make_workload("prefill")
+    T, H, E, K, A = w.num_tokens, w.hidden, w.num_experts, w.num_topk, w.expert_alignment
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    wts = torch.from_numpy(w.topk_weights).to(dev)
+    fronts = np.tile(np.arange(K, dtype=np.int64) * (E // K), (T, 1))
+    out = {}
+    recv = None
+    for name, idx_np in (("prefill_routing", w.topk_idx), ("eight_fronts", fronts)):
+        idx = torch.from_numpy(idx_np).to(dev)
+        lay = ep.ep_get_layout(idx, E, A)
+        R = lay.num_recv_rows()
+        N = int((idx_np >= 0).sum())
+        if recv is None or recv.shape[0] < lay.max_recv_rows:
+            recv = torch.empty((lay.max_recv_rows, H), dtype=torch.bfloat16, device=dev)
+        rw = torch.empty(lay.max_recv_rows, dtype=torch.float32, device=dev)
+        nbytes = algorithmic_bytes(T, H, K, N, R)[1]
+        fn = lambda: ep.ep_dispatch(x, lay, wts, out=(recv, None, rw))
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        cold = cold_per_op(torch, dev, iters, {name: fn})[name]
+        out[name] = {"N": N, "R": R, "bytes": nbytes, "us": round(us, 2),
+                     "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "cold_us": cold["median_us"],
+                     "cold_GBps": round(nbytes / (cold["median_us"] * 1e-6) / 1e9, 1)}
+        assert lay.check() == 0
+        del lay, rw
+    fill = recv[:T * K]
+    cold = cold_per_op(torch, dev, iters, {"fill": lambda: fill.fill_(1.0)})["fill"]
+    nb = fill.numel() * 2
+    out["sequential_write"] = {"bytes": nb, "cold_us": cold["median_us"],
+                               "cold_GBps": round(nb / (cold["median_us"] * 1e-6) / 1e9, 1)}
+    del recv, fill, x
+    torch.cuda.empty_cache()
+    return out
+
+
 def cold_per_op(torch, dev, iters, ops):
     """Each operation timed alone, `iters` times, after a 768 MiB write that
     evicts L2 and the memory-side cache; the flush is outside the event pair.
@@ -506,6 +557,8 @@ def main():
         torch.cuda.empty_cache()
         res["other_workloads"] = other_workloads(ep, torch, dev, args.steps,
                                                  0 if args.no_cold else min(args.steps, 20))
+        if not args.no_cold:
+            res["row_placement"] = row_placement(ep, torch, dev, args.steps, min(args.steps, 20))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)
