@@ -183,9 +183,21 @@ class Layout:
     def num_partitions(self):
         return self.params.num_partitions
 
+    _BUFFERS = frozenset(("num_tokens_per_expert", "expert_offset", "num_tokens_per_partition",
+                          "is_token_in_partition", "dst_slot", "src_of_slot", "status",
+                          "partition_offset", "token_slot", "num_tokens_per_group",
+                          "partition_src"))
+
+    def __setattr__(self, name, value):
+        object.__setattr__(self, name, value)
+        if name in Layout._BUFFERS:
+            # a replaced (or dropped) buffer: the pointer struct must not keep
+            # the old address, whose memory torch may hand out again
+            object.__setattr__(self, "_ptrs", None)
+
     def ptrs(self) -> LayoutPtrs:
-        """The buffers' device pointers as the C struct (built once: the
-        buffers live as long as the layout)."""
+        """The buffers' device pointers as the C struct, built on first use
+        after any buffer attribute was (re)assigned."""
         if self._ptrs is None:
             opt = [None if t is None else t.data_ptr()
                    for t in (self.partition_offset, self.token_slot, self.num_tokens_per_group,

@@ -200,3 +200,21 @@ def test_status_strings():
     lib = _abi.load()
     for code in (0, -1, -2, -3, -4, 7):
         assert lib.ep_status_string(code)
+
+
+def test_layout_pointer_struct_follows_buffer_changes():
+    """The binding keeps each layout's pointer struct between calls; replacing
+    or dropping a buffer must rebuild it, or a call would pass the freed
+    buffer's address (whose memory torch may already have handed out)."""
+    import torch
+    import combine_ep_get_layout_amd as ep
+    p = _abi.LayoutParams(num_tokens=4, num_topk=2, num_experts=8, expert_alignment=1,
+                          num_partitions=2, max_recv_rows=8)
+    lay = ep.Layout(p, torch.device("cpu"), partition_layout=True)
+    first = lay.ptrs()
+    assert lay.ptrs() is first and first.partition_src == lay.partition_src.data_ptr()
+    lay.partition_src = None
+    second = lay.ptrs()
+    assert second is not first and not second.partition_src
+    lay.dst_slot = torch.empty((4, 2), dtype=torch.int32)
+    assert lay.ptrs().dst_slot == lay.dst_slot.data_ptr()

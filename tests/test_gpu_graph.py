@@ -147,3 +147,74 @@ def test_graph_capacity_fill_small_batch_and_fp8(gpu):
         assert torch.equal(got[4].view(torch.int16), exp[4].view(torch.int16))
         assert torch.equal(got[5].view(torch.int16), exp[5].view(torch.int16))
         assert torch.equal(got[6], le_t.dst_slot)
+
+
+@pytest.mark.parametrize("T,H", [(2000, 1024), (17000, 64)])
+def test_graph_one_call_and_noalloc_layout(gpu, T, H):
+    """ep_dispatch_with_layout + ep_combine (the benchmark's step: count kernel,
+    row kernel deriving the slots; at T >= 16,384 the token queue), and
+    ep_get_layout_noalloc + ep_dispatch, captured once and replayed with new
+    inputs; every replay equals the eager two-call path bit for bit."""
+    E, K, A = 256, 8, 128
+    dev = "cuda:0"
+    rows = gpu.worst_case_recv_rows(T, K, E, A)
+    s_idx = torch.empty((T, K), dtype=torch.int64, device=dev)
+    s_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    s_x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    s_y = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    recv = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    rw = torch.empty(rows, dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    recv2 = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    out2 = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def fill(seed):
+        w = ep_inputs.make_workload("prefill", seed=seed, T=T, H=H)
+        s_idx.copy_(to_dev(w.topk_idx))
+        s_w.copy_(to_dev(w.topk_weights))
+        s_x.copy_(bf16_to_dev(w.x))
+        s_y.copy_(bf16_to_dev(ep_inputs.make_y(w.rng, rows, H)))
+
+    fill(0)
+    lay = gpu.ep_get_layout(s_idx, E, A)
+    lay2 = gpu.ep_get_layout(s_idx, E, A)
+
+    def step():
+        gpu.ep_dispatch_with_layout(s_x, s_idx, E, A, s_w, layout=lay, out=(recv, None, rw))
+        gpu.ep_combine(s_y, lay, s_w, out=out)
+        gpu.ep_get_layout_noalloc(s_idx, lay2)
+        gpu.ep_dispatch(s_x, lay2, s_w, out=(recv2, None, None))
+        gpu.ep_combine(s_y, lay2, s_w, out=out2)
+
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step()                                  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for seed in (1, 2, 3):
+        announce("graph replay (one call, no-alloc layout)", T, H, seed)
+        fill(seed)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        lay_e = gpu.ep_get_layout(s_idx, E, A)
+        recv_e, _, rw_e = gpu.ep_dispatch(s_x, lay_e, s_w)
+        out_e, _ = gpu.ep_combine(s_y, lay_e, s_w)
+        torch.cuda.synchronize()
+        R = lay_e.num_recv_rows()
+        for l in (lay, lay2):
+            assert torch.equal(l.dst_slot, lay_e.dst_slot)
+            assert torch.equal(l.expert_offset, lay_e.expert_offset)
+            assert torch.equal(l.src_of_slot[:R], lay_e.src_of_slot[:R])
+            assert int(l.status.item()) == 0
+        used = lay_e.src_of_slot[:R] >= 0        # padding rows are left as they were
+        for r in (recv, recv2):
+            assert torch.equal(r[:R][used].view(torch.int16), recv_e[:R][used].view(torch.int16))
+        assert torch.equal(rw[:R], rw_e[:R])
+        for o in (out, out2):
+            assert torch.equal(o.view(torch.int16), out_e.view(torch.int16))
