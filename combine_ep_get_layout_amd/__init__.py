@@ -126,7 +126,9 @@ class Layout:
     dst_slot [T, K], src_of_slot [max_recv_rows], status [1]; with the
     partition layout also partition_offset [P+1], num_tokens_per_group [P/G]
     and, for P <= 64, token_slot [T, P] and partition_src [T*P] (the token of
-    each partition row) (else None)."""
+    each partition row) (else None).  A buffer may be replaced or dropped by
+    assigning the attribute; resizing one in place is not supported (the
+    calls pass each buffer's address as it was when last assigned)."""
 
     def __init__(self, params: LayoutParams, device, partition_layout: bool = False):
         T, K, P = params.num_tokens, params.num_topk, params.num_partitions
