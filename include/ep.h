@@ -22,7 +22,9 @@
  *     point to CPU memory read before the call returns.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *     enqueued on it and the call returns without synchronising.  No call
- *     allocates or frees memory, and the library keeps no state between calls.
+ *     allocates or frees memory.  Apart from the scratch array behind
+ *     ep_get_layout_noalloc and a cached compute-unit count per device, the
+ *     library keeps no state between calls.
  *   - Argument errors the host can see return a negative ep_status before
  *     anything is enqueued.  Errors only the device can see set bits in
  *     layout->status (EP_DEV_*), read by the caller after synchronising.
@@ -55,7 +57,7 @@ typedef enum {
 /* Bits OR-ed into layout->status by the device. */
 enum {
     EP_DEV_BAD_EXPERT = 1,     /* an id outside [-1, E): the pair is ignored    */
-    EP_DEV_CAPACITY = 2,       /* fixed capacity: an expert got more than C     */
+    EP_DEV_CAPACITY = 2,       /* fixed capacity: a segment got more than C     */
     EP_DEV_RECV_OVERFLOW = 4   /* a slot >= the rows the caller allocated       */
 };
 
@@ -312,8 +314,10 @@ int ep_combine_partitioned(const void *y, int32_t hidden, int64_t num_y_rows, co
  * ascending), fp32; with bf16_partials = 1 each p_q is rounded to bf16 (the
  * dtype a partial would travel in between ranks).  Level 2: acc = 0;
  * acc += bias0; acc += bias1; acc += p_q for q ascending (fp32);
- * out = bf16_rne(acc).  topk_idx is the routing (device int64 [T, K]); the
- * other arguments are as ep_combine.  EP_ERR_UNSUPPORTED when K > 64. */
+ * out = bf16_rne(acc).  topk_idx is the routing (device int64 [T, K]); a
+ * pair's partition is its expert id / (E/P), whether the layout is expert-
+ * or partition-major.  The other arguments are as ep_combine.
+ * EP_ERR_UNSUPPORTED when K > 64. */
 int ep_combine_reduced(const void *y, int32_t hidden, int64_t num_y_rows, const int64_t *topk_idx,
                        const float *topk_weights, const void *bias0, const void *bias1,
                        const ep_layout_params *params, const ep_layout *layout, void *out,
