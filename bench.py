@@ -345,7 +345,7 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, runs=3):
+def cpu_baseline(w, runs=7):
     """The oracle, as it stands, on the whole prefill batch: layout, bf16
     dispatch and ordered fp32 combine (the same step the GPU line times).
     Timed once on one thread and once with the rows and the combine split
