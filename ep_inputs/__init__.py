@@ -34,7 +34,7 @@ import numpy as np
 __all__ = [
     "Workload", "make_rng", "bf16_normal", "routing_uniform", "routing_prefill",
     "routing_zipf", "softmax_weights", "make_workload", "make_y", "WORKLOADS",
-    "worst_case_recv_rows",
+    "worst_case_recv_rows", "make_y_wide",
 ]
 
 
@@ -188,3 +188,34 @@ def make_workload(name: str, seed: int = 0, with_x: bool = True, **over) -> Work
 def make_y(rng: np.random.Generator, rows: int, hidden: int) -> np.ndarray:
     """Expert outputs for combine: bf16 N(0,1), uint16 bits [rows, hidden]."""
     return bf16_normal(rng, (rows, hidden))
+
+
+def make_y_wide(rng: np.random.Generator, rows: int, hidden: int, specials: bool = True) -> np.ndarray:
+    """Expert outputs with a wide dynamic range, for the logarithmic payload:
+    per 128-channel group a scale 2^U(-60, 60), per element a spread of
+    2^N(0, 5) and a random sign; about 3% exact zeros (both signs), 1% bf16
+    subnormals, a few magnitudes at the top of the bf16 range, and with
+    ``specials`` about 1% of groups holding an infinity or a NaN.  uint16
+    bits [rows, hidden]; hidden a multiple of 128."""
+    shape = (int(rows), int(hidden))
+    if rows == 0:
+        return np.empty(shape, np.uint16)
+    G = hidden // 128
+    scale = rng.uniform(-60.0, 60.0, (rows, G, 1))
+    spread = rng.normal(0.0, 5.0, (rows, G, 128))
+    sign = np.where(rng.random((rows, G, 128)) < 0.5, -1.0, 1.0)
+    v = (sign * np.exp2(scale + spread)).astype(np.float32).reshape(shape)
+    out = _f32_to_bf16_bits(v)
+    u = rng.random(shape)
+    out[u < 0.03] = np.where(rng.random(shape) < 0.5, 0x0000, 0x8000)[u < 0.03]
+    sub = (u >= 0.03) & (u < 0.04)
+    out[sub] = rng.integers(1, 128, shape, dtype=np.uint16)[sub] | \
+        np.where(rng.random(shape) < 0.5, 0, 0x8000).astype(np.uint16)[sub]
+    top = (u >= 0.04) & (u < 0.0405)
+    out[top] = rng.integers(0x7F70, 0x7F80, shape, dtype=np.uint16)[top]
+    if specials:
+        grp = rng.random((rows, G)) < 0.01
+        r, g = np.nonzero(grp)
+        c = g * 128 + rng.integers(0, 128, r.size)
+        out[r, c] = rng.choice(np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC1], np.uint16), r.size)
+    return out

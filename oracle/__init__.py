@@ -382,3 +382,81 @@ def combine_reduced_f32(y, topk_idx, dst, num_experts, num_partitions, topk_weig
                                    ctypes.c_int(1 if bf16_partials else 0), _p(tk), _i64(n),
                                    _p(out))
     return out
+
+
+# --- 10-bit logarithmic combine payload ([API] sec. 3.4, use_logfmt) -------
+LOGFMT_GROUP = 128
+LOGFMT_POISON = 0xFFFF
+
+
+def logfmt_encode(x_bits):
+    """bf16 rows [rows, H] -> (codes uint16 [rows, H] holding 10-bit codes,
+    refs uint16 [rows, H/128]); see the reading in ep_oracle.c."""
+    x = _c(x_bits, np.uint16)
+    rows, H = x.shape
+    codes = np.zeros((rows, H), np.uint16)
+    refs = np.zeros((rows, H // LOGFMT_GROUP), np.uint16)
+    rc = _load().oracle_logfmt_encode(_p(x), _i64(rows), _i64(H), _p(codes), _p(refs))
+    if rc != 0:
+        raise ValueError("logfmt_encode: hidden must be a positive multiple of 128")
+    return codes, refs
+
+
+def logfmt_decode(codes, refs):
+    """(codes, refs) -> bf16 bit patterns [rows, H] (exact); raises on a code
+    or reference the encoder never writes."""
+    codes = _c(codes, np.uint16)
+    refs = _c(refs, np.uint16)
+    rows, H = codes.shape
+    out = np.zeros((rows, H), np.uint16)
+    rc = _load().oracle_logfmt_decode(_p(codes), _p(refs), _i64(rows), _i64(H), _p(out))
+    if rc != 0:
+        raise ValueError("logfmt_decode: invalid code or reference")
+    return out
+
+
+def logfmt_row_bytes(hidden):
+    """Bytes of one packed payload row: H code bytes, H/4 bytes of high-bit
+    words, H/128 references of two bytes, padded to 16."""
+    used = hidden + hidden // 4 + 2 * (hidden // LOGFMT_GROUP)
+    return (used + 15) // 16 * 16
+
+
+def logfmt_pack(codes, refs):
+    """Packed payload rows (uint8 [rows, logfmt_row_bytes(H)]): bytes [0, H)
+    hold each code's low eight bits; then one little-endian 32-bit word per 16
+    channels whose bit j is bit 8 of channel 16v+j's code and bit 16+j its
+    sign bit; then the references as little-endian uint16; zero padding."""
+    codes = np.asarray(codes, np.uint32)
+    refs = np.asarray(refs, np.uint16)
+    rows, H = codes.shape
+    out = np.zeros((rows, logfmt_row_bytes(H)), np.uint8)
+    out[:, :H] = (codes & 0xFF).astype(np.uint8)
+    blocks = codes.reshape(rows, H // 16, 16)
+    j = np.arange(16, dtype=np.uint32)
+    words = (((blocks >> 8) & 1) << j).sum(axis=2, dtype=np.uint32) \
+        | (((blocks >> 9) & 1) << (j + 16)).sum(axis=2, dtype=np.uint32)
+    out[:, H:H + H // 4] = words.astype("<u4").view(np.uint8).reshape(rows, H // 4)
+    G = H // LOGFMT_GROUP
+    out[:, H + H // 4:H + H // 4 + 2 * G] = refs.astype("<u2").view(np.uint8).reshape(rows, 2 * G)
+    return out
+
+
+def logfmt_unpack(payload, hidden):
+    """Inverse of logfmt_pack: (codes, refs)."""
+    payload = np.asarray(payload, np.uint8)
+    rows, H = payload.shape[0], hidden
+    lo = payload[:, :H].astype(np.uint16)
+    words = np.ascontiguousarray(payload[:, H:H + H // 4]).view("<u4").reshape(rows, H // 16, 1)
+    j = np.arange(16, dtype=np.uint32)
+    b8 = ((words >> j) & 1).reshape(rows, H).astype(np.uint16)
+    sg = ((words >> (j + 16)) & 1).reshape(rows, H).astype(np.uint16)
+    G = H // LOGFMT_GROUP
+    refs = np.ascontiguousarray(payload[:, H + H // 4:H + H // 4 + 2 * G]).view("<u2").reshape(rows, G)
+    return lo | (b8 << 8) | (sg << 9), refs.astype(np.uint16)
+
+
+def combine_logfmt_f32(codes, refs, dst, topk_weights=None, bias0=None, bias1=None, tokens=None):
+    """The combine over a logfmt payload: the rows decoded (exactly, to bf16),
+    then the ordered fp32 combine of combine_f32."""
+    return combine_f32(logfmt_decode(codes, refs), dst, topk_weights, bias0, bias1, tokens)

@@ -626,3 +626,101 @@ void oracle_combine_reduced_f32(const uint16_t *y, int64_t H, const int64_t *idx
         }
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* 10-bit logarithmic combine payload ([API] sec. 3.4: low_latency_combine's
+ * use_logfmt option, a "10-bit log format" for the expert outputs sent back
+ * to their tokens; the page fixes only the width).  Reading:
+ *   - values travel in groups of 128 channels of one row (the grouping of the
+ *     same API's fp8 payload, sec. 4.2), with one 16-bit reference per group;
+ *   - the log of a bf16 magnitude is its 15 magnitude bits read as a
+ *     fixed-point base-2 logarithm (exponent field, then the stored mantissa
+ *     as the fraction: Mitchell's piecewise-linear log2, exact at powers of
+ *     two), rounded to five fractional bits, nearest, ties to even, and held
+ *     at the largest finite value 0x1FDF (bf16 0x7F7C);
+ *   - the reference is the group's largest log; a value's code is one sign
+ *     bit over a 9-bit index = log - reference + 511, so the largest
+ *     magnitude maps to 511; index 0 is zero, for zeros, for logs of 0 and for
+ *     values more than 510/32 log units below the reference (flushed);
+ *   - a group holding an infinity or NaN has the reference 0xFFFF and all
+ *     codes 0; it decodes to NaN in all 128 channels;
+ *   - decoding is exact: sign, then magnitude bits (reference - 511 + index)
+ *     shifted left by two, a bf16 number with five fraction bits. */
+#define OR_LOGFMT_GROUP 128
+#define OR_LOGFMT_MAXLOG 0x1FDF
+#define OR_LOGFMT_POISON 0xFFFF
+
+/* Log code of a bf16 pattern, -1 for an infinity or NaN. */
+int32_t oracle_logfmt_log(uint16_t b)
+{
+    uint32_t u = b & 0x7FFFu;
+    if (u >= 0x7F80u) return -1;
+    uint32_t q = u / 4, r = u % 4;
+    if (r > 2 || (r == 2 && q % 2 == 1)) q += 1;
+    if (q > OR_LOGFMT_MAXLOG) q = OR_LOGFMT_MAXLOG;
+    return (int32_t)q;
+}
+
+/* codes [rows, H] (10-bit values in uint16), refs [rows, H/128]. */
+int oracle_logfmt_encode(const uint16_t *x, int64_t rows, int64_t H, uint16_t *codes,
+                         uint16_t *refs)
+{
+    if (H <= 0 || H % OR_LOGFMT_GROUP != 0 || rows < 0) return OR_EINVAL;
+    int64_t G = H / OR_LOGFMT_GROUP;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t g = 0; g < G; ++g) {
+            const uint16_t *xs = x + r * H + g * OR_LOGFMT_GROUP;
+            uint16_t *cs = codes + r * H + g * OR_LOGFMT_GROUP;
+            int poison = 0;
+            int32_t top = 0;
+            for (int c = 0; c < OR_LOGFMT_GROUP; ++c) {
+                int32_t l = oracle_logfmt_log(xs[c]);
+                if (l < 0) poison = 1;
+                else if (l > top) top = l;
+            }
+            refs[r * G + g] = (uint16_t)(poison ? OR_LOGFMT_POISON : top);
+            for (int c = 0; c < OR_LOGFMT_GROUP; ++c) {
+                uint16_t code = 0;
+                if (!poison) {
+                    int32_t l = oracle_logfmt_log(xs[c]);
+                    int32_t idx = l - top + 511;
+                    if (l >= 1 && idx >= 1) code = (uint16_t)(idx | ((xs[c] & 0x8000u) ? 512 : 0));
+                }
+                cs[c] = code;
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* bf16 patterns [rows, H] from codes and refs; OR_EINVAL for a code or
+ * reference the encoder never writes. */
+int oracle_logfmt_decode(const uint16_t *codes, const uint16_t *refs, int64_t rows, int64_t H,
+                         uint16_t *out)
+{
+    if (H <= 0 || H % OR_LOGFMT_GROUP != 0 || rows < 0) return OR_EINVAL;
+    int64_t G = H / OR_LOGFMT_GROUP;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < H; ++c) {
+            uint16_t ref = refs[r * G + c / OR_LOGFMT_GROUP];
+            uint16_t code = codes[r * H + c];
+            if (code > 1023) return OR_EINVAL;
+            if (ref == OR_LOGFMT_POISON) {
+                if (code != 0) return OR_EINVAL;
+                out[r * H + c] = 0x7FC0u;
+                continue;
+            }
+            if (ref > OR_LOGFMT_MAXLOG) return OR_EINVAL;
+            int32_t idx = code & 511, sign = code >> 9;
+            if (idx == 0) {
+                if (sign) return OR_EINVAL;
+                out[r * H + c] = 0;
+                continue;
+            }
+            int32_t n = (int32_t)ref - 511 + idx;
+            if (n < 1 || n > OR_LOGFMT_MAXLOG) return OR_EINVAL;
+            out[r * H + c] = (uint16_t)((sign ? 0x8000u : 0u) | ((uint32_t)n << 2));
+        }
+    }
+    return OR_OK;
+}
