@@ -495,6 +495,12 @@ def main():
     fus_ms = per_op(fused_dispatch)
     dis_ms = per_op(lambda: ep.ep_dispatch(x, lay, wts, out=(recv, None, recv_w)))
     com_ms = per_op(lambda: ep.ep_combine(y, lay, wts, out=out))
+    # the low-latency combine's 10-bit logarithmic payload: encode the R
+    # receive rows, then the combine that reads the payload
+    y_used = y[:R]
+    pay = ep.ep_logfmt_encode(y_used)
+    enc_ms = per_op(lambda: ep.ep_logfmt_encode(y_used, out=pay))
+    lcm_ms = per_op(lambda: ep.ep_combine_logfmt(pay, H, lay, wts, out=out))
     assert lay.check() == 0
     cold = None
     if not args.no_cold:
@@ -506,6 +512,8 @@ def main():
                 ep.ep_get_layout(idx, E, A, w.num_partitions, w.capacity, layout=lay),
                 ep.ep_dispatch(x, lay, wts, out=(recv, None, recv_w))),
             "combine": lambda: ep.ep_combine(y, lay, wts, out=out),
+            "logfmt_encode": lambda: ep.ep_logfmt_encode(y_used, out=pay),
+            "combine_logfmt": lambda: ep.ep_combine_logfmt(pay, H, lay, wts, out=out),
         })
     reference = None if args.no_cold else torch_reference(torch, dev, args.steps, lay, x, K, N)
 
@@ -519,6 +527,11 @@ def main():
         "dispatch_rows": {"ms": dis_ms, "bytes": rb, "GBps": rb / (dis_ms * 1e-3) / 1e9},
         "combine": {"ms": com_ms, "bytes": cb, "GBps": cb / (com_ms * 1e-3) / 1e9},
     }
+    pay_row = H + H // 4 + 2 * (H // 128)      # payload bytes per row, tail excluded
+    enc_b = R * H * 2 + R * pay_row
+    lcm_b = N * pay_row + T * K * 8 + T * H * 2
+    kern["logfmt_encode"] = {"ms": enc_ms, "bytes": enc_b, "GBps": enc_b / (enc_ms * 1e-3) / 1e9}
+    kern["combine_logfmt"] = {"ms": lcm_ms, "bytes": lcm_b, "GBps": lcm_b / (lcm_ms * 1e-3) / 1e9}
     for v in kern.values():   # each operation as a fraction of the HBM roofline, and tokens/s
         v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
         v["tokens_per_s"] = T / (v["ms"] * 1e-3)
@@ -545,7 +558,8 @@ def main():
     if cold is not None:
         lb_, rb_, cb_ = algorithmic_bytes(T, H, K, N, R)
         nbytes = {"layout": lb_, "dispatch_reused_layout": rb_, "dispatch_fresh_layout": lb_ + rb_,
-                  "dispatch_fresh_layout_two_calls": lb_ + rb_, "combine": cb_}
+                  "dispatch_fresh_layout_two_calls": lb_ + rb_, "combine": cb_,
+                  "logfmt_encode": enc_b, "combine_logfmt": lcm_b}
         for k, v in cold.items():
             v["GBps_median"] = round(nbytes[k] / (v["median_us"] * 1e-6) / 1e9, 1)
             v["hbm_frac_median"] = round(v["GBps_median"] / HBM_PEAK_GBS, 4)
@@ -553,7 +567,7 @@ def main():
     if reference is not None:
         res["torch_reference"] = reference
     if not args.no_other_workloads:
-        del recv, y
+        del recv, y, y_used, pay
         torch.cuda.empty_cache()
         res["other_workloads"] = other_workloads(ep, torch, dev, args.steps,
                                                  0 if args.no_cold else min(args.steps, 20))

@@ -34,7 +34,8 @@ from ._abi import (EP_DEV_BAD_EXPERT, EP_DEV_CAPACITY, EP_DEV_RECV_OVERFLOW, EpE
 
 __all__ = ["load_library", "Layout", "ep_get_layout", "ep_get_layout_noalloc", "ep_dispatch",
            "ep_dispatch_with_layout",
-           "ep_combine", "ep_cast_fp8",
+           "ep_combine", "ep_cast_fp8", "logfmt_row_bytes", "ep_logfmt_encode",
+           "ep_logfmt_decode", "ep_combine_logfmt",
            "ep_dispatch_partitioned", "ep_combine_partitioned", "ep_combine_reduced",
            "worst_case_recv_rows", "EpError", "EP_DEV_BAD_EXPERT", "EP_DEV_CAPACITY",
            "EP_DEV_RECV_OVERFLOW"]
@@ -469,6 +470,92 @@ def ep_combine(y: torch.Tensor, layout: Layout, topk_weights: Optional[torch.Ten
             _ptr(y), H, rows, _ptr(topk_weights), _ptr(b0), _ptr(b1),
             ctypes.byref(params), ctypes.byref(ptrs), _ptr(recv_topk_weights),
             _ptr(cw), _ptr(out), _stream(y.device))
+    return out, cw
+
+
+def logfmt_row_bytes(hidden: int) -> int:
+    """Bytes of one row of the 10-bit logarithmic payload (hidden a positive
+    multiple of 128)."""
+    n = int(load_library().ep_logfmt_row_bytes(int(hidden)))
+    if n < 0:
+        raise ValueError("hidden must be a positive multiple of 128")
+    return n
+
+
+_U8 = (torch.uint8,)
+
+
+def ep_logfmt_encode(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16 rows [rows, H] -> 10-bit logarithmic payload, uint8
+    [rows, logfmt_row_bytes(H)] (the use_logfmt format of the low-latency
+    combine; layout and rounding in include/ep.h)."""
+    lib = load_library()
+    _need_cuda(y, "y")
+    if y.dtype != torch.bfloat16 or y.dim() != 2:
+        raise ValueError("y must be bf16 [rows, H]")
+    rows, H = y.shape
+    rb = logfmt_row_bytes(H)
+    if out is None:
+        out = torch.empty((rows, rb), dtype=torch.uint8, device=y.device)
+    _check(out, "out", _U8, rb, rows=rows)
+    _launch("ep_logfmt_encode", y.device, lib.ep_logfmt_encode, [out],
+            _ptr(y), rows, H, _ptr(out), _stream(y.device))
+    return out
+
+
+def ep_logfmt_decode(payload: torch.Tensor, hidden: int,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """10-bit logarithmic payload -> bf16 rows [rows, hidden] (exact)."""
+    lib = load_library()
+    rb = logfmt_row_bytes(hidden)
+    _check(payload, "payload", _U8, rb)
+    rows = payload.shape[0]
+    if out is None:
+        out = torch.empty((rows, hidden), dtype=torch.bfloat16, device=payload.device)
+    _check(out, "out", _BF16, hidden, rows=rows)
+    _launch("ep_logfmt_decode", payload.device, lib.ep_logfmt_decode, [out],
+            _ptr(payload), rows, hidden, _ptr(out), _stream(payload.device))
+    return out
+
+
+def ep_combine_logfmt(payload: torch.Tensor, hidden: int, layout: Layout,
+                      topk_weights: Optional[torch.Tensor] = None,
+                      bias: Union[None, torch.Tensor, Tuple[torch.Tensor, torch.Tensor]] = None,
+                      recv_topk_weights: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None):
+    """ep_combine over payload rows from ep_logfmt_encode (uint8
+    [rows, logfmt_row_bytes(hidden)]): bit for bit the combine of the decoded
+    rows.  Returns (combined_x, combined_topk_weights or None)."""
+    lib = load_library()
+    rb = logfmt_row_bytes(hidden)
+    _check(payload, "payload", _U8, rb)
+    rows, H = payload.shape[0], hidden
+    T, K = layout.num_tokens, layout.num_topk
+    b0 = b1 = None
+    if isinstance(bias, (tuple, list)):
+        b0, b1 = (list(bias) + [None, None])[:2]
+    elif bias is not None:
+        b0 = bias
+    for name, b in (("bias0", b0), ("bias1", b1)):
+        if b is not None:
+            _need_cuda(b, name)
+            if b.dtype != torch.bfloat16 or tuple(b.shape) != (T, H):
+                raise ValueError(f"{name} must be bf16 [T, H]")
+    _check(topk_weights, "topk_weights", _F32, K, rows=T)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=payload.device)
+    _check(out, "out", _BF16, H, rows=T)
+    cw = None
+    if recv_topk_weights is not None:
+        _check(recv_topk_weights, "recv_topk_weights", _F32, min_rows=rows)
+        cw = torch.empty((T, K), dtype=torch.float32, device=payload.device)
+    params = layout.params
+    ptrs = layout.ptrs()
+    _launch("ep_combine_logfmt", payload.device, lib.ep_combine_logfmt,
+            [topk_weights, b0, b1, recv_topk_weights, out, layout.status],
+            _ptr(payload), H, rows, _ptr(topk_weights), _ptr(b0), _ptr(b1),
+            ctypes.byref(params), ctypes.byref(ptrs), _ptr(recv_topk_weights),
+            _ptr(cw), _ptr(out), _stream(payload.device))
     return out, cw
 
 

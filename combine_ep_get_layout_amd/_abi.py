@@ -32,7 +32,8 @@ EP_MAX_HIDDEN = 1 << 20
 EXPORTS = ("ep_get_layout_workspace_bytes", "ep_worst_case_recv_rows", "ep_get_layout",
            "ep_get_layout_noalloc",
            "ep_dispatch", "ep_dispatch_with_layout", "ep_combine", "ep_dispatch_partitioned", "ep_combine_partitioned",
-           "ep_combine_reduced", "ep_cast_fp8", "ep_status_string")
+           "ep_combine_reduced", "ep_cast_fp8", "ep_logfmt_row_bytes", "ep_logfmt_encode",
+           "ep_logfmt_decode", "ep_combine_logfmt", "ep_status_string")
 
 
 class LayoutParams(ctypes.Structure):
@@ -103,6 +104,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ep_combine_reduced.restype = ctypes.c_int
     lib.ep_cast_fp8.argtypes = [vp, i32, i32, i32, ctypes.c_int, vp, vp, vp]
     lib.ep_cast_fp8.restype = ctypes.c_int
+    lib.ep_logfmt_row_bytes.argtypes = [i32]
+    lib.ep_logfmt_row_bytes.restype = i64
+    lib.ep_logfmt_encode.argtypes = [vp, i64, i32, vp, vp]
+    lib.ep_logfmt_encode.restype = ctypes.c_int
+    lib.ep_logfmt_decode.argtypes = [vp, i64, i32, vp, vp]
+    lib.ep_logfmt_decode.restype = ctypes.c_int
+    lib.ep_combine_logfmt.argtypes = [vp, i32, i64, vp, vp, vp, P(LayoutParams), P(LayoutPtrs),
+                                      vp, vp, vp, vp]
+    lib.ep_combine_logfmt.restype = ctypes.c_int
     lib.ep_status_string.argtypes = [ctypes.c_int]
     lib.ep_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -419,6 +419,65 @@ int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group
                                          x_fp8, scales, (hipStream_t)stream));
 }
 
+static bool logfmt_hidden_ok(int32_t hidden) {
+    return hidden >= 128 && hidden % 128 == 0;
+}
+
+int64_t ep_logfmt_row_bytes(int32_t hidden) {
+    if (!logfmt_hidden_ok(hidden)) return EP_ERR_INVALID_ARG;
+    return ep::logfmt_row_bytes(hidden);
+}
+
+int ep_logfmt_encode(const void *x, int64_t num_rows, int32_t hidden, void *payload,
+                     void *stream) {
+    if (!logfmt_hidden_ok(hidden) || num_rows < 0) return EP_ERR_INVALID_ARG;
+    if (num_rows == 0) return EP_OK;
+    if (!x || !payload || !aligned16(x) || !aligned16(payload)) return EP_ERR_INVALID_ARG;
+    return to_status(ep::launch_logfmt(x, payload, num_rows, hidden, true, (hipStream_t)stream));
+}
+
+int ep_logfmt_decode(const void *payload, int64_t num_rows, int32_t hidden, void *out,
+                     void *stream) {
+    if (!logfmt_hidden_ok(hidden) || num_rows < 0) return EP_ERR_INVALID_ARG;
+    if (num_rows == 0) return EP_OK;
+    if (!payload || !out || !aligned16(payload) || !aligned16(out)) return EP_ERR_INVALID_ARG;
+    return to_status(ep::launch_logfmt(payload, out, num_rows, hidden, false,
+                                       (hipStream_t)stream));
+}
+
+int ep_combine_logfmt(const void *payload, int32_t hidden, int64_t num_y_rows,
+                      const float *topk_weights, const void *bias0, const void *bias1,
+                      const ep_layout_params *p, const ep_layout *layout,
+                      const float *recv_topk_weights, float *combined_topk_weights, void *out,
+                      void *stream) {
+    int rc = check_params(p);
+    if (rc != EP_OK) return rc;
+    if (!layout || !layout->status || (p->num_tokens > 0 && !layout->dst_slot))
+        return EP_ERR_INVALID_ARG;
+    if (!logfmt_hidden_ok(hidden) || num_y_rows < 0) return EP_ERR_INVALID_ARG;
+    if (combined_topk_weights && !recv_topk_weights) return EP_ERR_INVALID_ARG;
+    if (p->num_tokens > 0) {
+        if (!out || !aligned16(out)) return EP_ERR_INVALID_ARG;
+        if (num_y_rows > 0 && (!payload || !aligned16(payload))) return EP_ERR_INVALID_ARG;
+        if ((bias0 && !aligned16(bias0)) || (bias1 && !aligned16(bias1))) return EP_ERR_INVALID_ARG;
+    }
+    ep::CombineArgs c = {};
+    c.y = payload;
+    c.y_rows = num_y_rows;
+    c.w = topk_weights;
+    c.bias0 = bias0;
+    c.bias1 = bias1;
+    c.dst = layout->dst_slot;
+    c.status = layout->status;
+    c.recv_w = recv_topk_weights;
+    c.combined_w = combined_topk_weights;
+    c.out = out;
+    c.T = p->num_tokens;
+    c.K = p->num_topk;
+    c.hidden = hidden;
+    return to_status(ep::launch_combine_logfmt(c, (hipStream_t)stream));
+}
+
 const char *ep_status_string(int code) {
     switch (code) {
         case EP_OK: return "ok";

@@ -341,6 +341,65 @@ int ep_combine_reduced(const void *y, int32_t hidden, int64_t num_y_rows, const 
 int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group,
                 int out_dtype, uint8_t *x_fp8, void *scales, void *stream);
 
+/* 10-bit logarithmic combine payload ([API] 3.4: low_latency_combine's
+ * use_logfmt, a "10-bit log format" for the expert outputs on their way back;
+ * the page fixes only the width, so the format below is this library's
+ * reading of it).
+ *
+ * Values travel in groups of 128 channels of one row.  The log of a bf16
+ * magnitude is its 15 magnitude bits read as a fixed-point base-2 logarithm
+ * (exponent field, then the stored mantissa as the fraction), rounded half to
+ * even to five fraction bits and held at 0x1FDF (bf16 0x7F7C, the largest
+ * value kept).  Each group stores its largest log as the reference; a value's
+ * 10-bit code is its sign (bit 9) over the index log - reference + 511
+ * (bits 0..8): the largest magnitude has index 511; index 0 is zero, used for
+ * zeros and for values 511 or more log units (about 16 octaves) under the
+ * reference.  A group that holds an infinity or NaN has the reference 0xFFFF
+ * and all codes 0, and decodes to NaN in its 128 channels.  Decoding is exact:
+ * the value is the bf16 number with magnitude bits (reference - 511 + index)
+ * << 2, i.e. x rounded to five fraction bits (relative error <= 2^-6 for
+ * normal values).
+ *
+ * Packed row, ep_logfmt_row_bytes(hidden) bytes (a multiple of 16): bytes
+ * [0, H) hold code bits 0..7 of each channel; then H/16 little-endian uint32
+ * words, word v carrying the high bits of channels 16v..16v+15: channel
+ * 16v+2p+e (p = 0..7, e = 0 or 1) has its code's bit 8 in bit 7-p+16e and its
+ * sign in bit 15-p+16e; then H/128 little-endian uint16 references; the tail up to
+ * the row size is neither written nor read.  The encoder writes only valid
+ * codes; a payload written by anything else decodes to unspecified values
+ * (never a memory fault).  hidden must be a positive multiple of 128. */
+
+/* Bytes of one packed payload row, or EP_ERR_INVALID_ARG for a bad hidden. */
+int64_t ep_logfmt_row_bytes(int32_t hidden);
+
+/* ep_logfmt_encode - bf16 rows to payload rows.
+ *   x        device bf16 [num_rows, hidden], 16-byte aligned.
+ *   payload  device uint8 [num_rows, ep_logfmt_row_bytes(hidden)], 16-byte
+ *            aligned (caller-owned; may be reused across calls).
+ * EP_ERR_INVALID_ARG for a bad hidden, negative num_rows or a NULL or
+ * misaligned pointer (with num_rows > 0). */
+int ep_logfmt_encode(const void *x, int64_t num_rows, int32_t hidden, void *payload,
+                     void *stream);
+
+/* ep_logfmt_decode - payload rows to bf16 rows (exact; NaN = 0x7FC0 for a
+ * marked group).  out: device bf16 [num_rows, hidden], 16-byte aligned.
+ * Errors as ep_logfmt_encode. */
+int ep_logfmt_decode(const void *payload, int64_t num_rows, int32_t hidden, void *out,
+                     void *stream);
+
+/* ep_combine_logfmt - ep_combine over payload rows ([API] 3.4: the weighted
+ * low-latency combine with use_logfmt): payload is device uint8 [num_y_rows,
+ * ep_logfmt_row_bytes(hidden)], 16-byte aligned, from ep_logfmt_encode of the
+ * receive rows.  The result is bit for bit ep_combine over the decoded rows
+ * (same fp32 order: biases, then fmaf over kept pairs in ascending k); every
+ * other argument, the status bits and the errors are as ep_combine, except
+ * that hidden must be a positive multiple of 128. */
+int ep_combine_logfmt(const void *payload, int32_t hidden, int64_t num_y_rows,
+                      const float *topk_weights, const void *bias0, const void *bias1,
+                      const ep_layout_params *params, const ep_layout *layout,
+                      const float *recv_topk_weights, float *combined_topk_weights, void *out,
+                      void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *ep_status_string(int code);
 

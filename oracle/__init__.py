@@ -425,21 +425,30 @@ def logfmt_row_bytes(hidden):
 def logfmt_pack(codes, refs):
     """Packed payload rows (uint8 [rows, logfmt_row_bytes(H)]): bytes [0, H)
     hold each code's low eight bits; then one little-endian 32-bit word per 16
-    channels whose bit j is bit 8 of channel 16v+j's code and bit 16+j its
-    sign bit; then the references as little-endian uint16; zero padding."""
+    channels: channel 16v + 2p + e (p = 0..7, e = 0 or 1) puts its code's
+    bit 8 at bit 7 - p + 16e and its sign bit at bit 15 - p + 16e; then the
+    references as little-endian uint16; zero padding."""
     codes = np.asarray(codes, np.uint32)
     refs = np.asarray(refs, np.uint16)
     rows, H = codes.shape
     out = np.zeros((rows, logfmt_row_bytes(H)), np.uint8)
     out[:, :H] = (codes & 0xFF).astype(np.uint8)
     blocks = codes.reshape(rows, H // 16, 16)
-    j = np.arange(16, dtype=np.uint32)
-    words = (((blocks >> 8) & 1) << j).sum(axis=2, dtype=np.uint32) \
-        | (((blocks >> 9) & 1) << (j + 16)).sum(axis=2, dtype=np.uint32)
+    pos8, pos9 = _logfmt_high_bit_positions()
+    words = (((blocks >> 8) & 1) << pos8).sum(axis=2, dtype=np.uint32) \
+        | (((blocks >> 9) & 1) << pos9).sum(axis=2, dtype=np.uint32)
     out[:, H:H + H // 4] = words.astype("<u4").view(np.uint8).reshape(rows, H // 4)
     G = H // LOGFMT_GROUP
     out[:, H + H // 4:H + H // 4 + 2 * G] = refs.astype("<u2").view(np.uint8).reshape(rows, 2 * G)
     return out
+
+
+def _logfmt_high_bit_positions():
+    """Bit positions, within a channel block's word, of bit 8 and of the sign
+    of the block's 16 codes (channel 2p + e: 7 - p + 16e and 15 - p + 16e)."""
+    j = np.arange(16, dtype=np.uint32)
+    p, e = j // 2, j % 2
+    return 7 - p + 16 * e, 15 - p + 16 * e
 
 
 def logfmt_unpack(payload, hidden):
@@ -448,9 +457,9 @@ def logfmt_unpack(payload, hidden):
     rows, H = payload.shape[0], hidden
     lo = payload[:, :H].astype(np.uint16)
     words = np.ascontiguousarray(payload[:, H:H + H // 4]).view("<u4").reshape(rows, H // 16, 1)
-    j = np.arange(16, dtype=np.uint32)
-    b8 = ((words >> j) & 1).reshape(rows, H).astype(np.uint16)
-    sg = ((words >> (j + 16)) & 1).reshape(rows, H).astype(np.uint16)
+    pos8, pos9 = _logfmt_high_bit_positions()
+    b8 = ((words >> pos8) & 1).reshape(rows, H).astype(np.uint16)
+    sg = ((words >> pos9) & 1).reshape(rows, H).astype(np.uint16)
     G = H // LOGFMT_GROUP
     refs = np.ascontiguousarray(payload[:, H + H // 4:H + H // 4 + 2 * G]).view("<u2").reshape(rows, G)
     return lo | (b8 << 8) | (sg << 9), refs.astype(np.uint16)

@@ -156,6 +156,31 @@ def test_combine_and_cast_reject_bad_arguments():
                            ctypes.c_void_p(18), None) == _abi.EP_ERR_INVALID_ARG   # float scales
 
 
+def test_logfmt_calls_reject_bad_arguments():
+    lib = _abi.load()
+    assert lib.ep_logfmt_row_bytes(7168) == 9072 and lib.ep_logfmt_row_bytes(128) == 176
+    for h in (0, -128, 64, 200, 1000):
+        assert lib.ep_logfmt_row_bytes(h) == _abi.EP_ERR_INVALID_ARG
+    v16, v8 = ctypes.c_void_p(16), ctypes.c_void_p(8)
+    for fn in (lib.ep_logfmt_encode, lib.ep_logfmt_decode):
+        assert fn(v16, 4, 192, v16, None) == _abi.EP_ERR_INVALID_ARG      # hidden % 128
+        assert fn(v16, -1, 128, v16, None) == _abi.EP_ERR_INVALID_ARG
+        assert fn(v8, 4, 128, v16, None) == _abi.EP_ERR_INVALID_ARG       # misaligned
+        assert fn(v16, 4, 128, None, None) == _abi.EP_ERR_INVALID_ARG
+        assert fn(None, 0, 128, None, None) == _abi.EP_OK                 # nothing to do
+    p = _params(T=4, K=2, E=8)
+    lay = _abi.LayoutPtrs(*([16] * 7))
+    assert lib.ep_combine_logfmt(v16, 64, 8, None, None, None, ctypes.byref(p), ctypes.byref(lay),
+                                 None, None, v16, None) == _abi.EP_ERR_INVALID_ARG
+    assert lib.ep_combine_logfmt(v16, 128, 8, None, v8, None, ctypes.byref(p), ctypes.byref(lay),
+                                 None, None, v16, None) == _abi.EP_ERR_INVALID_ARG
+    assert lib.ep_combine_logfmt(v16, 128, 8, None, None, None, ctypes.byref(p),
+                                 ctypes.byref(lay), None, v16, v16,
+                                 None) == _abi.EP_ERR_INVALID_ARG
+    assert lib.ep_combine_logfmt(v8, 128, 8, None, None, None, ctypes.byref(p), ctypes.byref(lay),
+                                 None, None, v16, None) == _abi.EP_ERR_INVALID_ARG
+
+
 def test_partition_layout_limits():
     lib = _abi.load()
     p = _params(T=4, K=2, E=128, P=128)

@@ -180,9 +180,11 @@ def test_packed_byte_layout():
     H = 256
     assert oracle.logfmt_row_bytes(H) == 336 and p.shape == (1, 336)
     assert p[0, 0] == 0x55 and p[0, 17] == 0xFF and p[0, 255] == 0xAA
-    assert p[0, H:H + 4].tolist() == [0x01, 0x00, 0x00, 0x00]          # channels 0..15
-    assert p[0, H + 4:H + 8].tolist() == [0x02, 0x00, 0x02, 0x00]      # channel 17
-    assert p[0, H + 60:H + 64].tolist() == [0x00, 0x00, 0x00, 0x80]    # channel 255
+    # channel 16v + 2p + e: bit 8 of the code at bit 7 - p + 16e of word v,
+    # the sign at bit 15 - p + 16e
+    assert p[0, H:H + 4].tolist() == [0x80, 0x00, 0x00, 0x00]          # channel 0: bit 7
+    assert p[0, H + 4:H + 8].tolist() == [0x00, 0x00, 0x80, 0x80]      # channel 17: 23, 31
+    assert p[0, H + 60:H + 64].tolist() == [0x00, 0x00, 0x00, 0x01]    # channel 255: 24
     assert p[0, H + 64:H + 68].tolist() == [0xBC, 0x0A, 0x34, 0x12]
     assert not p[0, H + 68:].any()
     assert np.count_nonzero(p[0, :H]) == 3
@@ -234,15 +236,19 @@ def test_combine_error_within_the_codec_bound():
     codes, refs = oracle.logfmt_encode(y)
     got = _val(oracle.combine_logfmt_f32(codes, refs, lay.dst, w.topk_weights))
     exact = oracle.combine_f64(y, lay.dst, w.topk_weights)
-    # |sum w y - sum w dec(y)| <= 2^-6 sum |w| |y| (all values normal, none
-    # flushed at N(0,1) scale), then one bf16 rounding of the result
+    # |sum w y - sum w dec(y)| <= sum |w| (2^-6 |y| for a kept value, or
+    # 2^-15 of its group's maximum for a flushed one), then one bf16
+    # rounding of the result
     absw = np.abs(w.topk_weights.astype(np.float64))
     mag = np.zeros_like(exact)
+    top = np.zeros_like(exact)
     yv = np.abs(_val(y))
+    gm = np.repeat(yv.reshape(lay.R, 2, 128).max(axis=2), 128, axis=1)
     for k in range(w.num_topk):
         d = lay.dst[:, k]
         ok = d >= 0
         mag[ok] += absw[ok, k, None] * yv[d[ok]]
-    bound = 2.0 ** -6 * mag + 2.0 ** -8 * np.abs(exact) + 1e-30
+        top[ok] += absw[ok, k, None] * gm[d[ok]]
+    bound = 2.0 ** -6 * mag + 2.0 ** -15 * top + 2.0 ** -8 * np.abs(exact)
     assert np.all(np.abs(got - exact) <= bound * 1.0001)
     assert np.any(got != _val(oracle.combine_f32(y, lay.dst, w.topk_weights)))
