@@ -12,7 +12,7 @@
 //   - reference = the group's largest log; code = sign bit (bit 9) over the
 //     index log - reference + 511 (bits 0..8): the largest magnitude is 511,
 //     index 0 is zero (zeros, logs of 0, and values 511 or more log units
-//     under the reference);
+//     under the reference), signed as the input;
 //   - a group holding an infinity or NaN gets the reference 0xFFFF and all
 //     codes 0, and decodes to NaN;
 //   - decoding is exact: the bf16 magnitude bits are (reference - 511 +
@@ -75,6 +75,22 @@ __device__ __forceinline__ uint32_t pk_mul_lo_u16(uint32_t a, uint32_t b) {
     asm("v_pk_mul_lo_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
     return d;
 }
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    uint32_t d;
+    asm("v_pk_max_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+// a - b per half, held at 0 (unsigned saturation).
+__device__ __forceinline__ uint32_t pk_sub_sat_u16(uint32_t a, uint32_t b) {
+    uint32_t d;
+    asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ uint32_t pk_lshr_u16(uint32_t a, uint32_t n2) {
+    uint32_t d;
+    asm("v_pk_lshrrev_b16 %0, %1, %2" : "=v"(d) : "v"(n2), "v"(a));
+    return d;
+}
 
 // max over aligned groups of 8 lanes, by DPP moves (all lanes active).
 __device__ __forceinline__ uint32_t group8_max(uint32_t v) {
@@ -84,18 +100,13 @@ __device__ __forceinline__ uint32_t group8_max(uint32_t v) {
     return v;
 }
 
-// Log of a bf16 pattern's magnitude, or kPoison for Inf / NaN.
-__device__ __forceinline__ uint32_t log_key(uint32_t b) {
-    const uint32_t u = b & 0x7FFFu;
-    const uint32_t l = min((u + 1u + ((u >> 2) & 1u)) >> 2, kMaxLog);
-    return u >= 0x7F80u ? kPoison : l;
-}
-
-__device__ __forceinline__ uint32_t half_of(const ep_u32x4 *v, int j) {
-    const uint32_t w = v[j >> 3][(j >> 1) & 3];
-    return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
+// Encoding works on the same channel pairs: the magnitude bits u of a pair
+// are one register (u = x & 0x7FFF7FFF); the group's reference comes from
+// the largest u (the log is monotone in u, and u >= 0x7F80 is an infinity
+// or NaN); per pair, l = min((u + 1 + bit 2 of u) >> 2, 0x1FDF) is the
+// rounded log of both halves (no carry crosses a half: u <= 0x7F7F there),
+// l + 511 where l >= 1, then a saturating subtract of the reference gives
+// both indices, 0 where flushed or zero.
 __global__ void __launch_bounds__(kBlock) logfmt_encode_kernel(LogfmtK a) {
     const int lane = __lane_id();
     const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
@@ -110,25 +121,35 @@ __global__ void __launch_bounds__(kBlock) logfmt_encode_kernel(LogfmtK a) {
         x[0] = load_nt(s);
         x[1] = load_nt(s + 1);
     }
-    uint32_t top = 0;
+    uint32_t w[8], u[8];
+    uint32_t umax2 = 0;
 #pragma unroll
-    for (int j = 0; j < kChanPerLane; ++j) top = max(top, log_key(half_of(x, j)));
-    top = group8_max(top);                        // groups never straddle a wave
+    for (int p = 0; p < 8; ++p) {                 // pair p: channels 2p, 2p+1
+        w[p] = x[p >> 2][p & 3];
+        u[p] = w[p] & 0x7FFF7FFFu;
+        umax2 = pk_max_u16(umax2, u[p]);
+    }
+    uint32_t umax = max(umax2 & 0xFFFFu, umax2 >> 16);
+    umax = group8_max(umax);                      // groups never straddle a wave
     if (!live) return;
+    const uint32_t top =
+        umax >= 0x7F80u ? kPoison : min((umax + 1u + ((umax >> 2) & 1u)) >> 2, kMaxLog);
     uint32_t lo[4] = {0u, 0u, 0u, 0u};
     uint32_t hi = 0;
     if (top != kPoison) {
+        const uint32_t top2 = top | (top << 16);
+        uint32_t idx[8];
 #pragma unroll
-        for (int j = 0; j < kChanPerLane; ++j) {
-            const uint32_t b = half_of(x, j);
-            const uint32_t l = log_key(b);
-            const int idx = (int)l - (int)top + 511;
-            if (l >= 1 && idx >= 1) {
-                const int sh = 16 * (j & 1) - (j >> 1);
-                lo[j >> 2] |= ((uint32_t)idx & 0xFFu) << (8 * (j & 3));
-                hi |= (((uint32_t)idx >> 8) << (7 + sh)) | ((b >> 15) << (15 + sh));
-            }
+        for (int p = 0; p < 8; ++p) {
+            const uint32_t s = u[p] + 0x00010001u + ((u[p] >> 2) & 0x00010001u);
+            const uint32_t l = pk_min_u16(pk_lshr_u16(s, 0x00020002u), 0x1FDF1FDFu);
+            const uint32_t t = pk_mad_u16(pk_min_u16(l, 0x00010001u), 0x01FF01FFu, l);
+            idx[p] = pk_sub_sat_u16(t, top2);
+            hi |= ((idx[p] >> (p + 1)) & (0x01000100u >> (p + 1))) |
+                  ((w[p] >> p) & (0x80008000u >> p));
         }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) lo[d] = __builtin_amdgcn_perm(idx[2 * d + 1], idx[2 * d], 0x06040200u);
     }
     uint8_t *row = a.dst + r * (int64_t)a.stride;
     ((ep_u32x4 *)row)[v] = ep_u32x4{lo[0], lo[1], lo[2], lo[3]};

@@ -354,7 +354,8 @@ int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group
  * 10-bit code is its sign (bit 9) over the index log - reference + 511
  * (bits 0..8): the largest magnitude has index 511; index 0 is zero, used for
  * zeros and for values 511 or more log units (about 16 octaves) under the
- * reference.  A group that holds an infinity or NaN has the reference 0xFFFF
+ * reference, and keeps the input's sign (-0 and flushed negative values
+ * decode to -0).  A group that holds an infinity or NaN has the reference 0xFFFF
  * and all codes 0, and decodes to NaN in its 128 channels.  Decoding is exact:
  * the value is the bf16 number with magnitude bits (reference - 511 + index)
  * << 2, i.e. x rounded to five fraction bits (relative error <= 2^-6 for

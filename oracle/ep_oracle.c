@@ -638,14 +638,17 @@ void oracle_combine_reduced_f32(const uint16_t *y, int64_t H, const int64_t *idx
  *     as the fraction: Mitchell's piecewise-linear log2, exact at powers of
  *     two), rounded to five fractional bits, nearest, ties to even, and held
  *     at the largest finite value 0x1FDF (bf16 0x7F7C);
- *   - the reference is the group's largest log; a value's code is one sign
+ *   - the reference is the group's largest log; a value's code is its sign
  *     bit over a 9-bit index = log - reference + 511, so the largest
  *     magnitude maps to 511; index 0 is zero, for zeros, for logs of 0 and for
- *     values more than 510/32 log units below the reference (flushed);
+ *     values more than 510/32 log units below the reference (flushed); a zero
+ *     keeps the sign of its input, so -0 and flushed negative values come
+ *     back as -0 (as e4m3 keeps the sign on underflow in the fp8 cast);
  *   - a group holding an infinity or NaN has the reference 0xFFFF and all
  *     codes 0; it decodes to NaN in all 128 channels;
  *   - decoding is exact: sign, then magnitude bits (reference - 511 + index)
- *     shifted left by two, a bf16 number with five fraction bits. */
+ *     shifted left by two (0 for index 0), a bf16 number with five fraction
+ *     bits. */
 #define OR_LOGFMT_GROUP 128
 #define OR_LOGFMT_MAXLOG 0x1FDF
 #define OR_LOGFMT_POISON 0xFFFF
@@ -684,7 +687,8 @@ int oracle_logfmt_encode(const uint16_t *x, int64_t rows, int64_t H, uint16_t *c
                 if (!poison) {
                     int32_t l = oracle_logfmt_log(xs[c]);
                     int32_t idx = l - top + 511;
-                    if (l >= 1 && idx >= 1) code = (uint16_t)(idx | ((xs[c] & 0x8000u) ? 512 : 0));
+                    if (l < 1 || idx < 1) idx = 0;
+                    code = (uint16_t)(idx | ((xs[c] & 0x8000u) ? 512 : 0));
                 }
                 cs[c] = code;
             }
@@ -713,8 +717,7 @@ int oracle_logfmt_decode(const uint16_t *codes, const uint16_t *refs, int64_t ro
             if (ref > OR_LOGFMT_MAXLOG) return OR_EINVAL;
             int32_t idx = code & 511, sign = code >> 9;
             if (idx == 0) {
-                if (sign) return OR_EINVAL;
-                out[r * H + c] = 0;
+                out[r * H + c] = (uint16_t)(sign ? 0x8000u : 0u);
                 continue;
             }
             int32_t n = (int32_t)ref - 511 + idx;

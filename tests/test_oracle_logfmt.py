@@ -6,8 +6,8 @@ The reading under test: groups of 128 channels; a magnitude's log is its bf16
 magnitude bits read as a fixed-point base-2 logarithm (exponent field, then
 the mantissa as fraction), rounded half to even to five fractional bits and
 held at the largest finite value; one sign bit over a 9-bit index measured
-down from the group's largest log (largest magnitude = 511, 0 = zero); groups
-with an infinity or NaN decode to NaN.
+down from the group's largest log (largest magnitude = 511, 0 = zero, which
+keeps the input's sign); groups with an infinity or NaN decode to NaN.
 
 Every pin below states the expected result in the value domain (frexp,
 ldexp, rint in float64) or by hand, not with the oracle's integer steps:
@@ -37,13 +37,19 @@ def _val(bits):
 def _round6(v):
     """|v| rounded half to even to 1 + 5 significant bits with the quantum of
     its binade (at least that of 2^-126), saturated at (2 - 2^-5) * 2^127;
-    sign kept, zero for zero."""
+    sign kept, also on a zero result."""
     a = np.abs(v)
     _, e = np.frexp(a)                       # a = f * 2^e, f in [0.5, 1)
     qe = np.maximum(e - 1, -126) - 5
     q = np.ldexp(np.rint(np.ldexp(a, -qe)), qe)
     q = np.minimum(q, (2.0 - 2.0 ** -5) * 2.0 ** 127)
-    return np.where(a == 0, 0.0, np.copysign(q, v))
+    return np.copysign(np.where(a == 0, 0.0, q), v)
+
+
+def _same(got, want):
+    """Equal values with equal signs (so -0 differs from +0)."""
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(want))
 
 
 def _groups_with(first, xs):
@@ -70,11 +76,11 @@ def test_round_trip_of_every_pattern_alone_in_its_group():
     # group's largest, index 511 (unless it rounds to zero)
     got = _val(dec[fin, 0])
     want = _round6(_val(ALL[fin]))
-    np.testing.assert_array_equal(got, want)
+    _same(got, want)
     nz = want != 0
     assert np.all(codes[fin, 0][nz] & 511 == 511)
-    assert np.all((codes[fin, 0][nz] >> 9) == (ALL[fin][nz] >> 15))
-    assert np.all(codes[fin, 0][~nz] == 0)
+    assert np.all((codes[fin, 0] >> 9) == (ALL[fin] >> 15))
+    assert np.all(codes[fin, 0][~nz] & 511 == 0)
     assert np.all(dec[fin, 1:] == 0)
 
 
@@ -89,8 +95,8 @@ def test_window_below_a_power_of_two_maximum(k):
     # 32 (111 + k) + 2 units: the pattern of 2^(k-16) * (1 + 2/32)
     smallest = 1.0625 * 2.0 ** (k - 16)
     q = _round6(_val(xs))
-    want = np.where(np.abs(q) >= smallest, q, 0.0)
-    np.testing.assert_array_equal(dec, want)
+    want = np.where(np.abs(q) >= smallest, q, np.copysign(0.0, q))
+    _same(dec, want)
     assert np.all(codes[:, 0] == 511)
 
 
@@ -100,8 +106,7 @@ def test_nothing_is_flushed_below_a_small_maximum():
     top_bits = np.uint16(0x0008)
     xs = FINITE[(FINITE & 0x7FFF) <= 0x0008]
     codes, refs = oracle.logfmt_encode(_groups_with(top_bits, xs))
-    np.testing.assert_array_equal(_val(oracle.logfmt_decode(codes, refs)[:, 1]),
-                                  _round6(_val(xs)))
+    _same(_val(oracle.logfmt_decode(codes, refs)[:, 1]), _round6(_val(xs)))
     assert np.all(refs[:, 0] == 2)
 
 
@@ -144,19 +149,21 @@ def test_hand_worked_group():
     #   to 0xFAB*4 = 0x3EAC (0.3359375)
     # 2^-16 = 0x3780: log 0xDE0 = 0xFE0 - 512: index -1, flushed
     # 1.0625 * 2^-16 = 0x3788: log 0xDE2: index 1
+    # +0 and -0: index 0, the sign kept: 0x000 and 0x200
+    # -2^-16 = 0xB780: flushed like 2^-16, the sign kept: 0x200, decodes to -0
     # 0x3F83 (1.0234375): 0x3F83/4 = 0xFE0.C -> 0xFE1 becomes the reference:
     #   every other index above drops by one
     row = np.zeros((1, 128), np.uint16)
-    row[0, :8] = [0x3F80, 0xBF00, 0x3F40, 0x3EAB, 0x3780, 0x3788, 0x0000, 0x8000]
+    row[0, :9] = [0x3F80, 0xBF00, 0x3F40, 0x3EAB, 0x3780, 0x3788, 0x0000, 0x8000, 0xB780]
     codes, refs = oracle.logfmt_encode(row)
     assert refs.tolist() == [[0x0FE0]]
-    assert codes[0, :8].tolist() == [0x1FF, 0x3DF, 0x1EF, 0x1CA, 0, 0x001, 0, 0]
+    assert codes[0, :9].tolist() == [0x1FF, 0x3DF, 0x1EF, 0x1CA, 0, 0x001, 0, 0x200, 0x200]
     dec = oracle.logfmt_decode(codes, refs)
-    assert dec[0, :8].tolist() == [0x3F80, 0xBF00, 0x3F40, 0x3EAC, 0, 0x3788, 0, 0]
+    assert dec[0, :9].tolist() == [0x3F80, 0xBF00, 0x3F40, 0x3EAC, 0, 0x3788, 0, 0x8000, 0x8000]
     row[0, 100] = 0x3F83
     codes, refs = oracle.logfmt_encode(row)
     assert refs.tolist() == [[0x0FE1]]
-    assert codes[0, :8].tolist() == [0x1FE, 0x3DE, 0x1EE, 0x1C9, 0, 0, 0, 0]
+    assert codes[0, :9].tolist() == [0x1FE, 0x3DE, 0x1EE, 0x1C9, 0, 0, 0, 0x200, 0x200]
     assert codes[0, 100] == 0x1FF
     # ties to even: 0x3F82 / 4 = 0xFE0.8 -> 0xFE0; 0x3F86 / 4 = 0xFE1.8 -> 0xFE2
     row2 = np.zeros((2, 128), np.uint16)
@@ -203,8 +210,13 @@ def test_codes_are_ten_bits_and_decode_rejects_others():
     assert codes.max() < 1024
     assert np.any(refs == oracle.LOGFMT_POISON)
     with pytest.raises(ValueError):
+        bad = refs.copy()
+        bad[0, 0] = 0x2000             # no finite log is that large
+        oracle.logfmt_decode(codes, bad)
+    with pytest.raises(ValueError):
+        r, g = np.argwhere(refs == oracle.LOGFMT_POISON)[0]
         bad = codes.copy()
-        bad[0, 0] = 0x200              # negative zero is never written
+        bad[r, g * 128] = 0x001        # a marked group holds only zero codes
         oracle.logfmt_decode(bad, refs)
     with pytest.raises(ValueError):
         oracle.logfmt_encode(np.zeros((2, 100), np.uint16))
