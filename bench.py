@@ -18,10 +18,14 @@ stream around K back-to-back launches of each operation (an event record
 between launches would leave a few microseconds of idle GPU time);
 `roofline` reports the longer of the two row kernels (the dispatch rows are
 timed on a reused layout, where the call is that one kernel) against
-MI355X's 8 TB/s HBM peak.  `cold_cache` times each operation after a 768 MiB
-flush, `torch_reference` PyTorch's own index_copy_ / index_select over the
-same routed slots, and `cpu_baseline` the CPU oracle on the same whole batch,
-on one thread and on the host's threads.
+MI355X's 8 TB/s HBM peak.  `kernels` also times the low-latency combine's
+10-bit logarithmic payload (use_logfmt): `logfmt_encode` over the R receive
+rows and `combine_logfmt`, the combine that reads that payload (N payload
+rows of H + H/4 + H/64 bytes instead of 2H).  `cold_cache` times each
+operation after a 768 MiB flush, `torch_reference` PyTorch's own
+index_copy_ / index_select over the same routed slots, and `cpu_baseline`
+the CPU oracle on the same whole batch, on one thread and on the host's
+threads.
 """
 from __future__ import annotations
 
@@ -532,9 +536,10 @@ def main():
     lcm_b = N * pay_row + T * K * 8 + T * H * 2
     kern["logfmt_encode"] = {"ms": enc_ms, "bytes": enc_b, "GBps": enc_b / (enc_ms * 1e-3) / 1e9}
     kern["combine_logfmt"] = {"ms": lcm_ms, "bytes": lcm_b, "GBps": lcm_b / (lcm_ms * 1e-3) / 1e9}
-    for v in kern.values():   # each operation as a fraction of the HBM roofline, and tokens/s
+    for k, v in kern.items():   # each operation as a fraction of the HBM roofline, and tokens/s
         v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
         v["tokens_per_s"] = T / (v["ms"] * 1e-3)
+        v["traffic"] = load_traffic(k)   # HBM bytes per launch from the PMC runs, or None
     dom = "dispatch_rows" if dis_ms >= com_ms else "combine"
     ach = kern[dom]["GBps"]
     tr = load_traffic(dom)

@@ -19,7 +19,8 @@
 //     index) << 2, so every decoded value is a bf16 number and the combine
 //     over the payload is the bf16 combine of the decoded rows.
 //
-// Packed row (stride ep_logfmt_row_bytes(H), 16-byte aligned): H bytes of
+// Packed row (stride ep_logfmt_row_bytes(H), a multiple of 128 bytes so
+// that every row starts on a cache line): H bytes of
 // code bits 0..7 in channel order; H/16 little-endian words, word v holding
 // the high bits of channels 16v..16v+15: channel 16v+2p+e (p = 0..7, e = 0,1)
 // has its code's bit 8 in bit 7-p+16e and its sign in bit 15-p+16e; H/128
@@ -313,7 +314,7 @@ int64_t grid_of(int64_t rows, int wpr) {
 
 int64_t logfmt_row_bytes(int hidden) {
     const int64_t used = (int64_t)hidden + hidden / 4 + 2 * (hidden / 128);
-    return (used + 15) / 16 * 16;
+    return (used + 127) / 128 * 128;
 }
 
 hipError_t launch_logfmt(const void *src, void *dst, int64_t rows, int hidden, bool encode,

@@ -361,7 +361,8 @@ int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group
  * << 2, i.e. x rounded to five fraction bits (relative error <= 2^-6 for
  * normal values).
  *
- * Packed row, ep_logfmt_row_bytes(hidden) bytes (a multiple of 16): bytes
+ * Packed row, ep_logfmt_row_bytes(hidden) bytes (a multiple of 128, so rows
+ * start on cache lines): bytes
  * [0, H) hold code bits 0..7 of each channel; then H/16 little-endian uint32
  * words, word v carrying the high bits of channels 16v..16v+15: channel
  * 16v+2p+e (p = 0..7, e = 0 or 1) has its code's bit 8 in bit 7-p+16e and its

@@ -417,9 +417,9 @@ def logfmt_decode(codes, refs):
 
 def logfmt_row_bytes(hidden):
     """Bytes of one packed payload row: H code bytes, H/4 bytes of high-bit
-    words, H/128 references of two bytes, padded to 16."""
+    words, H/128 references of two bytes, padded to a multiple of 128."""
     used = hidden + hidden // 4 + 2 * (hidden // LOGFMT_GROUP)
-    return (used + 15) // 16 * 16
+    return (used + 127) // 128 * 128
 
 
 def logfmt_pack(codes, refs):

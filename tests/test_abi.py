@@ -158,7 +158,7 @@ def test_combine_and_cast_reject_bad_arguments():
 
 def test_logfmt_calls_reject_bad_arguments():
     lib = _abi.load()
-    assert lib.ep_logfmt_row_bytes(7168) == 9072 and lib.ep_logfmt_row_bytes(128) == 176
+    assert lib.ep_logfmt_row_bytes(7168) == 9088 and lib.ep_logfmt_row_bytes(128) == 256
     for h in (0, -128, 64, 200, 1000):
         assert lib.ep_logfmt_row_bytes(h) == _abi.EP_ERR_INVALID_ARG
     v16, v8 = ctypes.c_void_p(16), ctypes.c_void_p(8)

@@ -66,7 +66,7 @@ def test_every_pattern_alone_and_under_maxima(gpu):
 
 def test_empty_rows(gpu):
     pay = gpu.ep_logfmt_encode(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda:0"))
-    assert pay.shape == (0, 336)
+    assert pay.shape == (0, 384)
     assert gpu.ep_logfmt_decode(pay, 256).shape == (0, 256)
 
 

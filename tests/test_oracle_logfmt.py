@@ -185,7 +185,7 @@ def test_packed_byte_layout():
     refs = np.array([[0x0ABC, 0x1234]], np.uint16)
     p = oracle.logfmt_pack(codes, refs)
     H = 256
-    assert oracle.logfmt_row_bytes(H) == 336 and p.shape == (1, 336)
+    assert oracle.logfmt_row_bytes(H) == 384 and p.shape == (1, 384)
     assert p[0, 0] == 0x55 and p[0, 17] == 0xFF and p[0, 255] == 0xAA
     # channel 16v + 2p + e: bit 8 of the code at bit 7 - p + 16e of word v,
     # the sign at bit 15 - p + 16e
@@ -195,7 +195,7 @@ def test_packed_byte_layout():
     assert p[0, H + 64:H + 68].tolist() == [0xBC, 0x0A, 0x34, 0x12]
     assert not p[0, H + 68:].any()
     assert np.count_nonzero(p[0, :H]) == 3
-    assert oracle.logfmt_row_bytes(7168) == 9072 and oracle.logfmt_row_bytes(128) == 176
+    assert oracle.logfmt_row_bytes(7168) == 9088 and oracle.logfmt_row_bytes(128) == 256
     rng = ep_inputs.make_rng(5)
     c, r = oracle.logfmt_encode(ep_inputs.make_y_wide(rng, 50, 384))
     c2, r2 = oracle.logfmt_unpack(oracle.logfmt_pack(c, r), 384)
