@@ -1,4 +1,5 @@
-"""CPU oracle for MoE expert-parallel layout / dispatch / combine / fp8 cast.
+"""CPU oracle for MoE expert-parallel layout / dispatch / combine / fp8 cast / the
+10-bit logarithmic combine payload.
 
 TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
 baseline leg are the only callers.  The GPU library never imports, links or

@@ -42,7 +42,11 @@
  *   - combine: acc = 0; acc += bias0; acc += bias1; then for k ascending over
  *     valid pairs acc = fmaf(w, y, acc); out = bf16 round-to-nearest-even;
  *     NULL weights mean w = 1 (the V1 unweighted sum).  A float64 version
- *     gives the tolerance reference.
+ *     gives the tolerance reference;
+ *   - the 10-bit log format of the low-latency combine ([API] sec. 3.4): a
+ *     sign bit over a 9-bit log index under a per-128-channel reference, the
+ *     log being the bf16 magnitude bits rounded to five fraction bits (the
+ *     full statement is at the logfmt functions below).
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared -o liboracle.so ep_oracle.c -lm
  */
