@@ -19,9 +19,10 @@ between launches would leave a few microseconds of idle GPU time);
 `roofline` reports the longer of the two row kernels (the dispatch rows are
 timed on a reused layout, where the call is that one kernel) against
 MI355X's 8 TB/s HBM peak.  `kernels` also times the low-latency combine's
-10-bit logarithmic payload (use_logfmt): `logfmt_encode` over the R receive
-rows and `combine_logfmt`, the combine that reads that payload (N payload
-rows of H + H/4 + H/64 bytes instead of 2H).  `cold_cache` times each
+10-bit logarithmic payload (use_logfmt): `logfmt_encode` of the N receive
+rows that hold a pair (padding rows skipped) and `combine_logfmt`, the
+combine that reads that payload (N payload rows of H + H/4 + H/64 bytes
+instead of 2H); the decode workload of `other_workloads` times both too.  `cold_cache` times each
 operation after a 768 MiB flush, `torch_reference` PyTorch's own
 index_copy_ / index_select over the same routed slots, and `cpu_baseline`
 the CPU oracle on the same whole batch, on one thread and on the host's
@@ -215,6 +216,17 @@ def other_workloads(ep, torch, dev, steps, cold_iters=0):
                 res["dispatch"]["valid_row_GBps"] = round(rb / (res["dispatch"]["us"] * 1e-6) / 1e9, 1)
             del recv
         res["combine"] = per_op(lambda: ep.ep_combine(y, lay, wts, out=out_c), cb, T)
+        if name == "decode":
+            # the low-latency combine's 10-bit payload: only the N rows of the
+            # capacity region that hold a pair are encoded
+            prow = H + H // 4 + 2 * (H // 128)
+            y_r = y[:R]
+            pay = ep.ep_logfmt_encode(y_r, layout=lay)
+            res["logfmt_encode"] = per_op(lambda: ep.ep_logfmt_encode(y_r, out=pay, layout=lay),
+                                          N * (H * 2 + prow), T)
+            res["combine_logfmt"] = per_op(lambda: ep.ep_combine_logfmt(pay, H, lay, wts, out=out_c),
+                                           N * prow + T * K * 8 + T * H * 2, T)
+            del pay, y_r
         assert lay.check() == 0
         if w.num_partitions > 1:
             res.update(partitioned_legs(ep, torch, dev, w, idx, wts, x, y, lay, out_c, per_op))
@@ -499,11 +511,12 @@ def main():
     fus_ms = per_op(fused_dispatch)
     dis_ms = per_op(lambda: ep.ep_dispatch(x, lay, wts, out=(recv, None, recv_w)))
     com_ms = per_op(lambda: ep.ep_combine(y, lay, wts, out=out))
-    # the low-latency combine's 10-bit logarithmic payload: encode the R
-    # receive rows, then the combine that reads the payload
+    # the low-latency combine's 10-bit logarithmic payload: encode the N
+    # receive rows that hold a pair (padding rows skipped by the layout's
+    # src_of_slot), then the combine that reads the payload
     y_used = y[:R]
-    pay = ep.ep_logfmt_encode(y_used)
-    enc_ms = per_op(lambda: ep.ep_logfmt_encode(y_used, out=pay))
+    pay = ep.ep_logfmt_encode(y_used, layout=lay)
+    enc_ms = per_op(lambda: ep.ep_logfmt_encode(y_used, out=pay, layout=lay))
     lcm_ms = per_op(lambda: ep.ep_combine_logfmt(pay, H, lay, wts, out=out))
     assert lay.check() == 0
     cold = None
@@ -516,7 +529,7 @@ def main():
                 ep.ep_get_layout(idx, E, A, w.num_partitions, w.capacity, layout=lay),
                 ep.ep_dispatch(x, lay, wts, out=(recv, None, recv_w))),
             "combine": lambda: ep.ep_combine(y, lay, wts, out=out),
-            "logfmt_encode": lambda: ep.ep_logfmt_encode(y_used, out=pay),
+            "logfmt_encode": lambda: ep.ep_logfmt_encode(y_used, out=pay, layout=lay),
             "combine_logfmt": lambda: ep.ep_combine_logfmt(pay, H, lay, wts, out=out),
         })
     reference = None if args.no_cold else torch_reference(torch, dev, args.steps, lay, x, K, N)
@@ -532,7 +545,7 @@ def main():
         "combine": {"ms": com_ms, "bytes": cb, "GBps": cb / (com_ms * 1e-3) / 1e9},
     }
     pay_row = H + H // 4 + 2 * (H // 128)      # payload bytes per row, tail excluded
-    enc_b = R * H * 2 + R * pay_row
+    enc_b = N * H * 2 + N * pay_row
     lcm_b = N * pay_row + T * K * 8 + T * H * 2
     kern["logfmt_encode"] = {"ms": enc_ms, "bytes": enc_b, "GBps": enc_b / (enc_ms * 1e-3) / 1e9}
     kern["combine_logfmt"] = {"ms": lcm_ms, "bytes": lcm_b, "GBps": lcm_b / (lcm_ms * 1e-3) / 1e9}

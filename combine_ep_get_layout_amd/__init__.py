@@ -485,10 +485,13 @@ def logfmt_row_bytes(hidden: int) -> int:
 _U8 = (torch.uint8,)
 
 
-def ep_logfmt_encode(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+def ep_logfmt_encode(y: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     layout: Optional[Layout] = None) -> torch.Tensor:
     """bf16 rows [rows, H] -> 10-bit logarithmic payload, uint8
     [rows, logfmt_row_bytes(H)] (the use_logfmt format of the low-latency
-    combine; layout and rounding in include/ep.h)."""
+    combine; layout and rounding in include/ep.h).  With `layout` (the
+    receive layout the rows belong to) only rows that hold a pair are
+    encoded; the others are left as they are (a combine never reads them)."""
     lib = load_library()
     _need_cuda(y, "y")
     if y.dtype != torch.bfloat16 or y.dim() != 2:
@@ -498,8 +501,17 @@ def ep_logfmt_encode(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> tor
     if out is None:
         out = torch.empty((rows, rb), dtype=torch.uint8, device=y.device)
     _check(out, "out", _U8, rb, rows=rows)
-    _launch("ep_logfmt_encode", y.device, lib.ep_logfmt_encode, [out],
-            _ptr(y), rows, H, _ptr(out), _stream(y.device))
+    if layout is None:
+        _launch("ep_logfmt_encode", y.device, lib.ep_logfmt_encode, [out],
+                _ptr(y), rows, H, None, None, _ptr(out), _stream(y.device))
+        return out
+    if rows > layout.max_recv_rows:
+        raise ValueError("y has more rows than the layout's max_recv_rows")
+    params = layout.params
+    ptrs = layout.ptrs()
+    _launch("ep_logfmt_encode", y.device, lib.ep_logfmt_encode, [out, layout.src_of_slot],
+            _ptr(y), rows, H, ctypes.byref(params), ctypes.byref(ptrs), _ptr(out),
+            _stream(y.device))
     return out
 
 

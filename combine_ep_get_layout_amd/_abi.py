@@ -106,7 +106,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ep_cast_fp8.restype = ctypes.c_int
     lib.ep_logfmt_row_bytes.argtypes = [i32]
     lib.ep_logfmt_row_bytes.restype = i64
-    lib.ep_logfmt_encode.argtypes = [vp, i64, i32, vp, vp]
+    lib.ep_logfmt_encode.argtypes = [vp, i64, i32, P(LayoutParams), P(LayoutPtrs), vp, vp]
     lib.ep_logfmt_encode.restype = ctypes.c_int
     lib.ep_logfmt_decode.argtypes = [vp, i64, i32, vp, vp]
     lib.ep_logfmt_decode.restype = ctypes.c_int

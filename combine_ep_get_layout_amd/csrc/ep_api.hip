@@ -428,12 +428,24 @@ int64_t ep_logfmt_row_bytes(int32_t hidden) {
     return ep::logfmt_row_bytes(hidden);
 }
 
-int ep_logfmt_encode(const void *x, int64_t num_rows, int32_t hidden, void *payload,
+int ep_logfmt_encode(const void *x, int64_t num_rows, int32_t hidden,
+                     const ep_layout_params *p, const ep_layout *layout, void *payload,
                      void *stream) {
     if (!logfmt_hidden_ok(hidden) || num_rows < 0) return EP_ERR_INVALID_ARG;
+    if ((p == nullptr) != (layout == nullptr)) return EP_ERR_INVALID_ARG;
+    const int32_t *row_src = nullptr;
+    int64_t pairs = 0;
+    if (p) {
+        int rc = check_params(p);
+        if (rc != EP_OK) return rc;
+        if (!layout->src_of_slot || num_rows > p->max_recv_rows) return EP_ERR_INVALID_ARG;
+        row_src = layout->src_of_slot;
+        pairs = (int64_t)p->num_tokens * p->num_topk;
+    }
     if (num_rows == 0) return EP_OK;
     if (!x || !payload || !aligned16(x) || !aligned16(payload)) return EP_ERR_INVALID_ARG;
-    return to_status(ep::launch_logfmt(x, payload, num_rows, hidden, true, (hipStream_t)stream));
+    return to_status(ep::launch_logfmt(x, payload, num_rows, hidden, true, row_src, pairs,
+                                       (hipStream_t)stream));
 }
 
 int ep_logfmt_decode(const void *payload, int64_t num_rows, int32_t hidden, void *out,
@@ -441,7 +453,7 @@ int ep_logfmt_decode(const void *payload, int64_t num_rows, int32_t hidden, void
     if (!logfmt_hidden_ok(hidden) || num_rows < 0) return EP_ERR_INVALID_ARG;
     if (num_rows == 0) return EP_OK;
     if (!payload || !out || !aligned16(payload) || !aligned16(out)) return EP_ERR_INVALID_ARG;
-    return to_status(ep::launch_logfmt(payload, out, num_rows, hidden, false,
+    return to_status(ep::launch_logfmt(payload, out, num_rows, hidden, false, nullptr, 0,
                                        (hipStream_t)stream));
 }
 

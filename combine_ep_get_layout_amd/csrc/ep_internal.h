@@ -140,10 +140,12 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t stream);
 
 // 10-bit logarithmic payload: bytes of one packed row, the encode (bf16 rows
 // -> payload) or decode (payload -> bf16 rows) pass, and the combine that
-// reads payload rows (CombineArgs.y) instead of bf16 rows.
+// reads payload rows (CombineArgs.y) instead of bf16 rows.  Encode skips rows
+// with row_src < 0 (when given); max_used_rows bounds the rows it marks and
+// picks the launch for sparse batches.
 int64_t logfmt_row_bytes(int hidden);
 hipError_t launch_logfmt(const void *src, void *dst, int64_t rows, int hidden, bool encode,
-                         hipStream_t stream);
+                         const int32_t *row_src, int64_t max_used_rows, hipStream_t stream);
 hipError_t launch_combine_logfmt(const CombineArgs &a, hipStream_t stream);
 
 hipError_t launch_cast_fp8(const void *x, int T, int hidden, int group, int scale_fmt, uint8_t *q,

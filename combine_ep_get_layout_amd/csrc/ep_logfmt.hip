@@ -48,10 +48,18 @@ constexpr int kChanPerWave = kChanPerLane * 64;
 constexpr uint32_t kMaxLog = 0x1FDF;
 constexpr uint32_t kPoison = 0xFFFF;
 constexpr int kRowsInFlight = 4;
+// Sparse encode (a layout whose pairs fill at most a quarter of the rows):
+// waves per 64-row block, and rows loaded together by one wave.  Four and
+// four measured best at the decode shape (1,024 of 32,768 rows: 9 us,
+// against 23 us for a wave per row); on dense batches this launch is slower
+// than a wave per row (154 against 133 us at prefill), hence the two.
+constexpr int kEncodeRows = 4;
+constexpr int kEncodeSplit = 4;
 
 struct LogfmtK {
     const uint8_t *src;     // bf16 rows (encode) or payload rows (decode)
     uint8_t *dst;           // payload rows (encode) or bf16 rows (decode)
+    const int32_t *row_src; // encode: rows with row_src[r] < 0 are skipped (or NULL)
     int64_t rows;
     int hidden;
     int stride;             // payload row bytes
@@ -108,20 +116,11 @@ __device__ __forceinline__ uint32_t group8_max(uint32_t v) {
 // rounded log of both halves (no carry crosses a half: u <= 0x7F7F there),
 // l + 511 where l >= 1, then a saturating subtract of the reference gives
 // both indices, 0 where flushed or zero.
-__global__ void __launch_bounds__(kBlock) logfmt_encode_kernel(LogfmtK a) {
-    const int lane = __lane_id();
-    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
-    const int64_t r = gw / a.wpr;
-    const int ci = gw - (int)r * a.wpr;
-    if (r >= a.rows) return;
-    const int v = ci * 64 + lane;                 // 16-channel block of the row
-    const bool live = v * kChanPerLane < a.hidden;
-    ep_u32x4 x[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-    if (live) {
-        const ep_u32x4 *s = (const ep_u32x4 *)(a.src + r * (int64_t)a.hidden * 2) + 2 * v;
-        x[0] = load_nt(s);
-        x[1] = load_nt(s + 1);
-    }
+// One row's 16 channels of this lane, loaded as x: codes and high bits
+// stored; the lane with (lane & 7) == 0 stores its group's reference.
+// Every lane of the wave calls it (the group max exchanges across lanes).
+__device__ __forceinline__ void encode_lane(const LogfmtK &a, int64_t r, int v, int lane,
+                                            bool live, const ep_u32x4 *x) {
     uint32_t w[8], u[8];
     uint32_t umax2 = 0;
 #pragma unroll
@@ -156,6 +155,80 @@ __global__ void __launch_bounds__(kBlock) logfmt_encode_kernel(LogfmtK a) {
     ((ep_u32x4 *)row)[v] = ep_u32x4{lo[0], lo[1], lo[2], lo[3]};
     ((uint32_t *)(row + a.hidden))[v] = hi;
     if ((lane & 7) == 0) ((uint16_t *)(row + a.hidden + a.hidden / 4))[v >> 3] = (uint16_t)top;
+}
+
+// One wave per 1,024 channels of a row; a row without a pair (row_src < 0)
+// is skipped.  The launch for batches where most rows are encoded.
+__global__ void __launch_bounds__(kBlock) logfmt_encode_kernel(LogfmtK a) {
+    const int lane = __lane_id();
+    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int64_t r = gw / a.wpr;
+    const int ci = gw - (int)r * a.wpr;
+    if (r >= a.rows) return;
+    if (a.row_src && a.row_src[r] < 0) return;
+    const int v = ci * 64 + lane;
+    const bool live = v * kChanPerLane < a.hidden;
+    ep_u32x4 x[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if (live) {
+        const ep_u32x4 *src = (const ep_u32x4 *)(a.src + r * (int64_t)a.hidden * 2) + 2 * v;
+        x[0] = load_nt(src);
+        x[1] = load_nt(src + 1);
+    }
+    encode_lane(a, r, v, lane, live, x);
+}
+
+// kEncodeSplit waves take 1,024 channels of a block of 64 consecutive rows:
+// one lane per row checks whether the row is to be encoded (inside the
+// batch, and holding a pair when row_src is given), a ballot collects them,
+// and wave s of the block encodes the collected rows whose rank is s modulo
+// kEncodeSplit, kEncodeRows at a time with their loads issued together.  A
+// sparse batch (a fixed-capacity region at decode size, 3% of its rows
+// used) then costs one check per 64 rows per wave instead of a wave per
+// row, and a dense one still spreads its rows over many waves.
+__global__ void __launch_bounds__(kBlock) logfmt_encode_sparse_kernel(LogfmtK a) {
+    constexpr int U = kEncodeRows;
+    constexpr int S = kEncodeSplit;
+    const int lane = __lane_id();
+    const int gw = (int)blockIdx.x * kWavesPerBlock + wave_uniform(threadIdx.x >> 6);
+    const int64_t rb = gw / (a.wpr * S);
+    const int rest = gw - (int)rb * a.wpr * S;
+    const int ci = rest / S;
+    const int part = rest - ci * S;
+    const int64_t r0 = rb * 64;
+    if (r0 >= a.rows) return;
+    const int64_t rl = r0 + lane;
+    const bool want = rl < a.rows && (!a.row_src || a.row_src[rl] >= 0);
+    uint64_t all = __ballot(want);
+    uint64_t todo = 0;
+    for (int rank = 0; all; ++rank) {             // wave-uniform
+        const uint64_t bit = all & (0ull - all);
+        all ^= bit;
+        if (rank % S == part) todo |= bit;
+    }
+    const int v = ci * 64 + lane;                 // 16-channel block of the row
+    const bool live = v * kChanPerLane < a.hidden;
+    while (todo) {
+        int off[U];
+        ep_u32x4 x[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            off[u] = -1;
+            x[u][0] = x[u][1] = ep_u32x4{0u, 0u, 0u, 0u};
+            if (todo) {
+                off[u] = __builtin_ctzll(todo);
+                todo &= todo - 1;
+                if (live) {
+                    const ep_u32x4 *s =
+                        (const ep_u32x4 *)(a.src + (r0 + off[u]) * (int64_t)a.hidden * 2) + 2 * v;
+                    x[u][0] = load_nt(s);
+                    x[u][1] = load_nt(s + 1);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (off[u] >= 0) encode_lane(a, r0 + off[u], v, lane, live, x[u]);
+    }
 }
 
 // (reference - 511) * 4 in both 16-bit halves.
@@ -318,18 +391,24 @@ int64_t logfmt_row_bytes(int hidden) {
 }
 
 hipError_t launch_logfmt(const void *src, void *dst, int64_t rows, int hidden, bool encode,
-                         hipStream_t stream) {
+                         const int32_t *row_src, int64_t max_used_rows, hipStream_t stream) {
     LogfmtK k = {};
     k.src = (const uint8_t *)src;
     k.dst = (uint8_t *)dst;
+    k.row_src = row_src;
     k.rows = rows;
     k.hidden = hidden;
     k.stride = (int)logfmt_row_bytes(hidden);
     k.wpr = (hidden + kChanPerWave - 1) / kChanPerWave;
-    const int64_t grid = grid_of(rows, k.wpr);
+    const bool sparse = encode && row_src && max_used_rows * 4 <= rows;
+    const int64_t units = sparse ? (rows + 63) / 64 * kEncodeSplit : rows;
+    const int64_t grid = grid_of(units, k.wpr);
     if (grid == 0) return hipSuccess;
-    if (grid > 0x7FFFFFFF || rows * k.wpr > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (encode)
+    if (grid > 0x7FFFFFFF || units * k.wpr > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (sparse)
+        hipLaunchKernelGGL(logfmt_encode_sparse_kernel, dim3((unsigned)grid), dim3(kBlock), 0,
+                           stream, k);
+    else if (encode)
         hipLaunchKernelGGL(logfmt_encode_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream, k);
     else
         hipLaunchKernelGGL(logfmt_decode_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream, k);

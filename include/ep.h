@@ -376,11 +376,25 @@ int64_t ep_logfmt_row_bytes(int32_t hidden);
 
 /* ep_logfmt_encode - bf16 rows to payload rows.
  *   x        device bf16 [num_rows, hidden], 16-byte aligned.
+ *   params, layout  the receive layout the rows belong to, or both NULL.
+ *            With a layout only rows that hold a pair (src_of_slot >= 0) are
+ *            encoded, the rows a combine reads (the low-latency combine sends
+ *            no others); the others keep their payload bytes, so the padding
+ *            rows of an aligned layout, or the unused rows of a
+ *            fixed-capacity region, cost nothing.  num_rows must not exceed
+ *            params->max_recv_rows; the layout writes no src_of_slot entry at
+ *            or past its R rows, so rows there are encoded or skipped by
+ *            whatever those entries hold (no combine reads them).  When the
+ *            pairs (num_tokens * num_topk) fill at most a quarter of num_rows
+ *            the encoder launches for a sparse batch (the result is the same).
  *   payload  device uint8 [num_rows, ep_logfmt_row_bytes(hidden)], 16-byte
  *            aligned (caller-owned; may be reused across calls).
- * EP_ERR_INVALID_ARG for a bad hidden, negative num_rows or a NULL or
- * misaligned pointer (with num_rows > 0). */
-int ep_logfmt_encode(const void *x, int64_t num_rows, int32_t hidden, void *payload,
+ * EP_ERR_INVALID_ARG for a bad hidden, negative num_rows, only one of params
+ * and layout, num_rows above max_recv_rows, or a NULL or misaligned x /
+ * payload (with num_rows > 0); the layout parameter errors of
+ * ep_get_layout. */
+int ep_logfmt_encode(const void *x, int64_t num_rows, int32_t hidden,
+                     const ep_layout_params *params, const ep_layout *layout, void *payload,
                      void *stream);
 
 /* ep_logfmt_decode - payload rows to bf16 rows (exact; NaN = 0x7FC0 for a

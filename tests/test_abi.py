@@ -162,7 +162,8 @@ def test_logfmt_calls_reject_bad_arguments():
     for h in (0, -128, 64, 200, 1000):
         assert lib.ep_logfmt_row_bytes(h) == _abi.EP_ERR_INVALID_ARG
     v16, v8 = ctypes.c_void_p(16), ctypes.c_void_p(8)
-    for fn in (lib.ep_logfmt_encode, lib.ep_logfmt_decode):
+    enc = lambda x, n, h, p, s: lib.ep_logfmt_encode(x, n, h, None, None, p, s)
+    for fn in (enc, lib.ep_logfmt_decode):
         assert fn(v16, 4, 192, v16, None) == _abi.EP_ERR_INVALID_ARG      # hidden % 128
         assert fn(v16, -1, 128, v16, None) == _abi.EP_ERR_INVALID_ARG
         assert fn(v8, 4, 128, v16, None) == _abi.EP_ERR_INVALID_ARG       # misaligned
@@ -170,6 +171,12 @@ def test_logfmt_calls_reject_bad_arguments():
         assert fn(None, 0, 128, None, None) == _abi.EP_OK                 # nothing to do
     p = _params(T=4, K=2, E=8)
     lay = _abi.LayoutPtrs(*([16] * 7))
+    assert lib.ep_logfmt_encode(v16, 4, 128, ctypes.byref(p), None, v16,
+                                None) == _abi.EP_ERR_INVALID_ARG     # params without layout
+    assert lib.ep_logfmt_encode(v16, 4, 128, None, ctypes.byref(lay), v16,
+                                None) == _abi.EP_ERR_INVALID_ARG
+    assert lib.ep_logfmt_encode(v16, p.max_recv_rows + 1, 128, ctypes.byref(p),
+                                ctypes.byref(lay), v16, None) == _abi.EP_ERR_INVALID_ARG
     assert lib.ep_combine_logfmt(v16, 64, 8, None, None, None, ctypes.byref(p), ctypes.byref(lay),
                                  None, None, v16, None) == _abi.EP_ERR_INVALID_ARG
     assert lib.ep_combine_logfmt(v16, 128, 8, None, v8, None, ctypes.byref(p), ctypes.byref(lay),

@@ -2,8 +2,9 @@
 once and replayed with new inputs, with eager work and synchronisation
 between replays; every replay must equal the eager results bit for bit.
 Covers the two-kernel and the one-workgroup layout, the streaming dispatch,
-the zero fill of a mostly-padding fixed-capacity region and the fused fp8
-cast."""
+the zero fill of a mostly-padding fixed-capacity region, the fused fp8
+cast, and the 10-bit logarithmic payload (encode of the rows holding a pair,
+then the combine over it)."""
 import numpy as np
 import pytest
 import torch
@@ -25,6 +26,8 @@ def test_graph_replays_match_eager(gpu):
     recv = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
     rw = torch.empty(rows, dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    pay = torch.empty((rows, gpu.logfmt_row_bytes(H)), dtype=torch.uint8, device=dev)
+    out_l = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     def fill(seed):
         w = ep_inputs.make_workload("prefill", seed=seed, T=T, H=H)
@@ -47,17 +50,21 @@ def test_graph_replays_match_eager(gpu):
         gpu.ep_get_layout(s_idx, E, A, layout=lay)
         gpu.ep_dispatch(s_x, lay, s_w, out=(recv, None, rw), zero_padding=True)
         gpu.ep_combine(s_y, lay, s_w, out=out)
+        gpu.ep_logfmt_encode(s_y, out=pay, layout=lay)
+        gpu.ep_combine_logfmt(pay, H, lay, s_w, out=out_l)
     for seed in (1, 2, 3, 4):
         announce("graph replay", seed)
         fill(seed)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = [lay.dst_slot.clone(), lay.expert_offset.clone(), recv.clone(), rw.clone(), out.clone()]
+        got = [lay.dst_slot.clone(), lay.expert_offset.clone(), recv.clone(), rw.clone(), out.clone(),
+               out_l.clone()]
         # eager reference on the same inputs
         lay_e = gpu.ep_get_layout(s_idx, E, A)
         recv_e, _, rw_e = gpu.ep_dispatch(s_x, lay_e, s_w, zero_padding=True)
         out_e, _ = gpu.ep_combine(s_y, lay_e, s_w)
+        out_le, _ = gpu.ep_combine_logfmt(gpu.ep_logfmt_encode(s_y), H, lay_e, s_w)
         torch.cuda.synchronize()
         R = int(lay_e.expert_offset[-1].item())
         assert torch.equal(got[0], lay_e.dst_slot)
@@ -65,6 +72,7 @@ def test_graph_replays_match_eager(gpu):
         assert torch.equal(got[2][:R].view(torch.int16), recv_e[:R].view(torch.int16))
         assert torch.equal(got[3][:R], rw_e[:R])
         assert torch.equal(got[4].view(torch.int16), out_e.view(torch.int16))
+        assert torch.equal(got[5].view(torch.int16), out_le.view(torch.int16))
 
 
 def test_graph_capacity_fill_small_batch_and_fp8(gpu):

@@ -64,6 +64,41 @@ def test_every_pattern_alone_and_under_maxima(gpu):
         _check_codec(gpu, rows)
 
 
+@pytest.mark.parametrize("T,E,C", [
+    (300, 32, 0),      # aligned layout: padding rows skipped, one wave per row
+    (300, 32, 64),     # fixed capacity, most rows used: one wave per row
+    (100, 64, 64),     # 400 pairs in 4,096 rows: the sparse launch
+    (50, 256, 128),    # decode-like region (3% of 32,768 rows used): sparse
+    (10, 33, 8),       # sparse, 264 rows: a ragged last block of 64 rows
+])
+def test_encode_skips_rows_without_a_pair(gpu, T, E, C):
+    """With the layout, rows that hold no pair (alignment padding, or the
+    unused rows of a fixed-capacity region) keep their bytes, and no row's
+    tail past the payload is written; the combine over it equals the one over
+    the fully encoded rows."""
+    H, K, A = 1152, 4, 8
+    announce("logfmt encode with the layout", T, E, C)
+    w = ep_inputs.make_workload("prefill", seed=21 + T + C, T=T, H=H, E=E, K=K, A=A, drop_p=0.05,
+                                with_x=False)
+    lay = gpu.ep_get_layout(to_dev(w.topk_idx), E, A, 1, C)
+    ref = oracle.get_layout(w.topk_idx, E, A, 1, C)
+    y = ep_inputs.make_y_wide(w.rng, ref.R, H)
+    yd = bf16_to_dev(y)
+    pay = torch.full((ref.R, gpu.logfmt_row_bytes(H)), 0xAB, dtype=torch.uint8, device="cuda:0")
+    gpu.ep_logfmt_encode(yd, out=pay, layout=lay)
+    got = pay.cpu().numpy()
+    used = ref.src_of_slot >= 0
+    assert 0 < used.sum() < ref.R
+    assert np.all(got[~used] == 0xAB)
+    assert np.all(got[:, _used(H):] == 0xAB)
+    codes, refs = oracle.logfmt_encode(y[used])
+    np.testing.assert_array_equal(got[used, :_used(H)], oracle.logfmt_pack(codes, refs)[:, :_used(H)])
+    wt = to_dev(w.topk_weights)
+    out, _ = gpu.ep_combine_logfmt(pay, H, lay, wt)
+    out_full, _ = gpu.ep_combine_logfmt(gpu.ep_logfmt_encode(yd), H, lay, wt)
+    assert torch.equal(out.view(torch.int16), out_full.view(torch.int16))
+
+
 def test_empty_rows(gpu):
     pay = gpu.ep_logfmt_encode(torch.empty((0, 256), dtype=torch.bfloat16, device="cuda:0"))
     assert pay.shape == (0, 384)
