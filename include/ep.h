@@ -362,12 +362,12 @@ int ep_cast_fp8(const void *x, int32_t num_tokens, int32_t hidden, int32_t group
  * normal values).
  *
  * Packed row, ep_logfmt_row_bytes(hidden) bytes (a multiple of 128, so rows
- * start on cache lines): bytes
- * [0, H) hold code bits 0..7 of each channel; then H/16 little-endian uint32
- * words, word v carrying the high bits of channels 16v..16v+15: channel
- * 16v+2p+e (p = 0..7, e = 0 or 1) has its code's bit 8 in bit 7-p+16e and its
- * sign in bit 15-p+16e; then H/128 little-endian uint16 references; the tail up to
- * the row size is neither written nor read.  The encoder writes only valid
+ * start on cache lines): bytes [0, H) hold code bits 0..7 of each channel;
+ * then H/16 little-endian uint32 words, word v carrying the high bits of
+ * channels 16v..16v+15: channel 16v+2p+e (p = 0..7, e = 0 or 1) has its
+ * code's bit 8 in bit 7-p+16e and its sign in bit 15-p+16e; then H/128
+ * little-endian uint16 references; the tail up to the row size is neither
+ * written nor read.  The encoder writes only valid
  * codes; a payload written by anything else decodes to unspecified values
  * (never a memory fault).  hidden must be a positive multiple of 128. */
 
