@@ -154,3 +154,60 @@ def test_random_layout_both_paths(gpu, case):
     exp, _, exp_w = oracle.dispatch(x, ref, wts, zero_padding=True)
     np.testing.assert_array_equal(bf16_bits(recv[:R]), exp[:R])
     np.testing.assert_array_equal(rw[:R].cpu().numpy(), exp_w[:R])
+
+
+def _logfmt_cases(n=int(os.environ.get("EP_RANDOM_LOGFMT_CASES", "24")), seed=20261205):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([4, 16, 33, 64, 256]))
+        K = int(rng.integers(1, min(E, 10) + 1))
+        T = int(rng.choice([1, 17, 128, 500, 1500]))
+        A = int(rng.choice([1, 4, 128]))
+        C = 0 if rng.random() < 0.6 else A * int(rng.integers(1, 6))
+        H = 128 * int(rng.choice([1, 2, 7, 8, 9, 56, 72]))
+        drop = float(rng.choice([0.0, 0.1, 0.5]))
+        bias = int(rng.integers(0, 3))
+        weighted = bool(rng.random() < 0.7)
+        out.append((i, T, K, E, A, C, H, drop, bias, weighted))
+    return out
+
+
+@pytest.mark.parametrize("case", _logfmt_cases(), ids=lambda c: f"l{c[0]}")
+def test_random_logfmt_payload(gpu, case):
+    """The 10-bit logarithmic payload on random layouts: the encoder given the
+    layout (dense or sparse launch by the pair count) writes exactly the rows
+    that hold a pair, byte for byte as the oracle packs them, and the combine
+    over the payload equals the oracle's combine of the decoded rows."""
+    i, T, K, E, A, C, H, drop, bias, weighted = case
+    announce("random logfmt", case)
+    rng = ep_inputs.make_rng(3000 + i)
+    idx, wts = ep_inputs.routing_uniform(rng, T, E, K)
+    idx[rng.random((T, K)) < drop] = -1
+    lay = gpu.ep_get_layout(to_dev(idx), E, A, 1, C)
+    ref = oracle.get_layout(idx, E, A, 1, C, rows_cap=lay.max_recv_rows)
+    R = min(ref.R, lay.max_recv_rows)
+    y = ep_inputs.make_y_wide(rng, R, H)
+    b = [ep_inputs.bf16_normal(rng, (T, H)) for _ in range(bias)]
+    wt = wts if weighted else None
+    used_bytes = H + H // 4 + 2 * (H // 128)
+    pay = torch.full((R, gpu.logfmt_row_bytes(H)), 0x5A, dtype=torch.uint8, device="cuda:0")
+    gpu.ep_logfmt_encode(bf16_to_dev(y), out=pay, layout=lay)
+    got = pay.cpu().numpy()
+    used = ref.src_of_slot[:R] >= 0
+    assert np.all(got[~used] == 0x5A) and np.all(got[:, used_bytes:] == 0x5A)
+    # the oracle encodes the rows that hold a pair; the others decode to 0
+    # here and no pair reads them
+    cu, ru = oracle.logfmt_encode(y[used])
+    np.testing.assert_array_equal(got[used, :used_bytes], oracle.logfmt_pack(cu, ru)[:, :used_bytes])
+    codes = np.zeros((R, H), np.uint16)
+    refs = np.zeros((R, H // 128), np.uint16)
+    codes[used], refs[used] = cu, ru
+    out, _ = gpu.ep_combine_logfmt(pay, H, lay, to_dev(wt) if weighted else None,
+                                   bias=tuple(bf16_to_dev(bb) for bb in b) if b else None)
+    dst = np.where(ref.dst < R, ref.dst, -1).astype(np.int32)
+    want = oracle.combine_logfmt_f32(codes, refs, dst, wt, *(b + [None] * (2 - len(b))))
+    gotb = bf16_bits(out)
+    gn, wn = (gotb & 0x7FFF) > 0x7F80, (want & 0x7FFF) > 0x7F80
+    np.testing.assert_array_equal(gn, wn)
+    np.testing.assert_array_equal(np.where(gn, 0, gotb), np.where(wn, 0, want))
