@@ -242,7 +242,10 @@ def row_placement(ep, torch, dev, steps, iters):
     experts: ~256 receive segments written at once), and a routing that sends
     every token's k-th pair to expert 32k (8 segments, each written in
     address order, one front per segment).  Also the sequential write of the
-    same receive buffer by torch's fill kernel.  Back to back and cold."""
+    same receive buffer by torch's fill kernel.  For each routing,
+    `stores_only` runs the same kernel with every token row replaced by a
+    register pattern (no token row read): the cost of the scatter's writes
+    alone.  Back to back and cold."""
     import ep_inputs
     w = ep_inputs.make_workload("prefill")
     T, H, E, K, A = w.num_tokens, w.hidden, w.num_experts, w.num_topk, w.expert_alignment
@@ -275,6 +278,23 @@ def row_placement(ep, torch, dev, steps, iters):
         out[name] = {"N": N, "R": R, "bytes": nbytes, "us": round(us, 2),
                      "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "cold_us": cold["median_us"],
                      "cold_GBps": round(nbytes / (cold["median_us"] * 1e-6) / 1e9, 1)}
+        # the same kernel's stores alone: every row a register pattern, no
+        # token row read (ep_probe_dispatch_stores); N rows of H bf16 written
+        probe = lambda: ep.ep_probe_dispatch_stores(recv, lay)
+        probe()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            probe()
+        e1.record()
+        torch.cuda.synchronize()
+        sus = e0.elapsed_time(e1) / steps * 1e3
+        scold = cold_per_op(torch, dev, iters, {"stores": probe})["stores"]
+        sb = N * H * 2
+        out[name]["stores_only"] = {"bytes": sb, "us": round(sus, 2),
+                                    "GBps": round(sb / (sus * 1e-6) / 1e9, 1),
+                                    "cold_us": scold["median_us"],
+                                    "cold_GBps": round(sb / (scold["median_us"] * 1e-6) / 1e9, 1)}
         assert lay.check() == 0
         del lay, rw
     fill = recv[:T * K]

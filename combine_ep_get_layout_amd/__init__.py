@@ -37,7 +37,7 @@ __all__ = ["load_library", "Layout", "ep_get_layout", "ep_get_layout_noalloc", "
            "ep_combine", "ep_cast_fp8", "logfmt_row_bytes", "ep_logfmt_encode",
            "ep_logfmt_decode", "ep_combine_logfmt",
            "ep_dispatch_partitioned", "ep_combine_partitioned", "ep_combine_reduced",
-           "worst_case_recv_rows", "EpError", "EP_DEV_BAD_EXPERT", "EP_DEV_CAPACITY",
+           "worst_case_recv_rows", "ep_probe_dispatch_stores", "EpError", "EP_DEV_BAD_EXPERT", "EP_DEV_CAPACITY",
            "EP_DEV_RECV_OVERFLOW"]
 
 
@@ -471,6 +471,25 @@ def ep_combine(y: torch.Tensor, layout: Layout, topk_weights: Optional[torch.Ten
             ctypes.byref(params), ctypes.byref(ptrs), _ptr(recv_topk_weights),
             _ptr(cw), _ptr(out), _stream(y.device))
     return out, cw
+
+
+def ep_probe_dispatch_stores(recv_x: torch.Tensor, layout: Layout, pattern: int = 0x3F803F80):
+    """A measurement aid, not a step of the method: the bf16 dispatch's row
+    stores (same kernel, grid and order) with every token row replaced by the
+    32-bit `pattern`, so that no token row is read.  Writes
+    recv_x[dst_slot[t, k]] for every kept pair; returns recv_x."""
+    lib = load_library()
+    _need_cuda(recv_x, "recv_x")
+    if recv_x.dtype != torch.bfloat16 or recv_x.dim() != 2:
+        raise ValueError("recv_x must be bf16 [rows, H]")
+    _check(recv_x, "recv_x", _BF16, recv_x.shape[1])
+    params = layout.params
+    ptrs = layout.ptrs()
+    _launch("ep_probe_dispatch_stores", recv_x.device, lib.ep_probe_dispatch_stores,
+            [recv_x, layout.status], recv_x.shape[1], int(pattern) & 0xFFFFFFFF,
+            ctypes.byref(params), ctypes.byref(ptrs), _ptr(recv_x), recv_x.shape[0],
+            _stream(recv_x.device))
+    return recv_x
 
 
 def logfmt_row_bytes(hidden: int) -> int:

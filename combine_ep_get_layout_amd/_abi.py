@@ -33,7 +33,8 @@ EXPORTS = ("ep_get_layout_workspace_bytes", "ep_worst_case_recv_rows", "ep_get_l
            "ep_get_layout_noalloc",
            "ep_dispatch", "ep_dispatch_with_layout", "ep_combine", "ep_dispatch_partitioned", "ep_combine_partitioned",
            "ep_combine_reduced", "ep_cast_fp8", "ep_logfmt_row_bytes", "ep_logfmt_encode",
-           "ep_logfmt_decode", "ep_combine_logfmt", "ep_status_string")
+           "ep_logfmt_decode", "ep_combine_logfmt", "ep_probe_dispatch_stores",
+           "ep_status_string")
 
 
 class LayoutParams(ctypes.Structure):
@@ -113,6 +114,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ep_combine_logfmt.argtypes = [vp, i32, i64, vp, vp, vp, P(LayoutParams), P(LayoutPtrs),
                                       vp, vp, vp, vp]
     lib.ep_combine_logfmt.restype = ctypes.c_int
+    lib.ep_probe_dispatch_stores.argtypes = [i32, ctypes.c_uint32, P(LayoutParams), P(LayoutPtrs),
+                                             vp, i64, vp]
+    lib.ep_probe_dispatch_stores.restype = ctypes.c_int
     lib.ep_status_string.argtypes = [ctypes.c_int]
     lib.ep_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -267,6 +267,35 @@ int ep_dispatch_with_layout(const int64_t *topk_idx, const ep_layout_params *p,
     return to_status(ep::launch_dispatch(a, st));
 }
 
+int ep_probe_dispatch_stores(int32_t hidden, uint32_t pattern, const ep_layout_params *p,
+                             const ep_layout *layout, void *recv_x, int64_t num_recv_rows,
+                             void *stream) {
+    int rc = check_params(p);
+    if (rc != EP_OK) return rc;
+    if (!layout || !layout->status || (p->num_tokens > 0 && !layout->dst_slot))
+        return EP_ERR_INVALID_ARG;
+    if (hidden < 8 || hidden % 8 != 0 || num_recv_rows < 0) return EP_ERR_INVALID_ARG;
+    if (hidden > EP_MAX_HIDDEN) return EP_ERR_UNSUPPORTED;
+    if (p->num_tokens > 0 && num_recv_rows > 0 && (!recv_x || !aligned16(recv_x)))
+        return EP_ERR_INVALID_ARG;
+    ep::DispatchArgs a = {};
+    a.dst = layout->dst_slot;
+    a.counts = layout->num_tokens_per_expert;
+    a.offsets = layout->expert_offset;
+    a.status = layout->status;
+    a.recv = recv_x;
+    a.recv_rows = num_recv_rows;
+    a.T = p->num_tokens;
+    a.K = p->num_topk;
+    a.E = (int)segments(p);
+    a.A = p->expert_alignment;
+    a.C = p->capacity;
+    a.hidden = hidden;
+    a.mode = ep::kModeStores;
+    a.pattern = pattern;
+    return to_status(ep::launch_dispatch(a, (hipStream_t)stream));
+}
+
 int ep_combine(const void *y, int32_t hidden, int64_t num_y_rows, const float *topk_weights,
                const void *bias0, const void *bias1, const ep_layout_params *p,
                const ep_layout *layout, const float *recv_topk_weights,

@@ -86,6 +86,7 @@ struct DispatchK {
     int32_t *cum_stats;
     uint32_t *queue;          // token queue: one counter per XCD, kQueueStride apart (or NULL)
     int lds_bytes;            // dynamic LDS per workgroup (host side)
+    uint32_t pattern;         // kModeStores: the word every stored row holds
 };
 
 constexpr int kBlock = 256;
@@ -620,9 +621,18 @@ __global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
     ep_u32x4 v0b[VPL], v1b[VPL];
     uint32_t s0b[kScaleRegs] = {}, s1b[kScaleRegs] = {};
     const bool regs = MODE == kModeCopyFp8 && ci == 0 && scales_in_regs(a);
+    // kModeStores: the row is a register pattern (the stores without the reads)
+    auto load = [&](int tt, ep_u32x4 (&v)[VPL]) {
+        if (MODE == kModeStores) {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) v[i] = ep_u32x4{a.pattern, a.pattern, a.pattern, a.pattern};
+        } else {
+            load_chunk<VPL>(a, tt, v0, lane, v);
+        }
+    };
     auto first = [&] {
         if (mine) {
-            load_chunk<VPL>(a, (int)t, v0, lane, v0b);
+            load((int)t, v0b);
             if (regs) load_scales(a, (int)t, lane, s0b);
         }
     };
@@ -637,7 +647,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
     for (int j = 0;; j += 2) {
         int64_t tn = tok(j + 1);
         if (tn < a.T) {
-            load_chunk<VPL>(a, (int)tn, v0, lane, v1b);
+            load((int)tn, v1b);
             if (regs) load_scales(a, (int)tn, lane, s1b);
         }
         store_token<VPL, MODE, PART>(a, (int)t, ci, v0, lane, v0b, s0b);
@@ -645,7 +655,7 @@ __global__ void __launch_bounds__(kBlock) dispatch_stream_kernel(DispatchK a) {
         t = tn;
         tn = tok(j + 2);
         if (tn < a.T) {
-            load_chunk<VPL>(a, (int)tn, v0, lane, v0b);
+            load((int)tn, v0b);
             if (regs) load_scales(a, (int)tn, lane, s0b);
         }
         store_token<VPL, MODE, PART>(a, (int)t, ci, v0, lane, v1b, s1b);
@@ -898,6 +908,21 @@ hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStr
     return hipGetLastError();
 }
 
+// The stores-only instances: the expanded stream kernel only.
+hipError_t launch_stores(const DispatchK &k, int vpl, int grid, hipStream_t stream) {
+#define EP_CASE(V)                                                                              \
+    case V:                                                                                     \
+        hipLaunchKernelGGL((dispatch_stream_kernel<V, kModeStores, kTokensPerGroup, false>),    \
+                           dim3(grid), dim3(kBlock), k.lds_bytes, stream, k);                   \
+        break;
+    switch (vpl) {
+        EP_CASE(1) EP_CASE(2) EP_CASE(4) EP_CASE(7) EP_CASE(8) EP_CASE(14) EP_CASE(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef EP_CASE
+    return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_mode(const DispatchK &k, int vpl, int grid, bool multi, hipStream_t stream) {
     return k.m > 0 ? launch_mode<MODE, true>(k, vpl, grid, multi, stream)
@@ -982,6 +1007,7 @@ hipError_t run(DispatchK k, int mode, hipStream_t stream) {
     }
     if (grid == 0) return hipSuccess;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (mode == kModeStores) return multi ? launch_stores(k, vpl, (int)grid, stream) : hipErrorInvalidValue;
     switch (mode) {
         case kModeCopy16: return launch_mode<kModeCopy16>(k, vpl, (int)grid, multi, stream);
         case kModeCopyFp8: return launch_mode<kModeCopyFp8>(k, vpl, (int)grid, multi, stream);
@@ -1044,7 +1070,8 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t stream) {
         k.cum_stats = f.cum_stats;
         k.lds_bytes = (int)f.lds_bytes;
     }
-    if (a.mode == kModeCopy16) {
+    k.pattern = a.pattern;
+    if (a.mode == kModeCopy16 || a.mode == kModeStores) {
         k.in_row_bytes = k.out_row_bytes = a.hidden * 2;
         k.nvec = a.hidden / 8;
     } else if (a.mode == kModeCopyFp8) {

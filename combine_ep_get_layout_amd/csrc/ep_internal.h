@@ -83,7 +83,9 @@ uint32_t *queue_of(const LayoutPlan &plan, void *workspace);
 
 // Row modes of a dispatch: bf16 rows copied, fp8 rows copied with their
 // scales, bf16 rows cast to fp8 on the way.
-enum { kModeCopy16 = 0, kModeCopyFp8 = 1, kModeCast = 2 };
+// kModeStores is a measurement aid, not a step of the method: the bf16 copy's
+// stores with every token row replaced by a fixed pattern (no row is read).
+enum { kModeCopy16 = 0, kModeCopyFp8 = 1, kModeCast = 2, kModeStores = 3 };
 
 struct DispatchArgs {
     const void *x;
@@ -112,6 +114,7 @@ struct DispatchArgs {
     float *recv_wk;                // [rows*K] or NULL
     const int32_t *part_src;       // [T*P] token of each receive row, or NULL
     const int32_t *part_offset;    // [P+1]
+    uint32_t pattern;              // kModeStores: the 32-bit word every row is filled with
     const FreshLayout *fresh;      // non-NULL: slots derived here from the count kernel's output
     uint32_t *queue;               // token-queue counters, zero when the dispatch starts, or NULL
 };

@@ -416,6 +416,25 @@ int ep_combine_logfmt(const void *payload, int32_t hidden, int64_t num_y_rows,
                       const float *recv_topk_weights, float *combined_topk_weights, void *out,
                       void *stream);
 
+/* ep_probe_dispatch_stores - a measurement aid, not a step of the method:
+ * the stores of ep_dispatch for bf16 rows (the same row kernel, grid and
+ * store order) with each token's row replaced by a fixed pattern held in
+ * registers, so that no token row is read.  It shows what the scatter's
+ * writes alone cost at a given routing.
+ *
+ *   hidden       channels per row (bf16), a multiple of 8, at most EP_MAX_HIDDEN.
+ *   pattern      the 32-bit word every written row is filled with.
+ *   params, layout  as produced by ep_get_layout; only dst_slot and status
+ *                are read.
+ *   recv_x       device [num_recv_rows, hidden] bf16, 16-byte aligned.
+ * Writes recv_x[dst_slot[t,k]] = pattern (every 4-byte word) for every kept
+ * pair; padding rows and everything else keep their bytes.  Slots at or past
+ * num_recv_rows are skipped and EP_DEV_RECV_OVERFLOW is set.
+ * Errors: EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED (hidden > EP_MAX_HIDDEN). */
+int ep_probe_dispatch_stores(int32_t hidden, uint32_t pattern, const ep_layout_params *params,
+                             const ep_layout *layout, void *recv_x, int64_t num_recv_rows,
+                             void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *ep_status_string(int code);
 

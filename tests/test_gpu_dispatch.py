@@ -311,3 +311,26 @@ def test_widest_rows(gpu):
     out, _ = gpu.ep_combine(bf16_to_dev(y), lay, to_dev(wts))
     np.testing.assert_array_equal(bf16_bits(out), oracle.combine_f32(y, ref.dst, wts))
     assert lay.check() == 0
+
+
+@pytest.mark.parametrize("T,H,E,K,A", [
+    (4096, 7168, 256, 8, 128),   # the prefill shape, the kernel instance the bench times
+    (333, 1000, 32, 4, 3),       # ragged row
+])
+def test_probe_dispatch_stores(gpu, T, H, E, K, A):
+    """The stores-only measurement aid writes the pattern into exactly the
+    rows that hold a pair (the oracle's src_of_slot) and nothing else."""
+    announce("probe stores", T, H, E, K, A)
+    w = ep_inputs.make_workload("prefill", T=T, H=H, E=E, K=K, A=A, drop_p=0.02)
+    lay, ref = _setup(gpu, w)
+    rows = lay.max_recv_rows
+    recv = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda:0")
+    recv.view(torch.int16).fill_(SENTINEL)
+    gpu.ep_probe_dispatch_stores(recv, lay, pattern=0x3F80BF80)
+    torch.cuda.synchronize()
+    used = torch.from_numpy(ref.src_of_slot >= 0).to("cuda:0")
+    words = recv[:ref.R].view(torch.int32)
+    assert bool((words[used] == 0x3F80BF80).all())
+    assert bool((recv[:ref.R][~used].view(torch.int16) == SENTINEL).all())
+    assert bool((recv[ref.R:].view(torch.int16) == SENTINEL).all())
+    assert lay.check() == 0
