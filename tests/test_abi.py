@@ -156,6 +156,24 @@ def test_combine_and_cast_reject_bad_arguments():
                            ctypes.c_void_p(18), None) == _abi.EP_ERR_INVALID_ARG   # float scales
 
 
+def test_probe_dispatch_stores_rejects_bad_arguments():
+    lib = _abi.load()
+    p = _params(T=4, K=2, E=8)
+    lay = _abi.LayoutPtrs(*([16] * 7))
+    f = lib.ep_probe_dispatch_stores
+    assert f(12, 0, ctypes.byref(p), ctypes.byref(lay), ctypes.c_void_p(16), 8, None) \
+        == _abi.EP_ERR_INVALID_ARG                               # hidden % 8 != 0
+    assert f(_abi.EP_MAX_HIDDEN + 8, 0, ctypes.byref(p), ctypes.byref(lay), ctypes.c_void_p(16), 8,
+             None) == _abi.EP_ERR_UNSUPPORTED
+    assert f(64, 0, ctypes.byref(p), ctypes.byref(lay), ctypes.c_void_p(8), 8, None) \
+        == _abi.EP_ERR_INVALID_ARG                               # misaligned rows
+    assert f(64, 0, ctypes.byref(p), None, ctypes.c_void_p(16), 8, None) == _abi.EP_ERR_INVALID_ARG
+    assert f(64, 0, ctypes.byref(p), ctypes.byref(lay), ctypes.c_void_p(16), -1, None) \
+        == _abi.EP_ERR_INVALID_ARG
+    assert f(64, 0, ctypes.byref(_params(E=6, P=4)), ctypes.byref(lay), ctypes.c_void_p(16), 8,
+             None) == _abi.EP_ERR_INVALID_ARG                    # the layout params are checked
+
+
 def test_logfmt_calls_reject_bad_arguments():
     lib = _abi.load()
     assert lib.ep_logfmt_row_bytes(7168) == 9088 and lib.ep_logfmt_row_bytes(128) == 256
